@@ -1,0 +1,23 @@
+// launch.hpp - internal launchers behind the C ABI (argument checks live in api.cpp).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mx {
+
+// MXFP4 quantizer: rows x K values (K % 32 == 0) -> codes [rows, K/2], scales [rows, K/32].
+hipError_t launch_quant_mx_bf16(const void* x, int64_t rows, int64_t K, void* q, void* s, hipStream_t st);
+hipError_t launch_quant_mx_f32(const void* x, int64_t rows, int64_t K, void* q, void* s, hipStream_t st);
+
+// PTPC FP8 quantizer: rows x K values (K % 8 == 0) -> E4M3 codes [rows, K], FP32 scales [rows].
+hipError_t launch_quant_ptpc_bf16(const void* x, int64_t rows, int64_t K, void* q, float* s, hipStream_t st);
+hipError_t launch_quant_ptpc_f32(const void* x, int64_t rows, int64_t K, void* q, float* s, hipStream_t st);
+
+// GEMMs (K % 128 == 0, M, N > 0).
+hipError_t launch_gemm_a4w4(const void* qa, const void* sa, const void* qw, const void* sw, void* y,
+                            int64_t M, int64_t N, int64_t K, hipStream_t st);
+hipError_t launch_gemm_a8w8(const void* qa, const float* sa, const void* qw, const float* sw, void* y,
+                            int64_t M, int64_t N, int64_t K, hipStream_t st);
+
+}  // namespace mx

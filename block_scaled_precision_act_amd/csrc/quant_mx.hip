@@ -1,0 +1,120 @@
+// quant_mx.hip - MXFP4 quantization (E2M1 codes + one E8M0 scale per 32 K-values).
+//
+// Format: "Kimi-K3 DSpark O-Proj-only MXFP4", section "Exact quantization
+// coverage" (32 consecutive input-channel values share one E8M0 scale; dynamic
+// MXFP4 activations); standard "OCP MXFP4" named by "Kimi-K3-Quark-MXFP4-
+// AttnFP8", section "Model Quantization".
+//
+// The kernel is integer-only.  Four lanes own one 32-value block, eight values
+// (one 16-byte BF16 load, or two FP32 loads) each:
+//   * shared exponent: the largest biased exponent field E of the block (a
+//     4-lane max); scale byte = max(E - 2, 0), which is floor(log2 amax) - 2
+//     + 127 clamped at the bottom of the E8M0 range; E == 255 (NaN/Inf in the
+//     block) gives scale 0xFF and codes 0.
+//   * element: with significand sig (hidden bit included; P fraction bits) and
+//     effective exponent Ee = max(E, 1), |x| / 2^(scale-127) times 4 equals
+//     sig / 2^u with u = scale + P - 2 - Ee >= P - 4, so every round-to-nearest-
+//     even decision on the E2M1 grid {0,.5,1,1.5,2,3,4,6} is an exact integer
+//     compare of sig against (midpoint*4) << u; ties at 0.25, 1.25, 2.5 and 5
+//     stay below (even code), ties at 0.75, 1.75 and 3.5 go up; above 6 the
+//     code saturates at 7.
+//   * one 32-bit store of 8 nibbles per lane (element 2j in the low nibble of
+//     byte j), one scale byte per block.
+// HBM-bound: 2 (or 4) bytes in, 0.5 + 1/32 bytes out per value.
+#include "launch.hpp"
+#include "mx_device.hpp"
+
+namespace mx {
+namespace {
+
+// magnitude code 0..7 of sig / 2^(u+2) on the E2M1 grid (see file comment)
+__device__ __forceinline__ uint32_t e2m1_magnitude(uint32_t sig, uint32_t u) {
+    return (uint32_t)(sig > (1u << u)) + (uint32_t)(sig >= (3u << u)) + (uint32_t)(sig > (5u << u)) +
+           (uint32_t)(sig >= (7u << u)) + (uint32_t)(sig > (10u << u)) + (uint32_t)(sig >= (14u << u)) +
+           (uint32_t)(sig > (20u << u));
+}
+
+template <int P>  // fraction bits of the input format (7 for BF16, 23 for FP32)
+__device__ __forceinline__ uint32_t encode8(const uint32_t (&mag)[8], uint32_t scale) {
+    uint32_t codes = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        uint32_t e = mag[i] >> P;
+        uint32_t sig = (mag[i] & ((1u << P) - 1u)) | (e ? (1u << P) : 0u);
+        uint32_t ee = e ? e : 1u;
+        uint32_t u = scale + (uint32_t)P - 2u - ee;
+        u = u < (uint32_t)(P + 1) ? u : (uint32_t)(P + 1);  // beyond P+1 every threshold exceeds sig
+        codes |= e2m1_magnitude(sig, u) << (4 * i);
+    }
+    return codes;
+}
+
+// One "unit" = 8 consecutive values = one quarter of a block.  units % 4 == 0
+// and the grid stride is a multiple of 4, so the four lanes of a block always
+// iterate together (the 4-lane shuffles below stay inside active lanes).
+template <bool F32>
+__global__ __launch_bounds__(256) void quant_mx_kernel(const void* __restrict__ xin, uint32_t* __restrict__ q,
+                                                        uint8_t* __restrict__ s, int64_t units) {
+    constexpr int P = F32 ? 23 : 7;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < units; u += stride) {
+        uint32_t mag[8];
+        uint32_t sgn = 0, emax = 0;
+        if constexpr (F32) {
+            const uint4* p = reinterpret_cast<const uint4*>(xin) + 2 * u;
+            const uint4 a = p[0], b = p[1];
+            const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                sgn |= (w[i] >> 31) << (4 * i + 3);
+                mag[i] = w[i] & 0x7fffffffu;
+                emax = max(emax, mag[i] >> 23);
+            }
+        } else {
+            const uint4 a = reinterpret_cast<const uint4*>(xin)[u];
+            const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t lo = w[i] & 0xffffu, hi = w[i] >> 16;
+                sgn |= ((lo >> 15) << (8 * i + 3)) | ((hi >> 15) << (8 * i + 7));
+                mag[2 * i] = lo & 0x7fffu;
+                mag[2 * i + 1] = hi & 0x7fffu;
+                emax = max(emax, max(mag[2 * i] >> 7, mag[2 * i + 1] >> 7));
+            }
+        }
+        emax = max(emax, (uint32_t)__shfl_xor((int)emax, 1));
+        emax = max(emax, (uint32_t)__shfl_xor((int)emax, 2));
+        uint32_t codes, scale;
+        if (emax == 0xffu) {  // NaN or Inf in the block
+            scale = 0xffu;
+            codes = 0;
+        } else {
+            scale = emax > 2u ? emax - 2u : 0u;
+            codes = encode8<P>(mag, scale) | sgn;
+        }
+        q[u] = codes;
+        if ((u & 3) == 0) s[u >> 2] = (uint8_t)scale;
+    }
+}
+
+template <bool F32>
+hipError_t launch(const void* x, int64_t rows, int64_t K, void* q, void* s, hipStream_t st) {
+    const int64_t units = rows * (K / 8);
+    int64_t blocks = (units + 255) / 256;
+    if (blocks > (1 << 20)) blocks = 1 << 20;
+    hipLaunchKernelGGL(quant_mx_kernel<F32>, dim3((unsigned)blocks), dim3(256), 0, st, x,
+                       reinterpret_cast<uint32_t*>(q), reinterpret_cast<uint8_t*>(s), units);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quant_mx_bf16(const void* x, int64_t rows, int64_t K, void* q, void* s, hipStream_t st) {
+    return launch<false>(x, rows, K, q, s, st);
+}
+
+hipError_t launch_quant_mx_f32(const void* x, int64_t rows, int64_t K, void* q, void* s, hipStream_t st) {
+    return launch<true>(x, rows, K, q, s, st);
+}
+
+}  // namespace mx

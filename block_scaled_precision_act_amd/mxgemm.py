@@ -1,0 +1,223 @@
+"""Thin ctypes binding of libmxgemm (include/mxgemm.h).
+
+Two layers:
+  * the C entry points under their own names (``mx_quant_act_bf16``,
+    ``mx_gemm_a4w4_bf16``, ``ptpc_quant_act_fp8``, ``gemm_a8w8_ptpc_bf16``, ...)
+    taking raw device pointers / sizes / a stream handle and returning the
+    mx_status integer;
+  * tensor helpers (``quant_act_mx``, ``gemm_a4w4``, ``linear_a4w4``, ...) that
+    check dtypes and shapes, allocate outputs with torch and call the entry
+    points on torch's current stream.
+
+Every computation runs in the HIP kernels of libmxgemm.so; torch only provides
+device memory and the stream.  Loading fails loudly if the library has not
+been built (``python -m block_scaled_precision_act_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmxgemm.so")
+
+MX_SUCCESS = 0
+MX_ERROR_INVALID_VALUE = 1
+MX_ERROR_UNSUPPORTED_SHAPE = 2
+MX_ERROR_MISALIGNED = 3
+MX_ERROR_WORKSPACE = 4
+MX_ERROR_LAUNCH = 5
+MX_ERROR_DEVICE = 6
+
+_lib = None
+
+
+class MxError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s" % (where, status_string(status)))
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libmxgemm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libmxgemm.so is not built (%s); run `python -m block_scaled_precision_act_amd.build`"
+                               % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.mx_abi_version.argtypes = []
+        L.mx_abi_version.restype = i32
+        L.mx_status_string.argtypes = [i32]
+        L.mx_status_string.restype = ctypes.c_char_p
+        for name in ("mx_quant_act_bf16", "mx_quant_weight_f32"):
+            getattr(L, name).argtypes = [vp, i64, i64, vp, vp, vp]
+            getattr(L, name).restype = i32
+        for name in ("ptpc_quant_act_fp8", "ptpc_quant_weight_f32"):
+            getattr(L, name).argtypes = [vp, i64, i64, vp, vp, vp]
+            getattr(L, name).restype = i32
+        L.mx_gemm_a4w4_workspace_bytes.argtypes = [i64, i64, i64]
+        L.mx_gemm_a4w4_workspace_bytes.restype = ctypes.c_size_t
+        L.mx_gemm_a4w4_bf16.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, ctypes.c_size_t, vp]
+        L.mx_gemm_a4w4_bf16.restype = i32
+        L.gemm_a8w8_ptpc_bf16.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
+        L.gemm_a8w8_ptpc_bf16.restype = i32
+        _lib = L
+    return _lib
+
+
+# ------------------------------------------------------------------ C entry points
+def mx_abi_version() -> int:
+    return lib().mx_abi_version()
+
+
+def status_string(status: int) -> str:
+    return lib().mx_status_string(int(status)).decode()
+
+
+def mx_quant_act_bf16(x, M, K, q, s, stream=None) -> int:
+    return lib().mx_quant_act_bf16(x, M, K, q, s, stream)
+
+
+def mx_quant_weight_f32(w, N, K, q, s, stream=None) -> int:
+    return lib().mx_quant_weight_f32(w, N, K, q, s, stream)
+
+
+def mx_gemm_a4w4_workspace_bytes(M, N, K) -> int:
+    return lib().mx_gemm_a4w4_workspace_bytes(M, N, K)
+
+
+def mx_gemm_a4w4_bf16(qa, sa, qw, sw, y, M, N, K, workspace=None, workspace_bytes=0, stream=None) -> int:
+    return lib().mx_gemm_a4w4_bf16(qa, sa, qw, sw, y, M, N, K, workspace, workspace_bytes, stream)
+
+
+def ptpc_quant_act_fp8(x, M, K, q, s, stream=None) -> int:
+    return lib().ptpc_quant_act_fp8(x, M, K, q, s, stream)
+
+
+def ptpc_quant_weight_f32(w, N, K, q, s, stream=None) -> int:
+    return lib().ptpc_quant_weight_f32(w, N, K, q, s, stream)
+
+
+def gemm_a8w8_ptpc_bf16(qa, sa, qw, sw, y, M, N, K, stream=None) -> int:
+    return lib().gemm_a8w8_ptpc_bf16(qa, sa, qw, sw, y, M, N, K, stream)
+
+
+# ------------------------------------------------------------------ tensor helpers
+def _torch():
+    import torch
+    return torch
+
+
+def _stream():
+    return _torch().cuda.current_stream().cuda_stream
+
+
+def _need(t, dtype, ndim, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if t.dim() != ndim:
+        raise ValueError("%s must be %d-D, got shape %s" % (name, ndim, tuple(t.shape)))
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _ok(status, where):
+    if status != MX_SUCCESS:
+        raise MxError(status, where)
+
+
+def quant_act_mx(x, q=None, s=None):
+    """BF16 [M, K] -> (codes uint8 [M, K/2], E8M0 scales uint8 [M, K/32])."""
+    torch = _torch()
+    _need(x, torch.bfloat16, 2, "x")
+    M, K = x.shape
+    q = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device) if q is None else q
+    s = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device) if s is None else s
+    _ok(mx_quant_act_bf16(x.data_ptr(), M, K, q.data_ptr(), s.data_ptr(), _stream()), "mx_quant_act_bf16")
+    return q, s
+
+
+def quant_weight_mx(w):
+    """FP32 [N, K] -> (codes uint8 [N, K/2], E8M0 scales uint8 [N, K/32])."""
+    torch = _torch()
+    _need(w, torch.float32, 2, "w")
+    N, K = w.shape
+    q = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device)
+    s = torch.empty((N, K // 32), dtype=torch.uint8, device=w.device)
+    _ok(mx_quant_weight_f32(w.data_ptr(), N, K, q.data_ptr(), s.data_ptr(), _stream()), "mx_quant_weight_f32")
+    return q, s
+
+
+def gemm_a4w4(qa, sa, qw, sw, y=None):
+    """MXFP4 codes/scales of A [M, .] and W [N, .] -> BF16 Y [M, N] = A . W^T."""
+    torch = _torch()
+    for t, n in ((qa, "qa"), (sa, "sa"), (qw, "qw"), (sw, "sw")):
+        _need(t, torch.uint8, 2, n)
+    M, K = qa.shape[0], qa.shape[1] * 2
+    N = qw.shape[0]
+    if qw.shape[1] * 2 != K or sa.shape != (M, K // 32) or sw.shape != (N, K // 32):
+        raise ValueError("inconsistent A4W4 operand shapes")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=qa.device) if y is None else y
+    ws = mx_gemm_a4w4_workspace_bytes(M, N, K)
+    wbuf = torch.empty(ws, dtype=torch.uint8, device=qa.device) if ws else None
+    _ok(mx_gemm_a4w4_bf16(qa.data_ptr(), sa.data_ptr(), qw.data_ptr(), sw.data_ptr(), y.data_ptr(), M, N, K,
+                          wbuf.data_ptr() if ws else None, ws, _stream()), "mx_gemm_a4w4_bf16")
+    return y
+
+
+def linear_a4w4(x, qw, sw):
+    """The A4W4 layer: dynamic MXFP4 quantization of BF16 x, then the block-scaled GEMM."""
+    qa, sa = quant_act_mx(x)
+    return gemm_a4w4(qa, sa, qw, sw)
+
+
+def quant_act_ptpc(x):
+    """BF16 [M, K] -> (E4M3fn codes uint8 [M, K], FP32 scales [M])."""
+    torch = _torch()
+    _need(x, torch.bfloat16, 2, "x")
+    M, K = x.shape
+    q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    s = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _ok(ptpc_quant_act_fp8(x.data_ptr(), M, K, q.data_ptr(), s.data_ptr(), _stream()), "ptpc_quant_act_fp8")
+    return q, s
+
+
+def quant_weight_ptpc(w):
+    """FP32 [N, K] -> (E4M3fn codes uint8 [N, K], FP32 per-output-channel scales [N])."""
+    torch = _torch()
+    _need(w, torch.float32, 2, "w")
+    N, K = w.shape
+    q = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+    s = torch.empty((N,), dtype=torch.float32, device=w.device)
+    _ok(ptpc_quant_weight_f32(w.data_ptr(), N, K, q.data_ptr(), s.data_ptr(), _stream()), "ptpc_quant_weight_f32")
+    return q, s
+
+
+def gemm_a8w8(qa, sa, qw, sw, y=None):
+    """E4M3 codes + FP32 row scales of A [M, K] and W [N, K] -> BF16 Y [M, N]."""
+    torch = _torch()
+    _need(qa, torch.uint8, 2, "qa")
+    _need(qw, torch.uint8, 2, "qw")
+    _need(sa, torch.float32, 1, "sa")
+    _need(sw, torch.float32, 1, "sw")
+    M, K = qa.shape
+    N = qw.shape[0]
+    if qw.shape[1] != K or sa.shape[0] != M or sw.shape[0] != N:
+        raise ValueError("inconsistent A8W8 operand shapes")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=qa.device) if y is None else y
+    _ok(gemm_a8w8_ptpc_bf16(qa.data_ptr(), sa.data_ptr(), qw.data_ptr(), sw.data_ptr(), y.data_ptr(), M, N, K,
+                            _stream()), "gemm_a8w8_ptpc_bf16")
+    return y
+
+
+def linear_a8w8(x, qw, sw):
+    """The A8W8 layer: dynamic per-token FP8 quantization of BF16 x, then the PTPC GEMM."""
+    qa, sa = quant_act_ptpc(x)
+    return gemm_a8w8(qa, sa, qw, sw)

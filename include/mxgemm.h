@@ -1,0 +1,147 @@
+/*
+ * mxgemm.h - C ABI of libmxgemm, the MI355X (gfx950) block-scaled linear layer.
+ *
+ * The layer is the attention output projection of "Kimi-K3 DSpark O-Proj-only
+ * MXFP4" (section "Exact quantization coverage"): weight stored (out, in) =
+ * (7168, 8192) as MXFP4 - E2M1 elements, one E8M0 scale per 32 consecutive
+ * input-channel values, scales (7168, 256) - run with dynamic MXFP4
+ * activations through an A4W4 GEMM.  Its sibling is the PTPC FP8 scheme of
+ * "Kimi-K3-DSpark-FP8-PTPC" (section "Phase 1 FP8 PTPC Quantization"): E4M3
+ * weights with an FP32 per-output-channel scale (out_features, 1) and dynamic
+ * per-token FP8 activations computed online.
+ *
+ * Conventions for every entry point
+ *   - Pointers are DEVICE pointers to caller-owned, contiguous, row-major
+ *     buffers.  The library never allocates device memory, keeps no state
+ *     between calls and never synchronizes the host: every call only enqueues
+ *     kernels on `stream` (a hipStream_t; NULL is the default stream) and
+ *     returns, so calls can be captured into a HIP graph.
+ *   - Shapes: X is [M, K] (tokens x in), W is [N, K] (out x in), Y = X . W^T is
+ *     [M, N]; there is no bias.  M, N >= 0; M == 0 or N == 0 is a successful
+ *     no-op that enqueues nothing.
+ *   - Packed MXFP4 codes are [rows, K/2] bytes: element 2j in the low nibble of
+ *     byte j, element 2j+1 in the high nibble; E2M1 code = sign<<3 | exp<<1 |
+ *     man.  E8M0 scales are [rows, K/32] bytes, value 2^(s-127), 0xFF = NaN.
+ *     E4M3 codes are OCP float8_e4m3fn bytes (max 448, 0x7F/0xFF = NaN).
+ *     BF16 is the upper half of an IEEE binary32.
+ *   - Numeric rules (the pages name "OCP MXFP4" - "Kimi-K3-Quark-MXFP4-AttnFP8",
+ *     section "Model Quantization" - but leave the details open; these are the
+ *     readings taken):
+ *       MX block: e = max(floor(log2(max|x|)) - 2, -127), scale byte e + 127;
+ *       element = round-to-nearest-even(x / 2^e) on {0,.5,1,1.5,2,3,4,6},
+ *       saturating at 6, sign kept (negative zero results encode as 0x8); an
+ *       all-zero block gets scale 0x00; a block with NaN/Inf gets scale 0xFF and
+ *       codes 0.
+ *       PTPC row: a = max|x|, s = fl32(a / 448) (s = 1 when a == 0),
+ *       code = E4M3fn round-to-nearest-even of fl32(x / s), saturating at 448;
+ *       a row with NaN/Inf gets s = NaN and every code 0x7F.
+ *       GEMMs accumulate in FP32 and round the result to BF16 (nearest even).
+ *   - Errors: argument errors are detected on the host before anything is
+ *     enqueued and returned as an mx_status; a launch failure returns
+ *     MX_ERROR_LAUNCH.  Faults during asynchronous execution surface on the
+ *     stream.  No C++ exception crosses this interface.
+ *   - Outputs must not alias inputs (not checked).
+ */
+#ifndef MXGEMM_H
+#define MXGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MX_SUCCESS = 0,
+    MX_ERROR_INVALID_VALUE = 1,     /* NULL pointer with a non-empty shape, negative size */
+    MX_ERROR_UNSUPPORTED_SHAPE = 2, /* K outside the rules stated per entry point        */
+    MX_ERROR_MISALIGNED = 3,        /* a pointer misses the alignment stated per entry    */
+    MX_ERROR_WORKSPACE = 4,         /* workspace smaller than the size query returned     */
+    MX_ERROR_LAUNCH = 5,            /* the HIP runtime refused a kernel launch            */
+    MX_ERROR_DEVICE = 6             /* the current device is not a gfx950 GPU             */
+} mx_status;
+
+/* Version of this interface (incremented on any ABI change). */
+int mx_abi_version(void);
+
+/* Static string naming a status code (never NULL). */
+const char *mx_status_string(mx_status status);
+
+/*
+ * Dynamic per-token MXFP4 quantization of BF16 activations ("dynamic MXFP4
+ * activations with A4W4 dispatch": "Kimi-K3 DSpark O-Proj-only MXFP4", section
+ * "Exact quantization coverage").
+ *   x_bf16 [M, K]      in   BF16, 16-byte aligned
+ *   q      [M, K/2]    out  packed E2M1 codes, 16-byte aligned
+ *   s      [M, K/32]   out  E8M0 scales (byte aligned)
+ * K > 0 and K % 32 == 0.
+ */
+mx_status mx_quant_act_bf16(const void *x_bf16, int64_t M, int64_t K,
+                            void *q, void *s, void *stream);
+
+/*
+ * Offline MXFP4 weight quantization from FP32 (the checkpoint conversion the
+ * same section describes: weight (N, K) -> E2M1 codes + (N, K/32) E8M0 scales).
+ * Same rules and layouts as mx_quant_act_bf16 with an FP32 input
+ * (16-byte aligned).
+ */
+mx_status mx_quant_weight_f32(const float *w, int64_t N, int64_t K,
+                              void *q, void *s, void *stream);
+
+/*
+ * Bytes of workspace mx_gemm_a4w4_bf16 needs for this shape (currently 0 for
+ * every shape; callers that pass the queried size stay correct if a later
+ * version needs one).
+ */
+size_t mx_gemm_a4w4_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * A4W4 block-scaled GEMM, Y = dequant(qa, sa) . dequant(qw, sw)^T, BF16 out
+ * ("A4W4 dispatch" of "Kimi-K3 DSpark O-Proj-only MXFP4", section "Exact
+ * quantization coverage").
+ *   qa [M, K/2], sa [M, K/32]   activation codes / scales (from mx_quant_act_bf16)
+ *   qw [N, K/2], sw [N, K/32]   weight codes / scales (e.g. from mx_quant_weight_f32)
+ *   y_bf16 [M, N]               out
+ * K > 0 and K % 128 == 0.  qa, qw 16-byte aligned; sa, sw 4-byte aligned;
+ * y_bf16 2-byte aligned.  workspace may be NULL when workspace_bytes is 0.
+ */
+mx_status mx_gemm_a4w4_bf16(const void *qa, const void *sa, const void *qw, const void *sw,
+                            void *y_bf16, int64_t M, int64_t N, int64_t K,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Dynamic per-token FP8 quantization of BF16 activations ("dynamic per-token
+ * FP8, computed online": "Kimi-K3-DSpark-FP8-PTPC", section "Phase 1 FP8 PTPC
+ * Quantization").
+ *   x_bf16 [M, K] in (16-byte aligned); q [M, K] E4M3fn out (8-byte aligned);
+ *   s [M] FP32 out (4-byte aligned).  K > 0 and K % 8 == 0.
+ */
+mx_status ptpc_quant_act_fp8(const void *x_bf16, int64_t M, int64_t K,
+                             void *q, float *s, void *stream);
+
+/*
+ * Offline per-output-channel FP8 weight quantization from FP32 (the weight
+ * side of the same scheme: E4M3 weight + FP32 (out_features, 1) scale).
+ *   w [N, K] FP32 in (16-byte aligned); q [N, K] out (8-byte aligned);
+ *   s [N] out.  K > 0 and K % 8 == 0.
+ */
+mx_status ptpc_quant_weight_f32(const float *w, int64_t N, int64_t K,
+                                void *q, float *s, void *stream);
+
+/*
+ * PTPC A8W8 GEMM: Y[m,n] = sa[m] * sw[n] * sum_k e4m3(qa[m,k]) * e4m3(qw[n,k]),
+ * BF16 out (ATOM A8W8 of "Kimi-K3 DSpark O-Proj-only MXFP4", section "Exact
+ * quantization coverage"; scales as in "Kimi-K3-DSpark-FP8-PTPC", section
+ * "Phase 1 FP8 PTPC Quantization").
+ *   qa [M, K], sa [M]; qw [N, K], sw [N] (the (out_features, 1) scale);
+ *   y_bf16 [M, N] out.  K > 0 and K % 128 == 0; qa, qw 16-byte aligned;
+ *   sa, sw 4-byte aligned; y_bf16 2-byte aligned.
+ */
+mx_status gemm_a8w8_ptpc_bf16(const void *qa, const float *sa, const void *qw, const float *sw,
+                              void *y_bf16, int64_t M, int64_t N, int64_t K, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MXGEMM_H */

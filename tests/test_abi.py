@@ -1,0 +1,98 @@
+"""The C-ABI library builds, loads and exports every entry point include/mxgemm.h
+declares; argument errors are reported on the host before anything reaches a
+device.  Runs without a GPU (no kernel is ever launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxgemm.h")
+
+
+@pytest.fixture(scope="module")
+def mx():
+    from block_scaled_precision_act_amd import build, mxgemm
+    if not os.path.exists(mxgemm.LIB_PATH):
+        build.build(verbose=False)
+    return mxgemm
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_four_path_entry_points():
+    names = declared_functions()
+    for n in ("mx_quant_act_bf16", "mx_gemm_a4w4_bf16", "ptpc_quant_act_fp8", "gemm_a8w8_ptpc_bf16"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(mx):
+    lib = ctypes.CDLL(mx.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert hasattr(mx, name) or name == "mx_status_string", name
+
+
+def test_version_and_status_strings(mx):
+    assert mx.mx_abi_version() == 1
+    for code in range(7):
+        assert mx.status_string(code).startswith("MX_")
+    assert mx.status_string(99) == "MX_ERROR_UNKNOWN"
+
+
+FAKE = 0x10000  # a non-null, 64K-aligned address that is never dereferenced
+
+
+def test_quantizer_argument_errors(mx):
+    assert mx.mx_quant_act_bf16(FAKE, -1, 64, FAKE, FAKE) == mx.MX_ERROR_INVALID_VALUE
+    assert mx.mx_quant_act_bf16(FAKE, 4, 48, FAKE, FAKE) == mx.MX_ERROR_UNSUPPORTED_SHAPE
+    assert mx.mx_quant_act_bf16(FAKE, 4, 0, FAKE, FAKE) == mx.MX_ERROR_UNSUPPORTED_SHAPE
+    assert mx.mx_quant_act_bf16(None, 4, 64, FAKE, FAKE) == mx.MX_ERROR_INVALID_VALUE
+    assert mx.mx_quant_act_bf16(FAKE + 2, 4, 64, FAKE, FAKE) == mx.MX_ERROR_MISALIGNED
+    assert mx.mx_quant_act_bf16(FAKE, 4, 64, FAKE + 8, FAKE) == mx.MX_ERROR_MISALIGNED
+    assert mx.mx_quant_act_bf16(None, 0, 64, None, None) == mx.MX_SUCCESS  # empty: no-op
+    assert mx.mx_quant_weight_f32(FAKE, 4, 40, FAKE, FAKE) == mx.MX_ERROR_UNSUPPORTED_SHAPE
+    assert mx.ptpc_quant_act_fp8(FAKE, 4, 12, FAKE, FAKE) == mx.MX_ERROR_UNSUPPORTED_SHAPE
+    assert mx.ptpc_quant_act_fp8(FAKE, 4, 64, FAKE, FAKE + 2) == mx.MX_ERROR_MISALIGNED
+    assert mx.ptpc_quant_act_fp8(FAKE, 4, 64, None, FAKE) == mx.MX_ERROR_INVALID_VALUE
+    assert mx.ptpc_quant_weight_f32(FAKE, -3, 64, FAKE, FAKE) == mx.MX_ERROR_INVALID_VALUE
+    assert mx.ptpc_quant_act_fp8(None, 0, 64, None, None) == mx.MX_SUCCESS
+
+
+def test_gemm_argument_errors(mx):
+    g4 = mx.mx_gemm_a4w4_bf16
+    assert g4(FAKE, FAKE, FAKE, FAKE, FAKE, -1, 8, 128) == mx.MX_ERROR_INVALID_VALUE
+    assert g4(FAKE, FAKE, FAKE, FAKE, FAKE, 8, -1, 128) == mx.MX_ERROR_INVALID_VALUE
+    assert g4(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 8, 96) == mx.MX_ERROR_UNSUPPORTED_SHAPE
+    assert g4(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 8, 0) == mx.MX_ERROR_UNSUPPORTED_SHAPE
+    assert g4(FAKE, None, FAKE, FAKE, FAKE, 8, 8, 128) == mx.MX_ERROR_INVALID_VALUE
+    assert g4(FAKE + 4, FAKE, FAKE, FAKE, FAKE, 8, 8, 128) == mx.MX_ERROR_MISALIGNED
+    assert g4(FAKE, FAKE + 2, FAKE, FAKE, FAKE, 8, 8, 128) == mx.MX_ERROR_MISALIGNED
+    assert g4(FAKE, FAKE, FAKE, FAKE, FAKE + 1, 8, 8, 128) == mx.MX_ERROR_MISALIGNED
+    assert g4(None, None, None, None, None, 0, 8, 128) == mx.MX_SUCCESS
+    assert g4(None, None, None, None, None, 8, 0, 128) == mx.MX_SUCCESS
+    assert mx.mx_gemm_a4w4_workspace_bytes(64, 7168, 8192) == 0
+    g8 = mx.gemm_a8w8_ptpc_bf16
+    assert g8(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 8, 64) == mx.MX_ERROR_UNSUPPORTED_SHAPE
+    assert g8(FAKE, FAKE + 2, FAKE, FAKE, FAKE, 8, 8, 128) == mx.MX_ERROR_MISALIGNED
+    assert g8(None, None, None, None, None, 0, 0, 128) == mx.MX_SUCCESS
+
+
+def test_valid_arguments_without_a_gpu_report_no_device(mx):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: valid arguments would launch a kernel")
+    assert mx.mx_quant_act_bf16(FAKE, 4, 64, FAKE, FAKE) == mx.MX_ERROR_DEVICE
+
+
+def test_tensor_helpers_reject_bad_inputs_before_the_library(mx):
+    import torch
+    with pytest.raises(TypeError):
+        mx.quant_act_mx(torch.zeros(2, 64, dtype=torch.float32))
+    with pytest.raises(ValueError):
+        mx.quant_act_mx(torch.zeros(2, 64, dtype=torch.bfloat16))  # not a device tensor
