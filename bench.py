@@ -1,0 +1,450 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-scaled o_proj layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20]
+
+Headline workload (one "step"): the A4W4 attention output projection at decode
+size - X [64, 8192] BF16 ~ N(0,1) is quantized dynamically to MXFP4
+(mx_quant_act_bf16) and multiplied with the pre-quantized MXFP4 weight
+[7168, 8192] + E8M0 scales [7168, 256] (mx_gemm_a4w4_bf16) into BF16 Y
+[64, 7168] (shapes: "Kimi-K3 DSpark O-Proj-only MXFP4", section "Exact
+quantization coverage"; M = 8 concurrent requests x 8 draft positions).  Every
+step reads a different copy of the weight (and activations) from a rotation
+large enough to defeat the 256 MB Infinity Cache, so weights stream from HBM.
+Steps are replayed from a HIP graph.  The printed JSON line also carries:
+  roofline      the GEMM kernel's achieved HBM bandwidth (algorithmic bytes per
+                launch / average launch time, HIP events on the launch stream)
+  cpu_baseline  the CPU oracle timed on the same layer on the host cores
+  also          the prefill layer (M = 8192), the PTPC FP8 A8W8 layers, the
+                M sweep and the quantizer kernels, each with its roofline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_FP4_TFLOPS = 10100.0   # dense MXFP4 / FP6 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # dense FP8 MFMA
+PEAK_FP16_TFLOPS = 2500.0   # dense FP16 / BF16 MFMA
+METRIC = "A4W4 o_proj GEMM TFLOP/s and GB/s (% roofline) at M=64 and M=8192, 1 GPU"
+ROTATE_MIN_BYTES = 512 << 20
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--kernel-reps", type=int, default=30, help="graph replays per kernel-timing measurement")
+    ap.add_argument("--no-extra", action="store_true", help="headline only (skip prefill / A8W8 / sweep)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="run each measured kernel a few times plus a plain copy of known size, for rocprofv3 --pmc")
+    return ap.parse_args()
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------- helpers
+def algorithmic_bytes(kind, M, N, K):
+    if kind == "a4w4":
+        return M * K // 2 + M * K // 32 + N * K // 2 + N * K // 32 + 2 * M * N
+    if kind == "a8w8":
+        return M * K + 4 * M + N * K + 4 * N + 2 * M * N
+    if kind == "mxq":
+        return 2 * M * K + M * K // 2 + M * K // 32
+    if kind == "ptpcq":
+        return 2 * M * K + M * K + 4 * M
+    raise ValueError(kind)
+
+
+class Ctx:
+    def __init__(self):
+        import torch
+        from block_scaled_precision_act_amd import mxgemm
+        if not os.path.exists(mxgemm.LIB_PATH):
+            from block_scaled_precision_act_amd import build
+            build.build()
+        self.torch = torch
+        self.mx = mxgemm
+        mxgemm.lib()
+        if not torch.cuda.is_available():
+            raise RuntimeError("bench.py needs a GPU")
+        self.dev = torch.device("cuda:0")
+        self.weights = {}
+
+    def weight(self, cfg_name, kind):
+        """Quantized weight of a config (generated on the host, converted on the GPU), cached."""
+        key = (cfg_name, kind)
+        if key not in self.weights:
+            from block_scaled_precision_act_amd import synth
+            w = self.torch.from_numpy(synth.make_weight(synth.CONFIGS[cfg_name])).to(self.dev)
+            self.weights[key] = self.mx.quant_weight_mx(w) if kind == "a4w4" else self.mx.quant_weight_ptpc(w)
+            del w
+        return self.weights[key]
+
+    def stream(self):
+        return self.torch.cuda.current_stream().cuda_stream
+
+    def capture(self, thunks):
+        torch = self.torch
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for f in thunks:
+                f()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for f in thunks:
+                f()
+        torch.cuda.synchronize()
+        return g
+
+    def event_ms(self, g, reps):
+        """Average ms per replay of graph g, HIP events on the replay stream."""
+        torch = self.torch
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g.replay()
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(reps):
+            g.replay()
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / reps
+
+
+def ok(status, what):
+    if status != 0:
+        from block_scaled_precision_act_amd import mxgemm
+        raise RuntimeError("%s failed: %s" % (what, mxgemm.status_string(status)))
+
+
+def dev_bf16(ctx, bits):
+    import numpy as np
+    return ctx.torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(ctx.torch.bfloat16).to(ctx.dev)
+
+
+def rotation_count(bytes_per_set, cap=64):
+    return max(2, min(cap, -(-ROTATE_MIN_BYTES // max(1, bytes_per_set))))
+
+
+# ----------------------------------------------------------------------------- A4W4 layer
+class A4W4Layer:
+    """R rotating copies of (X, quantized W, outputs) for one shape."""
+
+    def __init__(self, ctx, x_bits, qw, sw, rotate):
+        torch, mx = ctx.torch, ctx.mx
+        self.ctx = ctx
+        self.M, self.K = x_bits.shape
+        self.N = qw.shape[0]
+        x0 = dev_bf16(ctx, x_bits)
+        self.R = rotate
+        self.x = [x0] + [x0.clone() for _ in range(rotate - 1)]
+        self.qw = [qw] + [qw.clone() for _ in range(rotate - 1)]
+        self.sw = [sw] + [sw.clone() for _ in range(rotate - 1)]
+        M, N, K = self.M, self.N, self.K
+        self.qa = [torch.empty((M, K // 2), dtype=torch.uint8, device=ctx.dev) for _ in range(rotate)]
+        self.sa = [torch.empty((M, K // 32), dtype=torch.uint8, device=ctx.dev) for _ in range(rotate)]
+        self.y = [torch.empty((M, N), dtype=torch.bfloat16, device=ctx.dev) for _ in range(rotate)]
+        self.ws = mx.mx_gemm_a4w4_workspace_bytes(M, N, K)
+
+    def quant(self, r):
+        mx, ctx = self.ctx.mx, self.ctx
+        return lambda: ok(mx.mx_quant_act_bf16(self.x[r].data_ptr(), self.M, self.K, self.qa[r].data_ptr(),
+                                               self.sa[r].data_ptr(), ctx.stream()), "mx_quant_act_bf16")
+
+    def gemm(self, r):
+        mx, ctx = self.ctx.mx, self.ctx
+        return lambda: ok(mx.mx_gemm_a4w4_bf16(self.qa[r].data_ptr(), self.sa[r].data_ptr(), self.qw[r].data_ptr(),
+                                               self.sw[r].data_ptr(), self.y[r].data_ptr(), self.M, self.N, self.K,
+                                               None, 0, ctx.stream()), "mx_gemm_a4w4_bf16")
+
+    def step(self, r):
+        q, g = self.quant(r), self.gemm(r)
+        return lambda: (q(), g())
+
+
+class A8W8Layer:
+    def __init__(self, ctx, x_bits, qw, sw, rotate):
+        torch = ctx.torch
+        self.ctx = ctx
+        self.M, self.K = x_bits.shape
+        self.N = qw.shape[0]
+        x0 = dev_bf16(ctx, x_bits)
+        self.R = rotate
+        self.x = [x0] + [x0.clone() for _ in range(rotate - 1)]
+        self.qw = [qw] + [qw.clone() for _ in range(rotate - 1)]
+        self.sw = [sw] + [sw.clone() for _ in range(rotate - 1)]
+        M, N, K = self.M, self.N, self.K
+        self.qa = [torch.empty((M, K), dtype=torch.uint8, device=ctx.dev) for _ in range(rotate)]
+        self.sa = [torch.empty((M,), dtype=torch.float32, device=ctx.dev) for _ in range(rotate)]
+        self.y = [torch.empty((M, N), dtype=torch.bfloat16, device=ctx.dev) for _ in range(rotate)]
+
+    def quant(self, r):
+        mx, ctx = self.ctx.mx, self.ctx
+        return lambda: ok(mx.ptpc_quant_act_fp8(self.x[r].data_ptr(), self.M, self.K, self.qa[r].data_ptr(),
+                                                self.sa[r].data_ptr(), ctx.stream()), "ptpc_quant_act_fp8")
+
+    def gemm(self, r):
+        mx, ctx = self.ctx.mx, self.ctx
+        return lambda: ok(mx.gemm_a8w8_ptpc_bf16(self.qa[r].data_ptr(), self.sa[r].data_ptr(), self.qw[r].data_ptr(),
+                                                 self.sw[r].data_ptr(), self.y[r].data_ptr(), self.M, self.N, self.K,
+                                                 ctx.stream()), "gemm_a8w8_ptpc_bf16")
+
+    def step(self, r):
+        q, g = self.quant(r), self.gemm(r)
+        return lambda: (q(), g())
+
+
+def kernel_ms(ctx, layer, which, reps):
+    g = ctx.capture([getattr(layer, which)(r) for r in range(layer.R)])
+    return ctx.event_ms(g, reps) / layer.R
+
+
+def roofline_gemm(kind, M, N, K, ms):
+    flop = 2.0 * M * N * K
+    byt = algorithmic_bytes(kind, M, N, K)
+    tflops = flop / (ms * 1e-3) / 1e12
+    gbs = byt / (ms * 1e-3) / 1e9
+    peak_c = PEAK_FP4_TFLOPS if kind == "a4w4" else PEAK_FP8_TFLOPS
+    t_hbm = byt / (PEAK_HBM_GBS * 1e9)
+    t_mfma = flop / (peak_c * 1e12)
+    if t_hbm >= t_mfma:
+        return {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None, "kernel_us": round(ms * 1e3, 3),
+                "tflops": round(tflops, 2), "alg_bytes_per_launch": byt}
+    return {"bound": "mfma", "achieved": round(tflops, 1), "peak": peak_c, "unit": "TFLOP/s",
+            "frac": round(tflops / peak_c, 4), "traffic": None, "kernel_us": round(ms * 1e3, 3),
+            "gbs": round(gbs, 1), "alg_flop_per_launch": flop}
+
+
+def roofline_quant(kind, M, K, ms):
+    byt = algorithmic_bytes(kind, M, 0, K)
+    gbs = byt / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4), "kernel_us": round(ms * 1e3, 3), "alg_bytes_per_launch": byt}
+
+
+def pmc_traffic(kernel_key):
+    """HBM traffic per launch from the committed rocprofv3 --pmc summary, if it
+    was taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_hash") != source_hash():
+        return None
+    return d.get("kernels", {}).get(kernel_key)
+
+
+def source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_scaled_precision_act_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+# ----------------------------------------------------------------------------- workloads
+def make_a4w4(ctx, cfg_name, M=None, rotate=None):
+    from block_scaled_precision_act_amd import synth
+    cfg = synth.CONFIGS[cfg_name]
+    x_bits = synth.make_activations(cfg, M)
+    qw, sw = ctx.weight(cfg_name, "a4w4")  # offline weight conversion, on the GPU
+    Mx, K = x_bits.shape
+    per_set = algorithmic_bytes("a4w4", Mx, cfg["N"], K) + 2 * Mx * K
+    R = rotate or rotation_count(per_set)
+    return A4W4Layer(ctx, x_bits, qw, sw, R)
+
+
+def make_a8w8(ctx, cfg_name, rotate=None):
+    from block_scaled_precision_act_amd import synth
+    cfg = synth.CONFIGS[cfg_name]
+    x_bits = synth.make_activations(cfg)
+    qw, sw = ctx.weight(cfg_name, "a8w8")
+    Mx, K = x_bits.shape
+    per_set = algorithmic_bytes("a8w8", Mx, cfg["N"], K) + 2 * Mx * K
+    R = rotate or rotation_count(per_set)
+    return A8W8Layer(ctx, x_bits, qw, sw, R)
+
+
+def time_steps(ctx, layer, steps, warmup):
+    """Wall-clock time of exactly `steps` layer steps replayed from graphs."""
+    torch = ctx.torch
+    R = layer.R
+    full = ctx.capture([layer.step(r) for r in range(R)])
+    rem = steps % R
+    tail = ctx.capture([layer.step(r) for r in range(rem)]) if rem else None
+    for _ in range(-(-warmup // R)):
+        full.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps // R):
+        full.replay()
+    if tail is not None:
+        tail.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def layer_entry(ctx, layer, kind, args, label):
+    M, N, K = layer.M, layer.N, layer.K
+    gemm_ms = kernel_ms(ctx, layer, "gemm", args.kernel_reps)
+    quant_ms = kernel_ms(ctx, layer, "quant", args.kernel_reps)
+    step_ms = time_steps(ctx, layer, max(layer.R, 40), 10)
+    e = {"workload": label, "M": M, "N": N, "K": K, "rotation": layer.R,
+         "layer_ms": round(step_ms, 5), "layer_tflops": round(2.0 * M * N * K / (step_ms * 1e-3) / 1e12, 2),
+         "gemm": roofline_gemm(kind, M, N, K, gemm_ms),
+         "quant": roofline_quant("mxq" if kind == "a4w4" else "ptpcq", M, K, quant_ms)}
+    if kind == "a8w8":
+        e["gemm"]["note"] = ("E4M3 operands widened exactly to FP16 and run on FP16 MFMA (peak %.0f TFLOP/s); "
+                             "frac is against the FP8 peak" % PEAK_FP16_TFLOPS)
+    return e
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+def cpu_baseline():
+    import numpy as np
+    import oracle
+    from block_scaled_precision_act_amd import synth
+    cfg = synth.CONFIGS["oproj_decode_a4w4"]
+    threads = min(16, oracle.default_threads())
+    x_bits = synth.make_activations(cfg)
+    qw, sw = oracle.mx_quant_f32(synth.make_weight(cfg), nthreads=threads)  # offline, not timed
+    M, N, K = cfg["M"], cfg["N"], cfg["K"]
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        qa, sa = oracle.mx_quant_bf16(x_bits, nthreads=threads)
+        oracle.gemm_a4w4_at(qa, sa, qw, sw, nthreads=threads)
+        reps += 1
+        if time.perf_counter() - t0 > 8.0 or reps >= 5:
+            break
+    sec = (time.perf_counter() - t0) / reps
+    return {"value": round(2.0 * M * N * K / sec / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "full o_proj decode layer (MXFP4 quantization of X [64, 8192] + exact A4W4 GEMM against "
+                      "W [7168, 8192]), %d repetition(s), %.2f s each" % (reps, sec)}
+
+
+# ----------------------------------------------------------------------------- profile pass
+def profile_pass(ctx):
+    """Each measured kernel a few times + a plain device copy of known size,
+    for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs."""
+    torch = ctx.torch
+    src = torch.empty(256 << 20, dtype=torch.uint8, device=ctx.dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dec = make_a4w4(ctx, "oproj_decode_a4w4")
+    for r in range(min(4, dec.R)):
+        dec.quant(r)()
+        dec.gemm(r)()
+    torch.cuda.synchronize()
+    pre = make_a4w4(ctx, "oproj_prefill_a4w4", rotate=2)
+    for r in range(2):
+        pre.quant(r)()
+        pre.gemm(r)()
+    torch.cuda.synchronize()
+    log("profile pass done (copy of %d bytes x3)" % src.numel())
+
+
+# ----------------------------------------------------------------------------- main
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures the layer on one GPU only: the library has no multi-GPU path "
+              "(got --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+    if args.steps <= 0 or args.warmup < 0:
+        print("--steps must be > 0 and --warmup >= 0", file=sys.stderr)
+        sys.exit(2)
+    ctx = Ctx()
+    torch = ctx.torch
+    if args.profile_pass:
+        profile_pass(ctx)
+        return
+
+    log("generating the decode workload (X [64, 8192], W [7168, 8192])")
+    dec = make_a4w4(ctx, "oproj_decode_a4w4")
+    log("rotation: %d weight/activation copies" % dec.R)
+    gemm_ms = kernel_ms(ctx, dec, "gemm", args.kernel_reps)
+    quant_ms = kernel_ms(ctx, dec, "quant", args.kernel_reps)
+    log("decode GEMM %.2f us, quant %.2f us" % (gemm_ms * 1e3, quant_ms * 1e3))
+
+    ms_per_step = time_steps(ctx, dec, args.steps, args.warmup)
+    M, N, K = dec.M, dec.N, dec.K
+    value = 2.0 * M * N * K / (ms_per_step * 1e-3) / 1e12
+    log("step %.3f us -> %.2f TFLOP/s" % (ms_per_step * 1e3, value))
+
+    roof = roofline_gemm("a4w4", M, N, K, gemm_ms)
+    roof["traffic"] = pmc_traffic("gemm_decode_fp4_m64")
+    roof["kernel"] = "gemm_decode_kernel<FP4, MF=4, NW=8>"
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "mxfp4 (e2m1 x e2m1, e8m0 scales, fp32 accumulate, bf16 out)",
+        "data": "synthetic (seeded SplitMix64; X ~ N(0,1) bf16, W ~ N(0,0.01) fp32 quantized on the GPU)",
+        "config": {"workload": "A4W4 o_proj decode layer: BF16 X [64, 8192] -> dynamic MXFP4 -> A4W4 GEMM vs "
+                               "MXFP4 W [7168, 8192] + E8M0 [7168, 256] -> BF16 Y [64, 7168]",
+                   "M": M, "N": N, "K": K, "rotation": dec.R, "graph_replay": True},
+        "roofline": roof,
+        "layer_breakdown_us": {"quant": round(quant_ms * 1e3, 3), "gemm": round(gemm_ms * 1e3, 3)},
+    }
+    del dec
+    torch.cuda.empty_cache()
+
+    if not args.no_extra:
+        also = {}
+        log("prefill A4W4 (M = 8192)")
+        pre = make_a4w4(ctx, "oproj_prefill_a4w4", rotate=2)
+        also["a4w4_prefill_m8192"] = layer_entry(ctx, pre, "a4w4", args, "oproj_prefill_a4w4")
+        also["a4w4_prefill_m8192"]["gemm"]["traffic"] = pmc_traffic("gemm_tile_fp4_m8192")
+        del pre
+        ctx.weights.clear()
+        torch.cuda.empty_cache()
+        sweep = {}
+        for Ms in (1, 16, 128, 512, 2048):
+            log("outlier sweep M = %d" % Ms)
+            lay = make_a4w4(ctx, "msweep_outlier_a4w4", M=Ms)
+            sweep["M=%d" % Ms] = layer_entry(ctx, lay, "a4w4", args, "msweep_outlier_a4w4")
+            del lay
+            torch.cuda.empty_cache()
+        also["a4w4_msweep_outliers"] = sweep
+        ctx.weights.clear()
+        for name in ("ptpc_a8w8_m64", "ptpc_a8w8_m8192"):
+            log("A8W8 %s" % name)
+            lay = make_a8w8(ctx, name, rotate=2 if name.endswith("8192") else None)
+            also[name] = layer_entry(ctx, lay, "a8w8", args, name)
+            del lay
+            torch.cuda.empty_cache()
+        out["also"] = also
+
+    if not args.no_cpu_baseline:
+        log("CPU oracle baseline")
+        out["cpu_baseline"] = cpu_baseline()
+    out["device"] = torch.cuda.get_device_name(0)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

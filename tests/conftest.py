@@ -17,3 +17,16 @@ def orc():
     import oracle
     oracle.build()
     return oracle
+
+
+@pytest.fixture(scope="session")
+def mx():
+    """The HIP library binding, built in-tree first if it is missing; GPU tests only."""
+    import torch
+    from block_scaled_precision_act_amd import mxgemm
+    if not os.path.exists(mxgemm.LIB_PATH):
+        from block_scaled_precision_act_amd import build
+        build.build(verbose=False)
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    mxgemm.lib()
+    return mxgemm

@@ -19,15 +19,6 @@ pytestmark = pytest.mark.gpu
 NT = 16  # oracle threads
 
 
-@pytest.fixture(scope="module")
-def mx():
-    import torch
-    from block_scaled_precision_act_amd import mxgemm
-    assert torch.cuda.is_available(), "GPU tests need a GPU"
-    mxgemm.lib()
-    return mxgemm
-
-
 @functools.lru_cache(maxsize=None)
 def _weight_mx(name):
     import oracle

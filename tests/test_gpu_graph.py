@@ -1,0 +1,73 @@
+"""The entry points enqueue only kernels (no allocation, no memset, no host sync), so a
+whole layer can be captured into a HIP graph.  Each replay, with eager work and host
+synchronizations in between, must reproduce the eager result bit for bit."""
+import numpy as np
+import pytest
+
+from block_scaled_precision_act_amd import synth
+from parity import bf16_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _replays_match(mx, torch, thunk, outs):
+    thunk()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        thunk()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        thunk()
+    for rep in range(4):
+        for o in outs:
+            o.zero_()
+        junk = torch.randn(1 << 20, device="cuda").sum()  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert torch.equal(o.view(torch.uint8), e.view(torch.uint8)), "replay %d differs" % rep
+        del junk
+
+
+@pytest.mark.parametrize("M", [64, 300])
+def test_a4w4_layer_graph_replay(mx, M):
+    import torch
+    K, N = 1024, 512
+    x = bf16_dev(synth.act_normal(61, M, K))
+    qw, sw = mx.quant_weight_mx(torch.from_numpy(synth.weight_normal(62, N, K, 0.02)).cuda())
+    qa = torch.empty((M, K // 2), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((M, K // 32), dtype=torch.uint8, device="cuda")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+    def layer():
+        s = torch.cuda.current_stream().cuda_stream
+        assert mx.mx_quant_act_bf16(x.data_ptr(), M, K, qa.data_ptr(), sa.data_ptr(), s) == 0
+        assert mx.mx_gemm_a4w4_bf16(qa.data_ptr(), sa.data_ptr(), qw.data_ptr(), sw.data_ptr(), y.data_ptr(),
+                                    M, N, K, None, 0, s) == 0
+
+    _replays_match(mx, torch, layer, [qa, sa, y])
+
+
+@pytest.mark.parametrize("M", [64, 300])
+def test_a8w8_layer_graph_replay(mx, M):
+    import torch
+    K, N = 1024, 512
+    x = bf16_dev(synth.act_normal(63, M, K))
+    qw, sw = mx.quant_weight_ptpc(torch.from_numpy(synth.weight_normal(64, N, K, 0.01)).cuda())
+    qa = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((M,), dtype=torch.float32, device="cuda")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+    def layer():
+        s = torch.cuda.current_stream().cuda_stream
+        assert mx.ptpc_quant_act_fp8(x.data_ptr(), M, K, qa.data_ptr(), sa.data_ptr(), s) == 0
+        assert mx.gemm_a8w8_ptpc_bf16(qa.data_ptr(), sa.data_ptr(), qw.data_ptr(), sw.data_ptr(), y.data_ptr(),
+                                      M, N, K, s) == 0
+
+    _replays_match(mx, torch, layer, [qa, sa, y])

@@ -12,15 +12,6 @@ from parity import bf16_dev, to_dev
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(scope="module")
-def mx():
-    import torch
-    from block_scaled_precision_act_amd import mxgemm
-    assert torch.cuda.is_available(), "GPU tests need a GPU"
-    mxgemm.lib()  # fails loudly if the library is not built
-    return mxgemm
-
-
 def _gpu_mx_bf16(mx, bits):
     q, s = mx.quant_act_mx(bf16_dev(bits))
     return q.cpu().numpy(), s.cpu().numpy()
