@@ -159,7 +159,8 @@ class A4W4Layer:
         self.qa = [torch.empty((M, K // 2), dtype=torch.uint8, device=ctx.dev) for _ in range(rotate)]
         self.sa = [torch.empty((M, K // 32), dtype=torch.uint8, device=ctx.dev) for _ in range(rotate)]
         self.y = [torch.empty((M, N), dtype=torch.bfloat16, device=ctx.dev) for _ in range(rotate)]
-        self.ws = mx.mx_gemm_a4w4_workspace_bytes(M, N, K)
+        self.ws = mx.mx_gemm_a4w4_workspace_bytes(M, N, K)  # shared by the steps (they run in stream order)
+        self.wbuf = torch.empty(max(self.ws, 16), dtype=torch.uint8, device=ctx.dev)
 
     def quant(self, r):
         mx, ctx = self.ctx.mx, self.ctx
@@ -170,7 +171,7 @@ class A4W4Layer:
         mx, ctx = self.ctx.mx, self.ctx
         return lambda: ok(mx.mx_gemm_a4w4_bf16(self.qa[r].data_ptr(), self.sa[r].data_ptr(), self.qw[r].data_ptr(),
                                                self.sw[r].data_ptr(), self.y[r].data_ptr(), self.M, self.N, self.K,
-                                               None, 0, ctx.stream()), "mx_gemm_a4w4_bf16")
+                                               self.wbuf.data_ptr(), self.ws, ctx.stream()), "mx_gemm_a4w4_bf16")
 
     def step(self, r):
         q, g = self.quant(r), self.gemm(r)
@@ -398,7 +399,7 @@ def main():
 
     roof = roofline_gemm("a4w4", M, N, K, gemm_ms)
     roof["traffic"] = pmc_traffic("gemm_decode_fp4_m64")
-    roof["kernel"] = "gemm_decode_kernel<FP4, MF=4, NW=8>"
+    roof["kernel"] = "gemm_decode_lds_fp4<4>"
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak",

@@ -87,10 +87,8 @@ MX_API mx_status mx_quant_weight_f32(const float* w, int64_t N, int64_t K, void*
 }
 
 MX_API size_t mx_gemm_a4w4_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-    (void)M;
-    (void)N;
-    (void)K;
-    return 0;
+    if (check_gemm(M, N, K) != MX_SUCCESS || M == 0 || N == 0) return 0;
+    return mx::gemm_a4w4_workspace_bytes(M, N, K);
 }
 
 MX_API mx_status mx_gemm_a4w4_bf16(const void* qa, const void* sa, const void* qw, const void* sw, void* y_bf16,
@@ -100,12 +98,13 @@ MX_API mx_status mx_gemm_a4w4_bf16(const void* qa, const void* sa, const void* q
     if (st != MX_SUCCESS) return st;
     if (M == 0 || N == 0) return MX_SUCCESS;
     if (!qa || !sa || !qw || !sw || !y_bf16) return MX_ERROR_INVALID_VALUE;
-    if (workspace_bytes < mx_gemm_a4w4_workspace_bytes(M, N, K)) return MX_ERROR_WORKSPACE;
-    (void)workspace;
-    if (!aligned(qa, 16) || !aligned(qw, 16) || !aligned(sa, 4) || !aligned(sw, 4) || !aligned(y_bf16, 2))
+    const size_t need = mx_gemm_a4w4_workspace_bytes(M, N, K);
+    if (workspace_bytes < need || (need && !workspace)) return MX_ERROR_WORKSPACE;
+    if (!aligned(qa, 16) || !aligned(qw, 16) || !aligned(sa, 4) || !aligned(sw, 4) || !aligned(y_bf16, 2) ||
+        (need && !aligned(workspace, 16)))
         return MX_ERROR_MISALIGNED;
     if ((st = check_device()) != MX_SUCCESS) return st;
-    return launched(mx::launch_gemm_a4w4(qa, sa, qw, sw, y_bf16, M, N, K, reinterpret_cast<hipStream_t>(stream)));
+    return launched(mx::launch_gemm_a4w4(qa, sa, qw, sw, y_bf16, M, N, K, workspace, reinterpret_cast<hipStream_t>(stream)));
 }
 
 static mx_status quant_ptpc(bool f32, const void* x, int64_t rows, int64_t K, void* q, float* s, void* stream) {

@@ -187,6 +187,181 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(const uint8_t* __r
 }
 
 // ============================================================================
+// Decode path, LDS-staged (FP4, K % 512 == 0).
+// One workgroup (4 waves) per 32 output columns.  A stage is a 512-K slab of
+// the workgroup's operands: the 32 weight rows and the 16*MF activation rows,
+// 256 code bytes each, plus their 16 scale bytes.  Each wave instruction loads
+// 1 KB = 4 rows x 256 contiguous bytes (fully coalesced); kInFlight stages of
+// loads are kept in registers, each is written to a double-buffered LDS tile
+// just before it is consumed.  In LDS the 16-byte chunks of a row are XOR-
+// swizzled by (row % 16), so the MFMA-layout ds_read_b128 (16 rows, same
+// logical chunk) touches 16 distinct bank groups.  Wave w multiplies chunk w
+// (128 K) of every slab; the four partial tiles are summed through LDS in a
+// fixed order at the end (deterministic).
+// ============================================================================
+template <int MF>
+struct DecodeLds {
+    static constexpr int kNT = 32;                      // output columns per workgroup
+    static constexpr int kSlab = 256;                   // code bytes per row per stage
+    static constexpr int kRows = kNT + 16 * MF;         // weight rows, then activation rows
+    static constexpr int kCode = kRows * kSlab;
+    static constexpr int kStage = kCode + kRows * 16;   // + 16 scale bytes per row
+    static constexpr int kCodeLoads = kRows / 16;       // 16-byte loads per lane per stage
+    static constexpr int kScaleRows = kRows / 4;        // scale rows loaded per wave
+    static constexpr int kInFlight = 3;                 // stages of loads in registers
+    static_assert(kRows % 16 == 0 && kScaleRows <= 64, "stage shape");
+    static_assert((kStage % 256) == 0, "stage alignment");
+};
+
+template <int MF>
+struct DecodeRegs {
+    uint4 code[DecodeLds<MF>::kCodeLoads];
+    uint4 scale;
+};
+
+template <int MF>
+__global__ __launch_bounds__(256) void gemm_decode_lds_fp4(const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa,
+                                                           const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw,
+                                                           uint16_t* __restrict__ y, int M, int N, int K) {
+    using C = DecodeLds<MF>;
+    constexpr int NF = 2;
+    constexpr int V = MF * NF * 4;
+    constexpr int kLds = 2 * C::kStage > 4 * V * 64 * 4 ? 2 * C::kStage : 4 * V * 64 * 4;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r16 = lane & 15, q = lane >> 4;
+    const int n0 = blockIdx.x * C::kNT;
+    const int64_t KB = (int64_t)K / 2, KS = (int64_t)K / 32;
+    const int nslab = K / 512;
+
+    // load i of this lane covers row group g (4 rows): the first kWLoads loads of every wave
+    // are weight rows (streamed once: non-temporal, so they do not push the shared
+    // activations out of L2), the rest activation rows; lane -> row 4g + lane/16,
+    // logical chunk lane%16
+    constexpr int kWLoads = C::kNT / 16;
+    const uint8_t* src[C::kCodeLoads];
+    int dst[C::kCodeLoads];
+#pragma unroll
+    for (int i = 0; i < C::kCodeLoads; ++i) {
+        const int g = i < kWLoads ? wave * kWLoads + i : C::kNT / 4 + wave * (C::kCodeLoads - kWLoads) + (i - kWLoads);
+        const int rho = 4 * g + (lane >> 4);
+        const uint8_t* row = rho < C::kNT ? qw + (int64_t)min(n0 + rho, N - 1) * KB
+                                          : qa + (int64_t)min(rho - C::kNT, M - 1) * KB;
+        src[i] = row + 16 * (lane & 15);
+        dst[i] = rho * C::kSlab + 16 * ((lane & 15) ^ (rho & 15));
+    }
+    // scale load: lane < kScaleRows fetches the 16 scale bytes of row wave*kScaleRows + lane;
+    // the other lanes repeat the last row's load (never stashed), so the load is issued
+    // unconditionally and the compiler's vmcnt bookkeeping stays exact
+    const bool s_on = lane < C::kScaleRows;
+    const int srho = wave * C::kScaleRows + (s_on ? lane : C::kScaleRows - 1);
+    const uint8_t* ssrc = srho < C::kNT ? sw + (int64_t)min(n0 + srho, N - 1) * KS
+                                        : sa + (int64_t)min(srho - C::kNT, M - 1) * KS;
+
+    auto fetch = [&](DecodeRegs<MF>& r, int s) {
+#pragma unroll
+        for (int i = 0; i < C::kCodeLoads; ++i)
+            r.code[i] = i < kWLoads ? ldg16_stream(src[i] + (int64_t)s * C::kSlab) : ldg16(src[i] + (int64_t)s * C::kSlab);
+        r.scale = ldg16(ssrc + (int64_t)s * 16);
+    };
+    auto stash = [&](const DecodeRegs<MF>& r, int buf) {
+        uint8_t* st = lds + buf * C::kStage;
+#pragma unroll
+        for (int i = 0; i < C::kCodeLoads; ++i) *reinterpret_cast<uint4*>(st + dst[i]) = r.code[i];
+        if (s_on) *reinterpret_cast<uint4*>(st + C::kCode + srho * 16) = r.scale;
+    };
+
+    v4f acc[MF][NF];
+#pragma unroll
+    for (int i = 0; i < MF; ++i)
+#pragma unroll
+        for (int j = 0; j < NF; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    // this lane's physical chunk in every row it reads: logical chunk 4*wave + q, swizzled
+    const int pchunk = (4 * wave + q) ^ r16;
+    auto consume = [&](int buf) {
+        const uint8_t* st = lds + buf * C::kStage;
+        uint4 wv[NF];
+        int wsc[NF];
+#pragma unroll
+        for (int j = 0; j < NF; ++j) {
+            const int rho = 16 * j + r16;
+            wv[j] = *reinterpret_cast<const uint4*>(st + rho * C::kSlab + 16 * pchunk);
+            wsc[j] = st[C::kCode + rho * 16 + 4 * wave + q];
+        }
+#pragma unroll
+        for (int i = 0; i < MF; ++i) {
+            const int rho = C::kNT + 16 * i + r16;
+            const uint4 av = *reinterpret_cast<const uint4*>(st + rho * C::kSlab + 16 * pchunk);
+            const int asc = st[C::kCode + rho * 16 + 4 * wave + q];
+#pragma unroll
+            for (int j = 0; j < NF; ++j)
+                acc[i][j] = mfma16<kFmtFP4, 0>(fp4_operand(av), fp4_operand(wv[j]), acc[i][j], asc, wsc[j]);
+        }
+    };
+
+    // Stage s: stash its registers into LDS buffer s%2, barrier (which also retires the
+    // reads of that buffer from stage s-2), refill the registers with stage s+3, multiply.
+    // The steady-state loop fetches unconditionally, so the compiler's vmcnt bookkeeping
+    // stays exact (each stash waits only for its own stage); the tail is peeled.
+    DecodeRegs<MF> r0, r1, r2;
+    fetch(r0, 0);
+    fetch(r1, min(1, nslab - 1));  // unconditional (a short K re-reads its last slab)
+    fetch(r2, min(2, nslab - 1));
+    int s = 0;
+    for (; s + 5 < nslab; s += 3) {
+        stash(r0, s & 1);
+        __syncthreads();
+        fetch(r0, s + 3);
+        consume(s & 1);
+        stash(r1, (s + 1) & 1);
+        __syncthreads();
+        fetch(r1, s + 4);
+        consume((s + 1) & 1);
+        stash(r2, s & 1);
+        __syncthreads();
+        fetch(r2, s + 5);
+        consume(s & 1);
+    }
+    // tail: stages s .. nslab-1 (at most 5); r0, r1, r2 hold stages s, s+1, s+2 where they exist
+    for (int t = 0; s + t < nslab; t += 3) {
+        const int a = s + t;
+        stash(r0, a & 1);
+        __syncthreads();
+        if (a + 3 < nslab) fetch(r0, a + 3);
+        consume(a & 1);
+        if (a + 1 >= nslab) break;
+        stash(r1, (a + 1) & 1);
+        __syncthreads();
+        if (a + 4 < nslab) fetch(r1, a + 4);
+        consume((a + 1) & 1);
+        if (a + 2 >= nslab) break;
+        stash(r2, a & 1);
+        __syncthreads();
+        consume(a & 1);
+    }
+
+    // fixed-order sum of the four waves' partial tiles
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(lds);
+#pragma unroll
+    for (int i = 0; i < MF; ++i)
+#pragma unroll
+        for (int j = 0; j < NF; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[(wave * V + (i * NF + j) * 4 + r) * 64 + lane] = acc[i][j][r];
+    __syncthreads();
+    for (int e = threadIdx.x; e < V * 64; e += 256) {
+        const int v = e >> 6, l = e & 63;
+        const float sum = ((red[v * 64 + l] + red[(V + v) * 64 + l]) + red[(2 * V + v) * 64 + l]) + red[(3 * V + v) * 64 + l];
+        const int r = v & 3, ij = v >> 2, j = ij % NF, i = ij / NF;
+        const int m = 16 * i + 4 * (l >> 4) + r, n = n0 + 16 * j + (l & 15);
+        if (m < M && n < N) y[(int64_t)m * N + n] = (uint16_t)bf16_rne(sum);
+    }
+}
+
+// ============================================================================
 // Tile path (large M, MFMA-bound).
 // 256 x 256 output tile per workgroup of 4 waves (2 x 2, 128 x 128 each, 4 x 4
 // fragments of 32 x 32).  Each K-stage moves 128 code bytes per row of both
@@ -356,7 +531,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(const uint8_t* __rest
 
     // epilogue: lane holds, per fragment (f, g) and j, Y[m][n .. n+3] with
     // m = m0 + 128wm + 32g + l32 and n = n0 + 128wn + 32f + 8j + 4h
-    const bool vec_ok = (N & 3) == 0;
+    const bool vec_ok = (N & 3) == 0 && (reinterpret_cast<uintptr_t>(y) & 7) == 0;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
         const int m = m0 + 128 * wm + 32 * g + l32;
@@ -389,6 +564,408 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(const uint8_t* __rest
     }
 }
 
+// ============================================================================
+// Tile path, DMA-staged (FP4, K % 256 == 0).
+// 256 x 256 output tile, 4 waves (2 x 2, 128 x 128 each, 4 x 4 fragments of
+// 32 x 32).  A stage is K = 128 (64 code bytes per row) of both operands plus
+// their scale dwords; stages are copied global -> LDS with global_load_lds
+// (1 KB per wave instruction = 16 rows x 64 bytes, coalesced; 4-byte scale
+// DMAs) into a ring of STAGES buffers, so STAGES - 1 stages are in flight while one is
+// multiplied and no VGPRs are spent on staging (all 256 accumulators stay in
+// AGPRs).  In LDS a row's four 16-byte chunks are XOR-swizzled by (row/4)%4,
+// which spreads the 32 rows of an MFMA-layout ds_read_b128 over all banks.
+// The LDS reads are inline asm and every wait is explicit: per wave vmcnt for
+// its own DMAs of the stage, then a plain s_barrier.
+// MFMA K-permutation within a stage: lane group h (lanes 32h..32h+31) holds
+// chunks 2h and 2h+1 of its row; MFMA t multiplies chunk 2h+t, so the two
+// MFMAs of a stage cover chunks {0,2} and {1,3}; the row's scale dword (4
+// blocks) shifted right by 16h gives blocks 2h, 2h+1 in bytes 0, 1 (op_sel t).
+// ============================================================================
+namespace tile_dma {
+constexpr int kRows = 256;
+constexpr int kRowBytes = 64;                   // code bytes per row per stage (K = 128)
+constexpr int kOpBytes = kRows * kRowBytes;     // 16 KB per operand per stage
+constexpr int kScaleOff = 2 * kOpBytes;         // scale dwords: W then X, 1 KB each
+constexpr int kStage = 2 * kOpBytes + 2 * kRows * 4;
+constexpr int kLoadsPerStage = 10;              // per wave: 2 x 4 code DMAs + 2 scale DMAs
+}  // namespace tile_dma
+
+template <int STAGES>
+__global__ __launch_bounds__(256, 1) void gemm_tile_dma_fp4(const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa,
+                                                            const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw,
+                                                            uint16_t* __restrict__ y, int M, int N, int K, int tiles_m,
+                                                            int tiles_n) {
+    using namespace tile_dma;
+    constexpr int kStages = STAGES;
+    static_assert(kStages >= 3 && kStages * kStage <= 160 * 1024, "LDS ring");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * kStage];
+
+    int tm, tn;
+    tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * kTileM, n0 = tn * kTileN;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wn = wave & 1, wm = wave >> 1;
+    const int l32 = lane & 31, h = lane >> 5;
+    const int64_t KB = (int64_t)K / 2, KS = (int64_t)K / 32;
+    const int nst = (int)(KB / kRowBytes);
+
+    // code DMA sources: instruction i (0..3) of this wave covers rows 16*(4*wave+i) + lane/4;
+    // the lane fetches logical chunk (lane%4) ^ ((row/4)%4) into physical slot lane%4
+    const uint8_t* wsrc[4];
+    const uint8_t* xsrc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 16 * (4 * wave + i) + (lane >> 2);
+        const int chunk = (lane & 3) ^ ((row >> 2) & 3);
+        wsrc[i] = qw + (int64_t)min(n0 + row, N - 1) * KB + 16 * chunk;
+        xsrc[i] = qa + (int64_t)min(m0 + row, M - 1) * KB + 16 * chunk;
+    }
+    // scale DMA sources: row 64*wave + lane, one dword (4 blocks) per stage
+    const uint8_t* wssrc = sw + (int64_t)min(n0 + 64 * wave + lane, N - 1) * KS;
+    const uint8_t* xssrc = sa + (int64_t)min(m0 + 64 * wave + lane, M - 1) * KS;
+
+    auto issue = [&](int s) {
+        uint8_t* st = lds + (s % kStages) * kStage;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            g2lds16(wsrc[i] + (int64_t)s * kRowBytes, st + (4 * wave + i) * 1024);
+            g2lds16(xsrc[i] + (int64_t)s * kRowBytes, st + kOpBytes + (4 * wave + i) * 1024);
+        }
+        g2lds4(wssrc + 4 * s, st + kScaleOff + wave * 256);
+        g2lds4(xssrc + 4 * s, st + kScaleOff + kRows * 4 + wave * 256);
+    };
+
+    v16f acc[4][4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[f][g][r] = 0.f;
+
+#pragma unroll
+    for (int s = 0; s < kStages - 1; ++s)
+        if (s < nst) issue(s);
+
+    // per-lane LDS offsets inside a stage
+    int woff[4][2], xoff[4][2], wsoff[4], xsoff[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+        const int wr = 128 * wn + 32 * f + l32, xr = 128 * wm + 32 * f + l32;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            woff[f][t] = wr * kRowBytes + 16 * ((2 * h + t) ^ ((wr >> 2) & 3));
+            xoff[f][t] = kOpBytes + xr * kRowBytes + 16 * ((2 * h + t) ^ ((xr >> 2) & 3));
+        }
+        wsoff[f] = kScaleOff + wr * 4;
+        xsoff[f] = kScaleOff + kRows * 4 + xr * 4;
+    }
+    const uint32_t base = lds_addr(lds);
+    const int shift = 16 * h;
+
+    for (int s = 0; s < nst; ++s) {
+        const int ahead = min(kStages - 2, nst - 1 - s);
+        __builtin_amdgcn_sched_barrier(0);
+        if (ahead >= 2) wait_vmcnt<2 * kLoadsPerStage>();
+        else if (ahead == 1) wait_vmcnt<kLoadsPerStage>();
+        else wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        if (s + kStages - 1 < nst) issue(s + kStages - 1);
+        const uint32_t sb = base + (s % kStages) * kStage;
+        uint32_t wsc[4], xsc[4];
+        v4u wv[2][4], xv[2][4];
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+            wsc[f] = lds_read4(sb + wsoff[f]);
+            xsc[f] = lds_read4(sb + xsoff[f]);
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int f = 0; f < 4; ++f) {
+                wv[t][f] = lds_read16(sb + woff[f][t]);
+                xv[t][f] = lds_read16(sb + xoff[f][t]);
+            }
+        // LDS results return in issue order: lgkmcnt(8) covers the scales and the t = 0 operands
+        lds_wait_first(wv[0], xv[0], wsc, xsc);
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                acc[f][g] = mfma32<kFmtFP4, 0>(fp4_operand(wv[0][f]), fp4_operand(xv[0][g]), acc[f][g],
+                                               (int)(wsc[f] >> shift), (int)(xsc[g] >> shift));
+        __builtin_amdgcn_sched_barrier(0);
+        lds_wait_rest(wv[1], xv[1]);
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                acc[f][g] = mfma32<kFmtFP4, 1>(fp4_operand(wv[1][f]), fp4_operand(xv[1][g]), acc[f][g],
+                                               (int)(wsc[f] >> shift), (int)(xsc[g] >> shift));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // epilogue (same layout as gemm_tile_kernel): Y[m][n .. n+3] per register quad
+    const bool vec_ok = (N & 3) == 0 && (reinterpret_cast<uintptr_t>(y) & 7) == 0;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const int m = m0 + 128 * wm + 32 * g + l32;
+        if (m >= M) continue;
+        uint16_t* yrow = y + (int64_t)m * N;
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int n = n0 + 128 * wn + 32 * f + 8 * j + 4 * h;
+                if (vec_ok && n + 3 < N) {
+                    uint2 pk;
+                    pk.x = bf16_rne(acc[f][g][4 * j]) | (bf16_rne(acc[f][g][4 * j + 1]) << 16);
+                    pk.y = bf16_rne(acc[f][g][4 * j + 2]) | (bf16_rne(acc[f][g][4 * j + 3]) << 16);
+                    *reinterpret_cast<uint2*>(yrow + n) = pk;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < N) yrow[n + e] = (uint16_t)bf16_rne(acc[f][g][4 * j + e]);
+                }
+            }
+    }
+}
+
+// ============================================================================
+// Tile path, FP4, K % 512 == 0: full-cache-line staging.
+// A CU's vector memory path moves about one 64-byte half line per clock, and a
+// request for part of a 128-byte line costs as much as the whole line, so
+// every global -> LDS copy here moves whole lines: a superstage is K = 256
+// (128 code bytes per row) of both 256-row operands, 8 rows per wave
+// instruction, into one of two 64 KB slots.  Scales are fetched in bulk, 32
+// bytes per row (K = 1024, four superstages), into one of two 16 KB buffers,
+// a quarter of a block with every superstage's copies.
+// Output tile 256 x 256, 4 waves (2 x 2, 128 x 128 each), 32 x 32 x 64 MFMAs,
+// four k-steps per superstage.  One barrier per superstage, placed once every
+// wave has read all of superstage u (and its own copies of u + 1 have landed):
+// after it, each wave reads the scales and the first two k-steps of u + 1 and
+// issues the copies of u + 2 into the slot just released, both behind the 32
+// MFMAs of k-steps 2 and 3 of u (one copy after every other MFMA).
+// K-permutation inside a superstage: lane group h multiplies the row's 16-byte
+// chunks 4h .. 4h+3 in k-steps t = 0..3, so the scale dword at byte 8q + 4h of
+// the row's bulk scale segment (q = superstage within the block) serves all
+// four k-steps with op_sel t.  LDS chunks are XOR-swizzled by (row / 2) % 8,
+// which spreads the 16 lanes of every ds_read_b128 phase over all banks.
+// ============================================================================
+namespace tile_fp4 {
+constexpr int kRows = 256;
+constexpr int kRowBytes = 128;                   // code bytes per row per superstage
+constexpr int kOpBytes = kRows * kRowBytes;      // 32 KB
+constexpr int kSlot = 2 * kOpBytes;              // W rows, then A rows
+constexpr int kScaleRow = 32;                    // bulk scale bytes per row (K = 1024)
+constexpr int kScaleBuf = 2 * kRows * kScaleRow; // 16 KB: W rows, then A rows
+constexpr int kLds = 2 * kSlot + 2 * kScaleBuf;  // 160 KB
+constexpr int kOutPitch = 2 * kTileN + 16;       // epilogue staging pitch (bytes): 132 dwords
+static_assert(kTileM * kOutPitch <= kLds, "output staging");
+}  // namespace tile_fp4
+
+// VEC: N % 8 == 0 and y 16-byte aligned (whole 16-byte output stores allowed).
+template <bool VEC>
+__global__ __launch_bounds__(256, 1) void gemm_tile_fp4(const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa,
+                                                          const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw,
+                                                          uint16_t* __restrict__ y, int M, int N, int K, int tiles_m,
+                                                          int tiles_n) {
+    using namespace tile_fp4;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
+
+    int tm, tn;
+    tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * kTileM, n0 = tn * kTileN;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wn = wave & 1, wm = wave >> 1;
+    const int l32 = lane & 31, h = lane >> 5;
+    const int64_t KB = (int64_t)K / 2, KS = (int64_t)K / 32;
+    const int nsup = K / 256;
+
+    // code copy i (0..15): W rows for i < 8, A rows for i >= 8; rows 64 * wave + 8 * (i % 8) + lane / 8,
+    // the lane fills physical chunk lane % 8 with logical chunk (lane % 8) ^ ((row / 2) % 8)
+    const uint8_t* wrow[8];
+    const uint8_t* xrow[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int row = 64 * wave + 8 * i + (lane >> 3);
+        const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+        wrow[i] = qw + (int64_t)min(n0 + row, N - 1) * KB + 16 * chunk;
+        xrow[i] = qa + (int64_t)min(m0 + row, M - 1) * KB + 16 * chunk;
+    }
+    auto issue_code = [&](int u, int i) {  // copy i of superstage min(u, nsup - 1) into the slot of u
+        uint8_t* slot = lds + (u & 1) * kSlot;
+        const int64_t koff = (int64_t)min(u, nsup - 1) * kRowBytes;
+        if (i < 8) g2lds16(wrow[i] + koff, slot + (8 * wave + i) * 1024);
+        else g2lds16(xrow[i - 8] + koff, slot + kOpBytes + (8 * wave + i - 8) * 1024);
+    };
+    // scale copy part j (0..3) of block b: instruction 4j + wave moves the 32-byte segments of
+    // rows 32 (4j + wave) + lane / 2 (W rows 0..255, then A rows), lane % 2 = which 16-byte half.
+    // The part is copied with the codes of superstage 4b - 3 + j: after every wave has finished
+    // with block b - 2 in the same buffer (last read for superstage 4b - 5) and in time for 4b.
+    auto issue_scale = [&](int u) {
+        const int b = (u + 3) >> 2, j = (u + 3) & 3;
+        const int q = 4 * j + wave;
+        const int row = 32 * (q & 7) + (lane >> 1);
+        int64_t off = 32 * (int64_t)b + 16 * (lane & 1);
+        if (off >= KS) off = 0;  // past the last block: any in-row address, never read
+        const uint8_t* src =
+            q < 8 ? sw + (int64_t)min(n0 + row, N - 1) * KS + off : sa + (int64_t)min(m0 + row, M - 1) * KS + off;
+        g2lds16(src, lds + 2 * kSlot + (b & 1) * kScaleBuf + q * 1024);
+    };
+
+    // per-lane LDS offsets
+    int woff[4], xoff[4], wsoff[4], xsoff[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+        const int wr = 128 * wn + 32 * f + l32, xr = 128 * wm + 32 * f + l32;
+        woff[f] = wr * kRowBytes + ((wr >> 1) & 7);  // low bits: the swizzle key, split off below
+        xoff[f] = kOpBytes + xr * kRowBytes + ((xr >> 1) & 7);
+        wsoff[f] = wr * kScaleRow + 4 * h;
+        xsoff[f] = (kRows + xr) * kScaleRow + 4 * h;
+    }
+    const uint32_t base = lds_addr(lds);
+    auto rd_step = [&](v4u (&rw)[4], v4u (&rx)[4], int u, int t) {
+        const uint32_t sb = base + (u & 1) * kSlot;
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+            rw[f] = lds_read16(sb + (woff[f] & ~7) + 16 * ((4 * h + t) ^ (woff[f] & 7)));
+            rx[f] = lds_read16(sb + (xoff[f] & ~7) + 16 * ((4 * h + t) ^ (xoff[f] & 7)));
+        }
+    };
+    auto rd_scales = [&](uint32_t (&ws)[4], uint32_t (&xs)[4], int u) {
+        const uint32_t scb = base + 2 * kSlot + ((u >> 2) & 1) * kScaleBuf + 8 * (u & 3);
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+            ws[f] = lds_read4(scb + wsoff[f]);
+            xs[f] = lds_read4(scb + xsoff[f]);
+        }
+    };
+
+    v16f acc[4][4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[f][g][r] = 0.f;
+
+    // prologue: scale block 0, the codes of superstage 0, then the batch of superstage 1
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int q = 4 * j + wave;
+        const int row = 32 * (q & 7) + (lane >> 1);
+        const int64_t off = 16 * (lane & 1);
+        const uint8_t* src =
+            q < 8 ? sw + (int64_t)min(n0 + row, N - 1) * KS + off : sa + (int64_t)min(m0 + row, M - 1) * KS + off;
+        g2lds16(src, lds + 2 * kSlot + q * 1024);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) issue_code(0, i);
+    issue_scale(1);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) issue_code(1, i);
+    wait_vmcnt<17>();  // superstage 0 and scale block 0 are in (this wave's copies)
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+
+    uint32_t wsc[4], xsc[4];
+    v4u r0w[4], r0x[4], r1w[4], r1x[4], r2w[4], r2x[4], r3w[4], r3x[4];
+    rd_scales(wsc, xsc, 0);
+    rd_step(r0w, r0x, 0, 0);
+    rd_step(r1w, r1x, 0, 1);
+
+#define MX_STEP(RW, RX, T)                                                                                           \
+    _Pragma("unroll") for (int f = 0; f < 4; ++f) _Pragma("unroll") for (int g = 0; g < 4; ++g) acc[f][g] =          \
+        mfma32<kFmtFP4, T>(fp4_operand(RW[f]), fp4_operand(RX[g]), acc[f][g], (int)wsc[f], (int)xsc[g]);
+
+    for (int u = 0; u < nsup; ++u) {
+        // in flight: scales + k-steps 0, 1 of u (LDS reads); the copies of u + 1
+        lds_wait_first(r0w, r0x, wsc, xsc);  // lgkmcnt(8): scales and k-step 0
+        MX_STEP(r0w, r0x, 0)
+        __builtin_amdgcn_sched_barrier(0);
+        rd_step(r2w, r2x, u, 2);
+        lds_wait_n<8>(r1w, r1x);
+        MX_STEP(r1w, r1x, 1)
+        __builtin_amdgcn_sched_barrier(0);
+        rd_step(r3w, r3x, u, 3);
+        lds_wait_n<0>(r2w, r2x);
+        lds_wait_n<0>(r3w, r3x);
+        wait_vmcnt<0>();  // this wave's copies of u + 1 (and of the scale part) have landed
+        __builtin_amdgcn_s_barrier();  // every wave: done reading u, copies of u + 1 complete
+        __builtin_amdgcn_sched_barrier(0);
+        const uint32_t wsu[4] = {wsc[0], wsc[1], wsc[2], wsc[3]};
+        const uint32_t xsu[4] = {xsc[0], xsc[1], xsc[2], xsc[3]};
+        rd_scales(wsc, xsc, u + 1);  // past the end these read the repeated last superstage: unused
+        rd_step(r0w, r0x, u + 1, 0);
+        rd_step(r1w, r1x, u + 1, 1);
+        issue_scale(u + 2);
+#pragma unroll
+        for (int t = 2; t < 4; ++t)
+#pragma unroll
+            for (int f = 0; f < 4; ++f)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    if (t == 2)
+                        acc[f][g] = mfma32<kFmtFP4, 2>(fp4_operand(r2w[f]), fp4_operand(r2x[g]), acc[f][g], (int)wsu[f],
+                                                       (int)xsu[g]);
+                    else
+                        acc[f][g] = mfma32<kFmtFP4, 3>(fp4_operand(r3w[f]), fp4_operand(r3x[g]), acc[f][g], (int)wsu[f],
+                                                       (int)xsu[g]);
+                    if ((f * 4 + g) & 1) issue_code(u + 2, 8 * (t - 2) + ((f * 4 + g) >> 1));
+                }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // then one global -> LDS copy
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#undef MX_STEP
+    wait_vmcnt<0>();
+    lds_wait_n<0>(r0w, r0x);
+    lds_wait_n<0>(r1w, r1x);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Epilogue through LDS: each wave writes its BF16 sub-tile row-major (padded pitch), then the
+    // workgroup stores whole 512-byte tile rows.
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const int ml = 128 * wm + 32 * g + l32;
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int nl = 128 * wn + 32 * f + 8 * j + 4 * h;
+                uint2 pk;
+                pk.x = bf16x2_rne(acc[f][g][4 * j], acc[f][g][4 * j + 1]);
+                pk.y = bf16x2_rne(acc[f][g][4 * j + 2], acc[f][g][4 * j + 3]);
+                *reinterpret_cast<uint2*>(lds + ml * kOutPitch + 2 * nl) = pk;
+            }
+    }
+    __syncthreads();
+    // wave w stores tile rows 64 w .. 64 w + 63, two rows per instruction (32 lanes x 16 bytes each)
+#pragma unroll 4
+    for (int r = 0; r < 32; ++r) {
+        const int ml = 64 * wave + 2 * r + h;
+        const int m = m0 + ml;
+        const int n = n0 + 8 * l32;
+        const uint4 v = *reinterpret_cast<const uint4*>(lds + ml * kOutPitch + 16 * l32);
+        if (m >= M) continue;
+        uint16_t* dst = y + (int64_t)m * N + n;
+        if (VEC && n + 7 < N) {
+            *reinterpret_cast<uint4*>(dst) = v;
+        } else {
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (n + e < N) dst[e] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+        }
+    }
+}
+
 // ----------------------------------------------------------------------------
 // Host-side dispatch shared by the FP4 and FP8 entry points.
 // ----------------------------------------------------------------------------
@@ -399,7 +976,19 @@ inline hipError_t launch_gemm(const void* qa, const void* sa, const void* qw, co
     const uint8_t* w = reinterpret_cast<const uint8_t*>(qw);
     uint16_t* out = reinterpret_cast<uint16_t*>(y);
     const int m = (int)M, n = (int)N, k = (int)K;
-    if (M <= 128) {
+    if (!FP8 && M <= 128 && K % 512 == 0) {
+        const dim3 grid((unsigned)((N + 31) / 32));
+        const uint8_t* sa8 = reinterpret_cast<const uint8_t*>(sa);
+        const uint8_t* sw8 = reinterpret_cast<const uint8_t*>(sw);
+        if (M <= 16)
+            hipLaunchKernelGGL(gemm_decode_lds_fp4<1>, grid, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k);
+        else if (M <= 32)
+            hipLaunchKernelGGL(gemm_decode_lds_fp4<2>, grid, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k);
+        else if (M <= 64)
+            hipLaunchKernelGGL(gemm_decode_lds_fp4<4>, grid, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k);
+        else
+            hipLaunchKernelGGL(gemm_decode_lds_fp4<8>, grid, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k);
+    } else if (M <= 128) {
         const dim3 grid((unsigned)((N + 31) / 32));
         if (M <= 16)
             hipLaunchKernelGGL((gemm_decode_kernel<FP8, 1, 8>), grid, dim3(512), 0, st, a, sa, w, sw, out, m, n, k);
@@ -411,8 +1000,23 @@ inline hipError_t launch_gemm(const void* qa, const void* sa, const void* qw, co
             hipLaunchKernelGGL((gemm_decode_kernel<FP8, 8, 4>), grid, dim3(256), 0, st, a, sa, w, sw, out, m, n, k);
     } else {
         const int tiles_m = (int)((M + kTileM - 1) / kTileM), tiles_n = (int)((N + kTileN - 1) / kTileN);
-        hipLaunchKernelGGL((gemm_tile_kernel<FP8>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, st, a, sa, w,
-                           sw, out, m, n, k, tiles_m, tiles_n);
+        const uint8_t* sa8 = reinterpret_cast<const uint8_t*>(sa);
+        const uint8_t* sw8 = reinterpret_cast<const uint8_t*>(sw);
+        const bool scales16 = ((reinterpret_cast<uintptr_t>(sa) | reinterpret_cast<uintptr_t>(sw)) & 15) == 0;
+        const bool vec16 = N % 8 == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0;
+        if (!FP8 && K % 512 == 0 && scales16 && vec16)
+            hipLaunchKernelGGL(gemm_tile_fp4<true>, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, st, a, sa8, w,
+                               sw8, out, m, n, k, tiles_m, tiles_n);
+        else if (!FP8 && K % 512 == 0 && scales16)
+            hipLaunchKernelGGL(gemm_tile_fp4<false>, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, st, a, sa8, w,
+                               sw8, out, m, n, k, tiles_m, tiles_n);
+        else if (!FP8 && K % 256 == 0)
+            hipLaunchKernelGGL(gemm_tile_dma_fp4<4>, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, st, a,
+                               reinterpret_cast<const uint8_t*>(sa), w, reinterpret_cast<const uint8_t*>(sw), out, m, n,
+                               k, tiles_m, tiles_n);
+        else
+            hipLaunchKernelGGL((gemm_tile_kernel<FP8>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, st, a, sa,
+                               w, sw, out, m, n, k, tiles_m, tiles_n);
     }
     return hipGetLastError();
 }

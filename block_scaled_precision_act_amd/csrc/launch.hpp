@@ -16,7 +16,8 @@ hipError_t launch_quant_ptpc_f32(const void* x, int64_t rows, int64_t K, void* q
 
 // GEMMs (K % 128 == 0, M, N > 0).
 hipError_t launch_gemm_a4w4(const void* qa, const void* sa, const void* qw, const void* sw, void* y,
-                            int64_t M, int64_t N, int64_t K, hipStream_t st);
+                            int64_t M, int64_t N, int64_t K, void* workspace, hipStream_t st);
+size_t gemm_a4w4_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_a8w8(const void* qa, const float* sa, const void* qw, const float* sw, void* y,
                             int64_t M, int64_t N, int64_t K, hipStream_t st);
 

@@ -20,6 +20,10 @@ __device__ __forceinline__ v8i fp4_operand(uint4 x) {
     v8i r = {(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
     return r;
 }
+__device__ __forceinline__ v8i fp4_operand(unsigned __attribute__((ext_vector_type(4))) x) {
+    v8i r = {(int)x[0], (int)x[1], (int)x[2], (int)x[3], 0, 0, 0, 0};
+    return r;
+}
 
 // Two E4M3 codes (the low or high 16 bits of w) -> two FP16 values, exactly:
 // every finite E4M3 value (max 448, smallest 2^-9) is an FP16 normal.
@@ -66,7 +70,81 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
     return u >> 16;
 }
 
+// Two binary32 -> two bfloat16 (low half = a), round to nearest even, NaN stays NaN
+// (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    const f2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2));
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane i of the wave writes
+// lds_base + 16 * i (lds_base must be the same for the whole wave).
+__device__ __forceinline__ void g2lds16(const void* g, void* lds_base) {
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) (other counters untouched), N < 64.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// 32-bit LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// LDS reads issued as inline asm: the compiler does not see them as LDS accesses, so it
+// does not drain outstanding global->LDS loads before them.  The caller orders them after
+// its own explicit vmcnt wait + barrier, and must call lds_wait_* on the results before use.
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v4u lds_read16(uint32_t addr) {
+    v4u v;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
+    return v;
+}
+__device__ __forceinline__ uint32_t lds_read4(uint32_t addr) {
+    uint32_t v;
+    asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr));
+    return v;
+}
+// 4-byte global -> LDS (lane i writes lds_base + 4 * i).
+__device__ __forceinline__ void g2lds4(const void* g, void* lds_base) {
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
+}
+
+// lgkmcnt(8): all but the last eight LDS reads done; ties four 16-byte and four 4-byte
+// results of each of two groups to the wait.
+__device__ __forceinline__ void lds_wait_first(v4u (&a)[4], v4u (&b)[4], uint32_t (&c)[4], uint32_t (&d)[4]) {
+    asm volatile("s_waitcnt lgkmcnt(8)"
+                 : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]),
+                   "+v"(c[0]), "+v"(c[1]), "+v"(c[2]), "+v"(c[3]), "+v"(d[0]), "+v"(d[1]), "+v"(d[2]), "+v"(d[3]));
+}
+// lgkmcnt(0) tied to four 16-byte results of each of two groups.
+__device__ __forceinline__ void lds_wait_rest(v4u (&a)[4], v4u (&b)[4]) {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]));
+}
+
+// lgkmcnt(N) tied to four 16-byte results of each of two groups.
+template <int N>
+__device__ __forceinline__ void lds_wait_n(v4u (&a)[4], v4u (&b)[4]) {
+    static_assert(N >= 0 && N < 16, "lgkmcnt range");
+    asm volatile("s_waitcnt lgkmcnt(%8)"
+                 : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3])
+                 : "n"(N));
+}
+
 __device__ __forceinline__ uint4 ldg16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
+// 16-byte load of data used once (non-temporal hint: evict first from the caches).
+__device__ __forceinline__ uint4 ldg16_stream(const uint8_t* p) {
+    typedef unsigned u4 __attribute__((ext_vector_type(4)));
+    const u4 v = __builtin_nontemporal_load(reinterpret_cast<const u4*>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
 __device__ __forceinline__ int ldg4(const uint8_t* p) { return *reinterpret_cast<const int*>(p); }
 
 }  // namespace mx

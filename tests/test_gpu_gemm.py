@@ -55,10 +55,10 @@ def _random_mx(orc, seed, M, N, K, w_std=0.02):
     return qa, sa, qw, sw
 
 
-# decode path (M <= 128) and tile path (M > 128), ragged M / N, K tails of 128 and 256
+# decode path (M <= 128) and tile paths (M > 128; K % 256 == 0 or not), ragged M / N, several tiles
 SHAPES = [(1, 256, 128), (3, 100, 384), (16, 7168, 1024), (17, 33, 256), (37, 1000, 1024), (64, 512, 512),
           (100, 300, 2048), (128, 1024, 8192), (129, 300, 384), (300, 700, 1024), (512, 512, 512),
-          (600, 1100, 2176), (257, 257, 128)]
+          (600, 1100, 2176), (257, 257, 128), (259, 1030, 256), (1000, 800, 4096), (777, 520, 768)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
@@ -66,6 +66,24 @@ def test_a4w4_shapes(mx, orc, M, N, K):
     qa, sa, qw, sw = _random_mx(orc, M * 7 + N + K, M, N, K)
     y, ad, _ = orc.gemm_a4w4_at(qa, sa, qw, sw, nthreads=NT)
     _check(_a4w4_gpu(mx, qa, sa, qw, sw), y, ad, "a4w4 %dx%dx%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 520, 1024), (260, 300, 512)])
+def test_a4w4_scales_4byte_aligned(mx, orc, M, N, K):
+    # scale rows only 4-byte aligned (allowed by the ABI): the tile path must not use 16-byte scale copies
+    import torch
+    qa, sa, qw, sw = _random_mx(orc, M + N + K + 1, M, N, K)
+    y, ad, _ = orc.gemm_a4w4_at(qa, sa, qw, sw, nthreads=NT)
+
+    def shifted(a):
+        buf = torch.zeros(a.size + 4, dtype=torch.uint8, device="cuda")
+        view = buf[4:].view(a.shape)
+        view.copy_(torch.from_numpy(a))
+        assert view.data_ptr() % 16 != 0
+        return view
+
+    out = mx.gemm_a4w4(to_dev(qa), shifted(sa), to_dev(qw), shifted(sw))
+    _check(bf16_host(out), y, ad, "a4w4 4-byte-aligned scales %dx%dx%d" % (M, N, K))
 
 
 def test_a4w4_tiny_config_full(mx, orc):

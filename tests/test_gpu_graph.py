@@ -35,21 +35,22 @@ def _replays_match(mx, torch, thunk, outs):
         del junk
 
 
-@pytest.mark.parametrize("M", [64, 300])
-def test_a4w4_layer_graph_replay(mx, M):
+@pytest.mark.parametrize("M,N,K", [(64, 512, 1024), (300, 512, 1024), (64, 7168, 8192), (16, 2000, 4096)])
+def test_a4w4_layer_graph_replay(mx, M, N, K):
     import torch
-    K, N = 1024, 512
     x = bf16_dev(synth.act_normal(61, M, K))
     qw, sw = mx.quant_weight_mx(torch.from_numpy(synth.weight_normal(62, N, K, 0.02)).cuda())
     qa = torch.empty((M, K // 2), dtype=torch.uint8, device="cuda")
     sa = torch.empty((M, K // 32), dtype=torch.uint8, device="cuda")
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    wsb = mx.mx_gemm_a4w4_workspace_bytes(M, N, K)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
 
     def layer():
         s = torch.cuda.current_stream().cuda_stream
         assert mx.mx_quant_act_bf16(x.data_ptr(), M, K, qa.data_ptr(), sa.data_ptr(), s) == 0
         assert mx.mx_gemm_a4w4_bf16(qa.data_ptr(), sa.data_ptr(), qw.data_ptr(), sw.data_ptr(), y.data_ptr(),
-                                    M, N, K, None, 0, s) == 0
+                                    M, N, K, ws.data_ptr(), wsb, s) == 0
 
     _replays_match(mx, torch, layer, [qa, sa, y])
 
