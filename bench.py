@@ -399,7 +399,7 @@ def main():
 
     roof = roofline_gemm("a4w4", M, N, K, gemm_ms)
     roof["traffic"] = pmc_traffic("gemm_decode_fp4_m64")
-    roof["kernel"] = "gemm_decode_lds_fp4<4>"
+    roof["kernel"] = "gemm_decode_fp4<2>"
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak",

@@ -362,6 +362,202 @@ __global__ __launch_bounds__(256) void gemm_decode_lds_fp4(const uint8_t* __rest
 }
 
 // ============================================================================
+// Decode path, per-wave LDS rings (FP4, M <= 64, K % 2048 == 0, K <= 16384,
+// 16-byte aligned scale rows).
+// One workgroup (4 waves) per 32 output columns.  A slab is K = 256 of the
+// 32*MF activation rows and the 32 weight rows: 128 code bytes per row, copied
+// global -> LDS (global_load_lds) 8 whole rows (whole cache lines) per wave
+// instruction.  Wave w owns the w-th quarter of K (nmine = K / 1024
+// consecutive slabs, an even count) and a private ring of S slab slots, so it
+// waits only for its own copies; the scale bytes of its quarter of K (8 bytes
+// per row and slab) go to a private LDS block the same way.  No wave waits for another
+// until the end, when the four partial tiles are summed through LDS in a fixed
+// order (deterministic).
+// MFMA: 32 x 32 x 64, operand A = 32 weight rows (n), operand B = 32
+// activation rows (m); k-step t of a slab uses the row's chunks 4h + t in lane
+// group h (the K-permutation and (row / 2) % 8 chunk swizzle of the tile
+// path), so one scale dword per row and slab serves all four k-steps.  In the
+// scale block, row r's 16-byte pieces are rotated by r / 4, which spreads the
+// 32 rows of a fragment over the LDS banks.
+// ============================================================================
+namespace dec4 {
+constexpr int kNT = 32;             // output columns per workgroup
+constexpr int kSlab = 128;          // code bytes per row per slab (K = 256)
+constexpr int kMaxMine = 16;        // slabs per wave supported (K <= 16384)
+template <int MF, int S>
+struct Cfg {
+    static constexpr int kArows = 32 * MF;
+    static constexpr int kRows = kArows + kNT;              // activation rows, then weight rows
+    static constexpr int kSlabBytes = kRows * kSlab;         // 12 KB (MF = 2) or 8 KB
+    static constexpr int kCopies = kSlabBytes / 1024;        // copies per wave per slab
+    static constexpr int kScCopies = kRows * kMaxMine * 8 / 1024;  // scale copies per wave
+    static constexpr int kRing = 4 * S * kSlabBytes;
+    static constexpr int kScBlock = kScCopies * 1024;       // private scale block per wave
+    static constexpr int kLds = kRing + 4 * kScBlock;
+    static_assert(kScCopies + S * kCopies <= 63, "vmcnt");
+    static_assert(kLds <= 160 * 1024, "LDS");
+    static_assert(4 * MF * 16 * 64 * 4 <= kLds, "reduction staging");
+};
+}  // namespace dec4
+
+template <int MF, int S>
+__global__ __launch_bounds__(256, 1) void gemm_decode_fp4(const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa,
+                                                          const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw,
+                                                          uint16_t* __restrict__ y, int M, int N, int K) {
+    using C = dec4::Cfg<MF, S>;
+    using namespace dec4;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[C::kLds];
+    const int n0 = blockIdx.x * kNT;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l32 = lane & 31, h = lane >> 5;
+    const int64_t KB = (int64_t)K / 2;
+    const int KS = K / 32;                  // scale bytes per row
+    const int nmine = K / 1024;             // slabs per wave (even)
+    const int s0 = wave * nmine;            // first slab of this wave
+    uint8_t* const ring = lds + wave * S * C::kSlabBytes;
+    uint8_t* const scb = lds + C::kRing + wave * C::kScBlock;
+
+    // 1. this wave's scale bytes: row r, bytes [8 s0, 8 s0 + 8 nmine), ncw = nmine / 2 pieces of 16
+    //    bytes; piece position p of row r holds piece (p + r / 4) % ncw.  Positions past the data
+    //    repeat its last piece.
+    const int ncw = nmine / 2, sctotal = C::kRows * ncw;
+#pragma unroll
+    for (int it = 0; it < C::kScCopies; ++it) {
+        const int idx = min(64 * it + lane, sctotal - 1);
+        const int r = idx / ncw, p = idx - r * ncw;
+        const int c = (p + (r >> 2)) % ncw;
+        const int64_t off = 8 * (int64_t)s0 + 16 * c;
+        g2lds16(r < C::kArows ? sa + (int64_t)min(r, M - 1) * KS + off
+                              : sw + (int64_t)min(n0 + r - C::kArows, N - 1) * KS + off,
+                scb + 1024 * it);
+    }
+    // 2. code copies: copy i moves rows 8i .. 8i+7 (lane / 8) of the slab, the lane filling chunk
+    //    lane % 8 with logical chunk (lane % 8) ^ ((row / 2) % 8).  An activation copy whose 8 rows
+    //    all lie at or past M reads one address in every lane (one cache line): those rows only
+    //    feed output columns that are never stored.  A batch for a slab past the wave's last one
+    //    also reads a single address (one line, data unused), so every wave issues the same
+    //    number of copies and the wait counts below are fixed.
+    const uint8_t* rowp[C::kCopies];
+#pragma unroll
+    for (int i = 0; i < C::kCopies; ++i) {
+        const int r = 8 * i + (lane >> 3);
+        const int chunk = (lane & 7) ^ ((r >> 1) & 7);
+        if (r < C::kArows)
+            rowp[i] = 8 * i < M ? qa + (int64_t)min(r, M - 1) * KB + 16 * chunk : qa;
+        else
+            rowp[i] = qw + (int64_t)min(n0 + r - C::kArows, N - 1) * KB + 16 * chunk;
+    }
+    auto issue = [&](int j) {  // slab s0 + j into slot j % S
+        uint8_t* slot = ring + (j % S) * C::kSlabBytes;
+        const bool real = j < nmine;
+        const int64_t koff = (int64_t)(s0 + (real ? j : 0)) * kSlab;
+#pragma unroll
+        for (int i = 0; i < C::kCopies; ++i) {
+            const uint8_t* src = real ? rowp[i] + koff : qw;
+            if (8 * i < C::kArows) g2lds16(src, slot + 1024 * i);    // activations: reused by every CU
+            else g2lds16_nt(src, slot + 1024 * i);                   // weights: streamed once
+        }
+    };
+#pragma unroll
+    for (int j = 0; j < S; ++j) issue(j);
+
+    // per-lane LDS offsets (rows: activation fragment g = 32 g + l32, weight rows kArows + l32)
+    const uint32_t rbase = lds_addr(ring), sbase = lds_addr(scb);
+    int xoff[MF], xsw[MF], xsr[MF];
+#pragma unroll
+    for (int g = 0; g < MF; ++g) {
+        const int r = 32 * g + l32;
+        xoff[g] = r * kSlab;
+        xsw[g] = (r >> 1) & 7;
+        xsr[g] = r;
+    }
+    const int wr = C::kArows + l32;
+    const int woff = wr * kSlab, wsw = (wr >> 1) & 7;
+    auto scale_at = [&](int r, int j) -> uint32_t {  // dword of row r for local slab j, lane group h
+        int p = (j >> 1) - (r >> 2) % ncw;
+        if (p < 0) p += ncw;
+        return lds_read4(sbase + 16 * (r * ncw + p) + 8 * (j & 1) + 4 * h);
+    };
+
+    v16f acc[MF];
+#pragma unroll
+    for (int g = 0; g < MF; ++g)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[g][r] = 0.f;
+
+    for (int j = 0; j < nmine; ++j) {
+        // slab j (and, for j = 0, the scale block) has landed once only the later S - 1 batches
+        // may still be in flight
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<(S - 1) * C::kCopies>();
+        __builtin_amdgcn_sched_barrier(0);
+        const uint32_t sb = rbase + (j % S) * C::kSlabBytes;
+        uint32_t ws = scale_at(wr, j);
+        uint32_t xs[MF];
+#pragma unroll
+        for (int g = 0; g < MF; ++g) xs[g] = scale_at(xsr[g], j);
+        v4u wv[4], xv[4][MF];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            wv[t] = lds_read16(sb + woff + 16 * ((4 * h + t) ^ wsw));
+#pragma unroll
+            for (int g = 0; g < MF; ++g) xv[t][g] = lds_read16(sb + xoff[g] + 16 * ((4 * h + t) ^ xsw[g]));
+        }
+        lds_wait_dec<MF>(wv, xv, ws, xs);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(j + S);  // the slot is read: refill it
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int g = 0; g < MF; ++g) {
+            acc[g] = mfma32<kFmtFP4, 0>(fp4_operand(wv[0]), fp4_operand(xv[0][g]), acc[g], (int)ws, (int)xs[g]);
+            acc[g] = mfma32<kFmtFP4, 1>(fp4_operand(wv[1]), fp4_operand(xv[1][g]), acc[g], (int)ws, (int)xs[g]);
+            acc[g] = mfma32<kFmtFP4, 2>(fp4_operand(wv[2]), fp4_operand(xv[2][g]), acc[g], (int)ws, (int)xs[g]);
+            acc[g] = mfma32<kFmtFP4, 3>(fp4_operand(wv[3]), fp4_operand(xv[3][g]), acc[g], (int)ws, (int)xs[g]);
+        }
+    }
+
+    // 3. fixed-order reduction of the four partial tiles through LDS
+    wait_vmcnt<0>();  // the trailing refills
+    __syncthreads();  // every wave is done with its ring and scale block
+    float* red = reinterpret_cast<float*>(lds);  // [wave][g][reg][lane]
+#pragma unroll
+    for (int g = 0; g < MF; ++g)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) red[((wave * MF + g) * 16 + r) * 64 + lane] = acc[g][r];
+    __syncthreads();
+    // wave w finalizes register quad w of every fragment: D rows (n) 8w + 4h + e, column (m) l32
+    const bool vec_ok = (N & 3) == 0 && (reinterpret_cast<uintptr_t>(y) & 7) == 0;
+#pragma unroll
+    for (int g = 0; g < MF; ++g) {
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 4 * wave + e;
+            float t = red[((0 * MF + g) * 16 + r) * 64 + lane];
+            t += red[((1 * MF + g) * 16 + r) * 64 + lane];
+            t += red[((2 * MF + g) * 16 + r) * 64 + lane];
+            t += red[((3 * MF + g) * 16 + r) * 64 + lane];
+            v[e] = t;
+        }
+        const int m = 32 * g + l32;
+        const int n = n0 + 8 * wave + 4 * h;
+        if (m >= M) continue;
+        uint16_t* dst = y + (int64_t)m * N + n;
+        if (vec_ok && n + 3 < N) {
+            uint2 pk;
+            pk.x = bf16x2_rne(v[0], v[1]);
+            pk.y = bf16x2_rne(v[2], v[3]);
+            *reinterpret_cast<uint2*>(dst) = pk;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (n + e < N) dst[e] = (uint16_t)(bf16x2_rne(v[e], 0.f) & 0xffffu);
+        }
+    }
+}
+
+// ============================================================================
 // Tile path (large M, MFMA-bound).
 // 256 x 256 output tile per workgroup of 4 waves (2 x 2, 128 x 128 each, 4 x 4
 // fragments of 32 x 32).  Each K-stage moves 128 code bytes per row of both
@@ -976,7 +1172,16 @@ inline hipError_t launch_gemm(const void* qa, const void* sa, const void* qw, co
     const uint8_t* w = reinterpret_cast<const uint8_t*>(qw);
     uint16_t* out = reinterpret_cast<uint16_t*>(y);
     const int m = (int)M, n = (int)N, k = (int)K;
-    if (!FP8 && M <= 128 && K % 512 == 0) {
+    const bool scales16 = ((reinterpret_cast<uintptr_t>(sa) | reinterpret_cast<uintptr_t>(sw)) & 15) == 0;
+    if (!FP8 && M <= 64 && K % 2048 == 0 && K <= 1024 * dec4::kMaxMine && scales16) {
+        const dim3 grid((unsigned)((N + dec4::kNT - 1) / dec4::kNT));
+        const uint8_t* sa8 = reinterpret_cast<const uint8_t*>(sa);
+        const uint8_t* sw8 = reinterpret_cast<const uint8_t*>(sw);
+        if (M <= 32)
+            hipLaunchKernelGGL((gemm_decode_fp4<1, 3>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k);
+        else
+            hipLaunchKernelGGL((gemm_decode_fp4<2, 2>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k);
+    } else if (!FP8 && M <= 128 && K % 512 == 0) {
         const dim3 grid((unsigned)((N + 31) / 32));
         const uint8_t* sa8 = reinterpret_cast<const uint8_t*>(sa);
         const uint8_t* sw8 = reinterpret_cast<const uint8_t*>(sw);
@@ -1002,7 +1207,6 @@ inline hipError_t launch_gemm(const void* qa, const void* sa, const void* qw, co
         const int tiles_m = (int)((M + kTileM - 1) / kTileM), tiles_n = (int)((N + kTileN - 1) / kTileN);
         const uint8_t* sa8 = reinterpret_cast<const uint8_t*>(sa);
         const uint8_t* sw8 = reinterpret_cast<const uint8_t*>(sw);
-        const bool scales16 = ((reinterpret_cast<uintptr_t>(sa) | reinterpret_cast<uintptr_t>(sw)) & 15) == 0;
         const bool vec16 = N % 8 == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0;
         if (!FP8 && K % 512 == 0 && scales16 && vec16)
             hipLaunchKernelGGL(gemm_tile_fp4<true>, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, st, a, sa8, w,

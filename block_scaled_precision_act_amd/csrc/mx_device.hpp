@@ -85,6 +85,11 @@ __device__ __forceinline__ void g2lds16(const void* g, void* lds_base) {
     __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
 }
 
+// Same, non-temporal (streamed data: allocate in the caches with evict-first priority).
+__device__ __forceinline__ void g2lds16_nt(const void* g, void* lds_base) {
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 2);
+}
+
 // s_waitcnt vmcnt(N) (other counters untouched), N < 64.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -136,6 +141,18 @@ __device__ __forceinline__ void lds_wait_n(v4u (&a)[4], v4u (&b)[4]) {
     asm volatile("s_waitcnt lgkmcnt(%8)"
                  : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3])
                  : "n"(N));
+}
+
+// lgkmcnt(0) tied to the decode kernel's per-slab operands and scales.
+template <int MF>
+__device__ __forceinline__ void lds_wait_dec(v4u (&w)[4], v4u (&x)[4][MF], uint32_t& ws, uint32_t (&xs)[MF]) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]), "+v"(ws));
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int g = 0; g < MF; ++g) asm volatile("" : "+v"(x[t][g]));
+#pragma unroll
+    for (int g = 0; g < MF; ++g) asm volatile("" : "+v"(xs[g]));
 }
 
 __device__ __forceinline__ uint4 ldg16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
