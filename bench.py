@@ -46,6 +46,9 @@ def parse_args():
     ap.add_argument("--kernel-reps", type=int, default=30, help="graph replays per kernel-timing measurement")
     ap.add_argument("--no-extra", action="store_true", help="headline only (skip prefill / A8W8 / sweep)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarize two rocprofv3 --pmc runs of --profile-pass (FETCH_SIZE, then WRITE_SIZE) "
+                         "into profiles/pmc_traffic.json and exit (no GPU needed)")
     ap.add_argument("--profile-pass", action="store_true",
                     help="run each measured kernel a few times plus a plain copy of known size, for rocprofv3 --pmc")
     return ap.parse_args()
@@ -368,9 +371,71 @@ def profile_pass(ctx):
     log("profile pass done (copy of %d bytes x3)" % src.numel())
 
 
+# ----------------------------------------------------------------------------- PMC summary
+# Kernels whose HBM traffic the bench reports: key -> (name fragment, grid size in threads or None)
+PMC_KERNELS = {
+    "gemm_decode_fp4_m64": ("gemm_decode_fp4<2, 2>", None),
+    "gemm_tile_fp4_m8192": ("gemm_tile_fp4<true>", 896 * 256),
+}
+COPY_BYTES = 256 << 20  # the profile pass copies 256 MiB device -> device
+
+
+def read_pmc(folder, counter):
+    """Per-dispatch values (KiB) of one counter from rocprofv3 --output-format csv files."""
+    import csv
+    rows = []
+    for dirpath, _, files in os.walk(folder):
+        for fn in files:
+            if fn.endswith("counter_collection.csv"):
+                with open(os.path.join(dirpath, fn), newline="") as f:
+                    for r in csv.DictReader(f):
+                        if r["Counter_Name"] == counter:
+                            rows.append((r["Kernel_Name"], int(r["Grid_Size"]), float(r["Counter_Value"])))
+    if not rows:
+        raise SystemExit("no %s rows under %s" % (counter, folder))
+    return rows
+
+
+def pmc_summary(fetch_dir, write_dir):
+    fetch, write = read_pmc(fetch_dir, "FETCH_SIZE"), read_pmc(write_dir, "WRITE_SIZE")
+
+    def mean_of(rows, frag, grid):
+        v = [val for name, g, val in rows if frag in name and (grid is None or g == grid)]
+        return (sum(v) / len(v), len(v)) if v else (None, 0)
+
+    # the copy: the largest FETCH among kernels whose name says copy; its writes likewise
+    cf = max((val for name, _, val in fetch if "opy" in name), default=None)
+    cw = max((val for name, _, val in write if "opy" in name), default=None)
+    if not cf or not cw:
+        raise SystemExit("copy dispatch not found in the PMC runs")
+    f_fetch, f_write = COPY_BYTES / (cf * 1024.0), COPY_BYTES / (cw * 1024.0)
+    out = {"source_hash": source_hash(),
+           "copy_calibration": {"bytes": COPY_BYTES, "fetch_kib": cf, "write_kib": cw,
+                                "fetch_factor": round(f_fetch, 4), "write_factor": round(f_write, 4)},
+           "kernels": {}, "detail": {}}
+    for key, (frag, grid) in PMC_KERNELS.items():
+        mf, nf = mean_of(fetch, frag, grid)
+        mw, nw = mean_of(write, frag, grid)
+        if mf is None or mw is None:
+            continue
+        b = mf * 1024.0 * f_fetch + mw * 1024.0 * f_write
+        out["kernels"][key] = int(round(b))
+        out["detail"][key] = {"fetch_kib": round(mf, 1), "write_kib": round(mw, 1), "dispatches": [nf, nw],
+                              "fetch_bytes": int(round(mf * 1024.0 * f_fetch)),
+                              "write_bytes": int(round(mw * 1024.0 * f_write))}
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
+
+
 # ----------------------------------------------------------------------------- main
 def main():
     args = parse_args()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures the layer on one GPU only: the library has no multi-GPU path "
@@ -399,7 +464,7 @@ def main():
 
     roof = roofline_gemm("a4w4", M, N, K, gemm_ms)
     roof["traffic"] = pmc_traffic("gemm_decode_fp4_m64")
-    roof["kernel"] = "gemm_decode_fp4<2>"
+    roof["kernel"] = "gemm_decode_fp4<2, 2>"
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak",
