@@ -5,13 +5,14 @@
 // MXFP4 activations); standard "OCP MXFP4" named by "Kimi-K3-Quark-MXFP4-
 // AttnFP8", section "Model Quantization".
 //
-// The kernel is integer-only.  Four lanes own one 32-value block, eight values
-// (one 16-byte BF16 load, or two FP32 loads) each:
+// Four lanes own one 32-value block, eight values (one 16-byte BF16 load, or two
+// FP32 loads) each:
 //   * shared exponent: the largest biased exponent field E of the block (a
 //     4-lane max); scale byte = max(E - 2, 0), which is floor(log2 amax) - 2
 //     + 127 clamped at the bottom of the E8M0 range; E == 255 (NaN/Inf in the
 //     block) gives scale 0xFF and codes 0.
-//   * element: with significand sig (hidden bit included; P fraction bits) and
+//   * element (FP32 input; BF16 input uses the gfx950 scaled FP4 conversion,
+//     which takes the same decisions): with significand sig (hidden bit included; P fraction bits) and
 //     effective exponent Ee = max(E, 1), |x| / 2^(scale-127) times 4 equals
 //     sig / 2^u with u = scale + P - 2 - Ee >= P - 4, so every round-to-nearest-
 //     even decision on the E2M1 grid {0,.5,1,1.5,2,3,4,6} is an exact integer
@@ -50,58 +51,97 @@ __device__ __forceinline__ uint32_t encode8(const uint32_t (&mag)[8], uint32_t s
 }
 
 // One "unit" = 8 consecutive values = one quarter of a block.  units % 4 == 0
-// and the grid stride is a multiple of 4, so the four lanes of a block always
+// and every stride is a multiple of 4, so the four lanes of a block always
 // iterate together (the 4-lane shuffles below stay inside active lanes).
+template <bool F32>
+struct Unit {
+    uint4 a, b;  // 8 values (BF16: a only)
+};
+
+template <bool F32>
+__device__ __forceinline__ Unit<F32> load_unit(const void* __restrict__ xin, int64_t u) {
+    Unit<F32> r;
+    if constexpr (F32) {
+        const uint4* p = reinterpret_cast<const uint4*>(xin) + 2 * u;
+        r.a = p[0];
+        r.b = p[1];
+    } else {
+        r.a = reinterpret_cast<const uint4*>(xin)[u];
+    }
+    return r;
+}
+
+template <bool F32>
+__device__ __forceinline__ void convert_unit(const Unit<F32>& x, uint32_t* __restrict__ q, uint8_t* __restrict__ s,
+                                             int64_t u) {
+    constexpr int P = F32 ? 23 : 7;
+    uint32_t mag[8];
+    uint32_t sgn = 0, emax = 0;
+    if constexpr (F32) {
+        const uint32_t w[8] = {x.a.x, x.a.y, x.a.z, x.a.w, x.b.x, x.b.y, x.b.z, x.b.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            sgn |= (w[i] >> 31) << (4 * i + 3);
+            mag[i] = w[i] & 0x7fffffffu;
+            emax = max(emax, mag[i] >> 23);
+        }
+    } else {
+        const uint32_t w[4] = {x.a.x, x.a.y, x.a.z, x.a.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) emax = max(emax, max((w[i] >> 7) & 0xffu, (w[i] >> 23) & 0xffu));
+    }
+    emax = max(emax, (uint32_t)__shfl_xor((int)emax, 1));
+    emax = max(emax, (uint32_t)__shfl_xor((int)emax, 2));
+    uint32_t codes, scale;
+    if (emax == 0xffu) {  // NaN or Inf in the block
+        scale = 0xffu;
+        codes = 0;
+    } else {
+        scale = emax > 2u ? emax - 2u : 0u;
+        if constexpr (F32) {
+            codes = encode8<P>(mag, scale) | sgn;
+        } else {
+            // BF16: the hardware conversion divides by the (power-of-two) scale and rounds to the
+            // nearest E2M1 value, ties to the even code, saturating at 6 and keeping the sign: the
+            // same decision as the integer path, which it replaces for speed (the GPU tests compare
+            // every finite BF16 pattern with the oracle).
+            const float sc = __uint_as_float(scale ? scale << 23 : 1u << 22);  // 2^(scale - 127)
+            typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+            codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(0u, __builtin_bit_cast(bf2, x.a.x), sc, 0);
+            codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes, __builtin_bit_cast(bf2, x.a.y), sc, 1);
+            codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes, __builtin_bit_cast(bf2, x.a.z), sc, 2);
+            codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes, __builtin_bit_cast(bf2, x.a.w), sc, 3);
+        }
+    }
+    q[u] = codes;
+    if ((u & 3) == 0) s[u >> 2] = (uint8_t)scale;
+}
+
+// Each thread takes units u, u + stride, ...: kUnroll of them are loaded before any is
+// converted, so a wave keeps kUnroll kilobytes (BF16) of loads in flight.
+constexpr int kUnroll = 4;
+constexpr int64_t kMaxBlocks = 2048;
+
 template <bool F32>
 __global__ __launch_bounds__(256) void quant_mx_kernel(const void* __restrict__ xin, uint32_t* __restrict__ q,
                                                         uint8_t* __restrict__ s, int64_t units) {
-    constexpr int P = F32 ? 23 : 7;
     const int64_t stride = (int64_t)gridDim.x * 256;
-    for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < units; u += stride) {
-        uint32_t mag[8];
-        uint32_t sgn = 0, emax = 0;
-        if constexpr (F32) {
-            const uint4* p = reinterpret_cast<const uint4*>(xin) + 2 * u;
-            const uint4 a = p[0], b = p[1];
-            const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    for (; u + (kUnroll - 1) * stride < units; u += kUnroll * stride) {
+        Unit<F32> x[kUnroll];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                sgn |= (w[i] >> 31) << (4 * i + 3);
-                mag[i] = w[i] & 0x7fffffffu;
-                emax = max(emax, mag[i] >> 23);
-            }
-        } else {
-            const uint4 a = reinterpret_cast<const uint4*>(xin)[u];
-            const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+        for (int k = 0; k < kUnroll; ++k) x[k] = load_unit<F32>(xin, u + k * stride);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t lo = w[i] & 0xffffu, hi = w[i] >> 16;
-                sgn |= ((lo >> 15) << (8 * i + 3)) | ((hi >> 15) << (8 * i + 7));
-                mag[2 * i] = lo & 0x7fffu;
-                mag[2 * i + 1] = hi & 0x7fffu;
-                emax = max(emax, max(mag[2 * i] >> 7, mag[2 * i + 1] >> 7));
-            }
-        }
-        emax = max(emax, (uint32_t)__shfl_xor((int)emax, 1));
-        emax = max(emax, (uint32_t)__shfl_xor((int)emax, 2));
-        uint32_t codes, scale;
-        if (emax == 0xffu) {  // NaN or Inf in the block
-            scale = 0xffu;
-            codes = 0;
-        } else {
-            scale = emax > 2u ? emax - 2u : 0u;
-            codes = encode8<P>(mag, scale) | sgn;
-        }
-        q[u] = codes;
-        if ((u & 3) == 0) s[u >> 2] = (uint8_t)scale;
+        for (int k = 0; k < kUnroll; ++k) convert_unit<F32>(x[k], q, s, u + k * stride);
     }
+    for (; u < units; u += stride) convert_unit<F32>(load_unit<F32>(xin, u), q, s, u);
 }
 
 template <bool F32>
 hipError_t launch(const void* x, int64_t rows, int64_t K, void* q, void* s, hipStream_t st) {
     const int64_t units = rows * (K / 8);
     int64_t blocks = (units + 255) / 256;
-    if (blocks > (1 << 20)) blocks = 1 << 20;
+    if (blocks > kMaxBlocks) blocks = kMaxBlocks;
     hipLaunchKernelGGL(quant_mx_kernel<F32>, dim3((unsigned)blocks), dim3(256), 0, st, x,
                        reinterpret_cast<uint32_t*>(q), reinterpret_cast<uint8_t*>(s), units);
     return hipGetLastError();
