@@ -1162,6 +1162,214 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_fp4(const uint8_t* __restric
     }
 }
 
+// ============================================================================
+// Tile path, FP8 (E4M3 widened exactly to FP16), any K % 128 == 0.
+// The structure of gemm_tile_fp4: 256 x 256 output tile, 4 waves (2 x 2,
+// 128 x 128 each, 4 x 4 fragments of 32 x 32 in AGPRs), superstages of 128
+// code bytes per row (K = 128 here) copied whole-line global -> LDS into two
+// 64 KB slots, one barrier per superstage.  Every E4M3 value is an FP16 value,
+// so a 16-byte LDS read widens exactly into two 8-value FP16 operands of the
+// 32 x 32 x 16 FP16 MFMA (the FP8 MFMA rounds small products away next to
+// large ones; FP16 does not).  Lane group h multiplies the row's chunks
+// 4h .. 4h+3: read group j (chunk 4h + j) feeds two k-steps.  After the
+// barrier of superstage u each wave reads the first two groups of u + 1 and
+// issues the copies of u + 2, spread over the MFMAs of the last two groups of
+// u.  The per-row FP32 scales are applied in the epilogue, (acc * sA) * sW,
+// before the BF16 rounding.
+// ============================================================================
+namespace tile_fp8 {
+constexpr int kRows = 256;
+constexpr int kRowBytes = 128;                   // code bytes (K values) per row per superstage
+constexpr int kOpBytes = kRows * kRowBytes;      // 32 KB
+constexpr int kSlot = 2 * kOpBytes;              // W rows, then A rows
+constexpr int kOutPitch = 2 * kTileN + 16;       // epilogue staging pitch (bytes)
+constexpr int kLds = (2 * kSlot > kTileM * kOutPitch) ? 2 * kSlot : kTileM * kOutPitch;
+static_assert(kLds <= 160 * 1024, "LDS");
+}  // namespace tile_fp8
+
+// VEC: N % 8 == 0 and y 16-byte aligned (whole 16-byte output stores allowed).
+template <bool VEC>
+__global__ __launch_bounds__(256, 1) void gemm_tile_fp8(const uint8_t* __restrict__ qa, const float* __restrict__ sa,
+                                                        const uint8_t* __restrict__ qw, const float* __restrict__ sw,
+                                                        uint16_t* __restrict__ y, int M, int N, int K, int tiles_m,
+                                                        int tiles_n) {
+    using namespace tile_fp8;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
+
+    int tm, tn;
+    tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * kTileM, n0 = tn * kTileN;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wn = wave & 1, wm = wave >> 1;
+    const int l32 = lane & 31, h = lane >> 5;
+    const int64_t KB = (int64_t)K;
+    const int nst = K / 128;
+
+    // code copy i (0..15): W rows for i < 8, A rows for i >= 8; rows 64 * wave + 8 * (i % 8) + lane / 8,
+    // the lane fills physical chunk lane % 8 with logical chunk (lane % 8) ^ ((row / 2) % 8)
+    const uint8_t* wrow[8];
+    const uint8_t* xrow[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int row = 64 * wave + 8 * i + (lane >> 3);
+        const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+        wrow[i] = qw + (int64_t)min(n0 + row, N - 1) * KB + 16 * chunk;
+        xrow[i] = qa + (int64_t)min(m0 + row, M - 1) * KB + 16 * chunk;
+    }
+    auto issue_code = [&](int u, int i) {  // copy i of superstage min(u, nst - 1) into the slot of u
+        uint8_t* slot = lds + (u & 1) * kSlot;
+        const int64_t koff = (int64_t)min(u, nst - 1) * kRowBytes;
+        if (i < 8) g2lds16(wrow[i] + koff, slot + (8 * wave + i) * 1024);
+        else g2lds16(xrow[i - 8] + koff, slot + kOpBytes + (8 * wave + i - 8) * 1024);
+    };
+
+    int woff[4], xoff[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+        const int wr = 128 * wn + 32 * f + l32, xr = 128 * wm + 32 * f + l32;
+        woff[f] = wr * kRowBytes + ((wr >> 1) & 7);  // low bits: the swizzle key, split off below
+        xoff[f] = kOpBytes + xr * kRowBytes + ((xr >> 1) & 7);
+    }
+    const uint32_t base = lds_addr(lds);
+    auto rd_group = [&](v4u (&rw)[4], v4u (&rx)[4], int u, int j) {
+        const uint32_t sb = base + (u & 1) * kSlot;
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+            rw[f] = lds_read16(sb + (woff[f] & ~7) + 16 * ((4 * h + j) ^ (woff[f] & 7)));
+            rx[f] = lds_read16(sb + (xoff[f] & ~7) + 16 * ((4 * h + j) ^ (xoff[f] & 7)));
+        }
+    };
+
+    v16f acc[4][4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[f][g][r] = 0.f;
+
+    // one read group: widen half 0 to FP16, run its 16 MFMAs with the widening of half 1 spread
+    // between them (one 8-value operand per two MFMAs, so the VALU work hides behind the MFMA
+    // pipe), then the 16 MFMAs of half 1; CP copies interleaved, one after every fourth MFMA
+    auto group = [&](const v4u (&rw)[4], const v4u (&rx)[4], int cu, int c0, int CP) {
+        v8h wa0[4], xv0[4], wa1[4], xv1[4];
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+            wa0[f] = e4m3x8_to_f16x8(rw[f][0], rw[f][1]);
+            xv0[f] = e4m3x8_to_f16x8(rx[f][0], rx[f][1]);
+        }
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int i = f * 4 + g;
+                acc[f][g] = mfma32_f16(wa0[f], xv0[g], acc[f][g]);
+                if (i & 1) {
+                    const int k = i >> 1;  // 0..7: W operands 0..3, then A operands 0..3
+                    if (k < 4) wa1[k] = e4m3x8_to_f16x8(rw[k][2], rw[k][3]);
+                    else xv1[k - 4] = e4m3x8_to_f16x8(rx[k - 4][2], rx[k - 4][3]);
+                }
+                if (CP && (i & 3) == 3) issue_code(cu, c0 + (i >> 2));
+            }
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int i = f * 4 + g;
+                acc[f][g] = mfma32_f16(wa1[f], xv1[g], acc[f][g]);
+                if (CP && (i & 3) == 3) issue_code(cu, c0 + 4 + (i >> 2));
+            }
+    };
+
+    // prologue: superstages 0 and 1
+#pragma unroll
+    for (int i = 0; i < 16; ++i) issue_code(0, i);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) issue_code(1, i);
+    wait_vmcnt<16>();  // this wave's copies of superstage 0 have landed
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    v4u g0w[4], g0x[4], g1w[4], g1x[4], g2w[4], g2x[4], g3w[4], g3x[4];
+    rd_group(g0w, g0x, 0, 0);
+    rd_group(g1w, g1x, 0, 1);
+
+    for (int u = 0; u < nst; ++u) {
+        // in flight: LDS reads of groups 0, 1 of u; the copies of u + 1
+        lds_wait_n<8>(g0w, g0x);
+        group(g0w, g0x, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        rd_group(g2w, g2x, u, 2);
+        lds_wait_n<8>(g1w, g1x);
+        group(g1w, g1x, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        rd_group(g3w, g3x, u, 3);
+        lds_wait_n<8>(g2w, g2x);
+        lds_wait_n<0>(g3w, g3x);
+        wait_vmcnt<0>();               // this wave's copies of u + 1 have landed
+        __builtin_amdgcn_s_barrier();  // every wave: done reading u, copies of u + 1 complete
+        __builtin_amdgcn_sched_barrier(0);
+        rd_group(g0w, g0x, u + 1, 0);  // past the end these read the repeated last superstage: unused
+        rd_group(g1w, g1x, u + 1, 1);
+        // refill the slot just released with superstage u + 2 (past the end: the last one again,
+        // into a slot that is not read any more), one copy after every fourth MFMA
+        group(g2w, g2x, u + 2, 0, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        group(g3w, g3x, u + 2, 8, 1);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_vmcnt<0>();
+    lds_wait_n<0>(g0w, g0x);
+    lds_wait_n<0>(g1w, g1x);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Epilogue through LDS: scaled BF16 sub-tiles row-major (padded pitch), then whole 512-byte rows.
+    float swv[4][4][4];  // sW of this lane's columns: [f][j][e]
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) swv[f][j][e] = sw[min(n0 + 128 * wn + 32 * f + 8 * j + 4 * h + e, N - 1)];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const int ml = 128 * wm + 32 * g + l32;
+        const float sxm = sa[min(m0 + ml, M - 1)];
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int nl = 128 * wn + 32 * f + 8 * j + 4 * h;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = acc[f][g][4 * j + e] * sxm * swv[f][j][e];
+                uint2 pk;
+                pk.x = bf16x2_rne(v[0], v[1]);
+                pk.y = bf16x2_rne(v[2], v[3]);
+                *reinterpret_cast<uint2*>(lds + ml * kOutPitch + 2 * nl) = pk;
+            }
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int r = 0; r < 32; ++r) {
+        const int ml = 64 * wave + 2 * r + h;
+        const int m = m0 + ml;
+        const int n = n0 + 8 * l32;
+        const uint4 v = *reinterpret_cast<const uint4*>(lds + ml * kOutPitch + 16 * l32);
+        if (m >= M) continue;
+        uint16_t* dst = y + (int64_t)m * N + n;
+        if (VEC && n + 7 < N) {
+            *reinterpret_cast<uint4*>(dst) = v;
+        } else {
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (n + e < N) dst[e] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+        }
+    }
+}
+
 // ----------------------------------------------------------------------------
 // Host-side dispatch shared by the FP4 and FP8 entry points.
 // ----------------------------------------------------------------------------
@@ -1208,7 +1416,15 @@ inline hipError_t launch_gemm(const void* qa, const void* sa, const void* qw, co
         const uint8_t* sa8 = reinterpret_cast<const uint8_t*>(sa);
         const uint8_t* sw8 = reinterpret_cast<const uint8_t*>(sw);
         const bool vec16 = N % 8 == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0;
-        if (!FP8 && K % 512 == 0 && scales16 && vec16)
+        if (FP8 && vec16)
+            hipLaunchKernelGGL(gemm_tile_fp8<true>, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, st, a,
+                               reinterpret_cast<const float*>(sa), w, reinterpret_cast<const float*>(sw), out, m, n, k,
+                               tiles_m, tiles_n);
+        else if (FP8)
+            hipLaunchKernelGGL(gemm_tile_fp8<false>, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, st, a,
+                               reinterpret_cast<const float*>(sa), w, reinterpret_cast<const float*>(sw), out, m, n, k,
+                               tiles_m, tiles_n);
+        else if (!FP8 && K % 512 == 0 && scales16 && vec16)
             hipLaunchKernelGGL(gemm_tile_fp4<true>, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, st, a, sa8, w,
                                sw8, out, m, n, k, tiles_m, tiles_n);
         else if (!FP8 && K % 512 == 0 && scales16)
