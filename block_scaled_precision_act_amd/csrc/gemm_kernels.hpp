@@ -933,16 +933,17 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_dma_fp4(const uint8_t* __res
 // A CU's vector memory path moves about one 64-byte half line per clock, and a
 // request for part of a 128-byte line costs as much as the whole line, so
 // every global -> LDS copy here moves whole lines: a superstage is K = 256
-// (128 code bytes per row) of both 256-row operands, 8 rows per wave
-// instruction, into one of two 64 KB slots.  Scales are fetched in bulk, 32
-// bytes per row (K = 1024, four superstages), into one of two 16 KB buffers,
-// a quarter of a block with every superstage's copies.
-// Output tile 256 x 256, 4 waves (2 x 2, 128 x 128 each), 32 x 32 x 64 MFMAs,
-// four k-steps per superstage.  One barrier per superstage, placed once every
-// wave has read all of superstage u (and its own copies of u + 1 have landed):
+// (128 code bytes per row) of both TM-row operands, 8 rows per wave
+// instruction, into one of two slots.  Scales are fetched in bulk, 32 bytes
+// per row (K = 1024, four superstages), into one of two buffers, a quarter of
+// a block with every superstage's copies.
+// Output tile TM x TM (256, or 128 for shapes with too few 256-tiles to fill
+// the CUs), 4 waves (2 x 2, each TM/2 x TM/2 from 32 x 32 x 64 MFMAs), four
+// k-steps per superstage.  One barrier per superstage, placed once every wave
+// has read all of superstage u (and its own copies of u + 1 have landed):
 // after it, each wave reads the scales and the first two k-steps of u + 1 and
-// issues the copies of u + 2 into the slot just released, both behind the 32
-// MFMAs of k-steps 2 and 3 of u (one copy after every other MFMA).
+// issues the copies of u + 2 into the slot just released, both behind the
+// MFMAs of k-steps 2 and 3 of u.
 // K-permutation inside a superstage: lane group h multiplies the row's 16-byte
 // chunks 4h .. 4h+3 in k-steps t = 0..3, so the scale dword at byte 8q + 4h of
 // the row's bulk scale segment (q = superstage within the block) serves all
@@ -950,205 +951,234 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_dma_fp4(const uint8_t* __res
 // which spreads the 16 lanes of every ds_read_b128 phase over all banks.
 // ============================================================================
 namespace tile_fp4 {
-constexpr int kRows = 256;
-constexpr int kRowBytes = 128;                   // code bytes per row per superstage
-constexpr int kOpBytes = kRows * kRowBytes;      // 32 KB
-constexpr int kSlot = 2 * kOpBytes;              // W rows, then A rows
-constexpr int kScaleRow = 32;                    // bulk scale bytes per row (K = 1024)
-constexpr int kScaleBuf = 2 * kRows * kScaleRow; // 16 KB: W rows, then A rows
-constexpr int kLds = 2 * kSlot + 2 * kScaleBuf;  // 160 KB
-constexpr int kOutPitch = 2 * kTileN + 16;       // epilogue staging pitch (bytes): 132 dwords
-static_assert(kTileM * kOutPitch <= kLds, "output staging");
+template <int TM>
+struct Cfg {
+    static constexpr int kRows = TM;                          // rows of each operand
+    static constexpr int kFW = TM / 64;                       // 32 x 32 fragments per wave and dimension
+    static constexpr int kRowBytes = 128;                     // code bytes per row per superstage
+    static constexpr int kOpBytes = kRows * kRowBytes;
+    static constexpr int kSlot = 2 * kOpBytes;                // W rows, then A rows
+    static constexpr int kHalfCopies = kRows / 32;            // code copies per wave per operand and superstage
+    static constexpr int kCodeCopies = 2 * kHalfCopies;
+    static constexpr int kScaleRow = 32;                      // bulk scale bytes per row (K = 1024)
+    static constexpr int kScaleBuf = 2 * kRows * kScaleRow;   // W rows, then A rows
+    static constexpr int kScLane = TM == 256 ? 16 : 4;        // scale bytes per lane and copy
+    static constexpr int kScLanesPerRow = kScaleRow / kScLane;
+    static constexpr int kScRowsPerCopy = 64 / kScLanesPerRow;
+    static constexpr int kScaleCopies = kScaleBuf / (64 * kScLane);  // copies per block
+    static constexpr int kScPerWave = kScaleCopies / 16;             // per wave and superstage
+    static constexpr int kOutPitch = 2 * TM + 16;             // epilogue staging pitch (bytes), odd in 16 bytes
+    static constexpr int kRing = 2 * kSlot + 2 * kScaleBuf;
+    static constexpr int kLds = kRing > TM * kOutPitch ? kRing : TM * kOutPitch;
+    static_assert(kScPerWave >= 1 && kScaleCopies == 16 * kScPerWave && kFW >= 1, "tile shape");
+    static_assert(kLds <= 160 * 1024, "LDS");
+};
 }  // namespace tile_fp4
 
 // VEC: N % 8 == 0 and y 16-byte aligned (whole 16-byte output stores allowed).
-template <bool VEC>
+template <bool VEC, int TM>
 __global__ __launch_bounds__(256, 1) void gemm_tile_fp4(const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa,
-                                                          const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw,
-                                                          uint16_t* __restrict__ y, int M, int N, int K, int tiles_m,
-                                                          int tiles_n) {
-    using namespace tile_fp4;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
+                                                        const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw,
+                                                        uint16_t* __restrict__ y, int M, int N, int K, int tiles_m,
+                                                        int tiles_n) {
+    using C = tile_fp4::Cfg<TM>;
+    constexpr int FW = C::kFW;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[C::kLds];
 
     int tm, tn;
     tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
-    const int m0 = tm * kTileM, n0 = tn * kTileN;
+    const int m0 = tm * TM, n0 = tn * TM;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wn = wave & 1, wm = wave >> 1;
     const int l32 = lane & 31, h = lane >> 5;
     const int64_t KB = (int64_t)K / 2, KS = (int64_t)K / 32;
     const int nsup = K / 256;
 
-    // code copy i (0..15): W rows for i < 8, A rows for i >= 8; rows 64 * wave + 8 * (i % 8) + lane / 8,
-    // the lane fills physical chunk lane % 8 with logical chunk (lane % 8) ^ ((row / 2) % 8)
-    const uint8_t* wrow[8];
-    const uint8_t* xrow[8];
+    // code copy i (0 .. kCodeCopies-1): W rows for i < kHalfCopies, then A rows; copy i' = i mod
+    // kHalfCopies moves rows 8 (kHalfCopies * wave + i') + lane / 8, the lane filling physical chunk
+    // lane % 8 with logical chunk (lane % 8) ^ ((row / 2) % 8)
+    const uint8_t* wrow[C::kHalfCopies];
+    const uint8_t* xrow[C::kHalfCopies];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int row = 64 * wave + 8 * i + (lane >> 3);
+    for (int i = 0; i < C::kHalfCopies; ++i) {
+        const int row = 8 * (C::kHalfCopies * wave + i) + (lane >> 3);
         const int chunk = (lane & 7) ^ ((row >> 1) & 7);
         wrow[i] = qw + (int64_t)min(n0 + row, N - 1) * KB + 16 * chunk;
         xrow[i] = qa + (int64_t)min(m0 + row, M - 1) * KB + 16 * chunk;
     }
     auto issue_code = [&](int u, int i) {  // copy i of superstage min(u, nsup - 1) into the slot of u
-        uint8_t* slot = lds + (u & 1) * kSlot;
-        const int64_t koff = (int64_t)min(u, nsup - 1) * kRowBytes;
-        if (i < 8) g2lds16(wrow[i] + koff, slot + (8 * wave + i) * 1024);
-        else g2lds16(xrow[i - 8] + koff, slot + kOpBytes + (8 * wave + i - 8) * 1024);
+        uint8_t* slot = lds + (u & 1) * C::kSlot;
+        const int64_t koff = (int64_t)min(u, nsup - 1) * C::kRowBytes;
+        if (i < C::kHalfCopies) g2lds16(wrow[i] + koff, slot + (C::kHalfCopies * wave + i) * 1024);
+        else g2lds16(xrow[i - C::kHalfCopies] + koff, slot + C::kOpBytes + (C::kHalfCopies * wave + i - C::kHalfCopies) * 1024);
     };
-    // scale copy part j (0..3) of block b: instruction 4j + wave moves the 32-byte segments of
-    // rows 32 (4j + wave) + lane / 2 (W rows 0..255, then A rows), lane % 2 = which 16-byte half.
-    // The part is copied with the codes of superstage 4b - 3 + j: after every wave has finished
-    // with block b - 2 in the same buffer (last read for superstage 4b - 5) and in time for 4b.
-    auto issue_scale = [&](int u) {
-        const int b = (u + 3) >> 2, j = (u + 3) & 3;
-        const int q = 4 * j + wave;
-        const int row = 32 * (q & 7) + (lane >> 1);
-        int64_t off = 32 * (int64_t)b + 16 * (lane & 1);
+    // scale copy q (0 .. kScaleCopies-1) of block b moves the 32-byte segments of rows
+    // kScRowsPerCopy (q mod kScaleCopies/2) + lane / kScLanesPerRow (W rows, then A rows), each lane
+    // kScLane bytes of one; it lands at byte 64 kScLane q of the buffer, so row r of W sits at 32 r
+    // and row r of A at 32 (TM + r).  Part j (0..3) of a block is copies 4 kScPerWave j + kScPerWave
+    // wave + c (c < kScPerWave): every wave carries the same number, so no wave branches.  Part j
+    // travels with the codes of superstage 4b - 3 + j: after every wave has finished with block
+    // b - 2 in the same buffer (last read for superstage 4b - 5) and in time for 4b.
+    auto issue_scale_copy = [&](int q, int b) {
+        constexpr int half = C::kScaleCopies / 2;
+        const int row = C::kScRowsPerCopy * (q % half) + lane / C::kScLanesPerRow;
+        int64_t off = 32 * (int64_t)b + C::kScLane * (lane % C::kScLanesPerRow);
         if (off >= KS) off = 0;  // past the last block: any in-row address, never read
-        const uint8_t* src =
-            q < 8 ? sw + (int64_t)min(n0 + row, N - 1) * KS + off : sa + (int64_t)min(m0 + row, M - 1) * KS + off;
-        g2lds16(src, lds + 2 * kSlot + (b & 1) * kScaleBuf + q * 1024);
+        const uint8_t* src = q < half ? sw + (int64_t)min(n0 + row, N - 1) * KS + off
+                                      : sa + (int64_t)min(m0 + row, M - 1) * KS + off;
+        uint8_t* dst = lds + 2 * C::kSlot + (b & 1) * C::kScaleBuf + q * 64 * C::kScLane;
+        if constexpr (C::kScLane == 16) g2lds16(src, dst);
+        else g2lds4(src, dst);
+    };
+    auto issue_scale = [&](int u) {  // the scale part travelling with superstage u
+#pragma unroll
+        for (int c = 0; c < C::kScPerWave; ++c)
+            issue_scale_copy(4 * C::kScPerWave * ((u + 3) & 3) + C::kScPerWave * wave + c, (u + 3) >> 2);
     };
 
     // per-lane LDS offsets
-    int woff[4], xoff[4], wsoff[4], xsoff[4];
+    int woff[FW], xoff[FW], wsoff[FW], xsoff[FW];
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-        const int wr = 128 * wn + 32 * f + l32, xr = 128 * wm + 32 * f + l32;
-        woff[f] = wr * kRowBytes + ((wr >> 1) & 7);  // low bits: the swizzle key, split off below
-        xoff[f] = kOpBytes + xr * kRowBytes + ((xr >> 1) & 7);
-        wsoff[f] = wr * kScaleRow + 4 * h;
-        xsoff[f] = (kRows + xr) * kScaleRow + 4 * h;
+    for (int f = 0; f < FW; ++f) {
+        const int wr = (TM / 2) * wn + 32 * f + l32, xr = (TM / 2) * wm + 32 * f + l32;
+        woff[f] = wr * C::kRowBytes + ((wr >> 1) & 7);  // low bits: the swizzle key, split off below
+        xoff[f] = C::kOpBytes + xr * C::kRowBytes + ((xr >> 1) & 7);
+        wsoff[f] = wr * C::kScaleRow + 4 * h;
+        xsoff[f] = (C::kRows + xr) * C::kScaleRow + 4 * h;
     }
     const uint32_t base = lds_addr(lds);
-    auto rd_step = [&](v4u (&rw)[4], v4u (&rx)[4], int u, int t) {
-        const uint32_t sb = base + (u & 1) * kSlot;
+    auto rd_step = [&](v4u (&rw)[FW], v4u (&rx)[FW], int u, int t) {
+        const uint32_t sb = base + (u & 1) * C::kSlot;
 #pragma unroll
-        for (int f = 0; f < 4; ++f) {
+        for (int f = 0; f < FW; ++f) {
             rw[f] = lds_read16(sb + (woff[f] & ~7) + 16 * ((4 * h + t) ^ (woff[f] & 7)));
             rx[f] = lds_read16(sb + (xoff[f] & ~7) + 16 * ((4 * h + t) ^ (xoff[f] & 7)));
         }
     };
-    auto rd_scales = [&](uint32_t (&ws)[4], uint32_t (&xs)[4], int u) {
-        const uint32_t scb = base + 2 * kSlot + ((u >> 2) & 1) * kScaleBuf + 8 * (u & 3);
+    auto rd_scales = [&](uint32_t (&ws)[FW], uint32_t (&xs)[FW], int u) {
+        const uint32_t scb = base + 2 * C::kSlot + ((u >> 2) & 1) * C::kScaleBuf + 8 * (u & 3);
 #pragma unroll
-        for (int f = 0; f < 4; ++f) {
+        for (int f = 0; f < FW; ++f) {
             ws[f] = lds_read4(scb + wsoff[f]);
             xs[f] = lds_read4(scb + xsoff[f]);
         }
     };
 
-    v16f acc[4][4];
+    v16f acc[FW][FW];
 #pragma unroll
-    for (int f = 0; f < 4; ++f)
+    for (int f = 0; f < FW; ++f)
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
+        for (int g = 0; g < FW; ++g)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[f][g][r] = 0.f;
 
     // prologue: scale block 0, the codes of superstage 0, then the batch of superstage 1
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int q = 4 * j + wave;
-        const int row = 32 * (q & 7) + (lane >> 1);
-        const int64_t off = 16 * (lane & 1);
-        const uint8_t* src =
-            q < 8 ? sw + (int64_t)min(n0 + row, N - 1) * KS + off : sa + (int64_t)min(m0 + row, M - 1) * KS + off;
-        g2lds16(src, lds + 2 * kSlot + q * 1024);
-    }
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) issue_code(0, i);
+        for (int c = 0; c < C::kScPerWave; ++c) issue_scale_copy(4 * C::kScPerWave * j + C::kScPerWave * wave + c, 0);
+#pragma unroll
+    for (int i = 0; i < C::kCodeCopies; ++i) issue_code(0, i);
     issue_scale(1);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) issue_code(1, i);
-    wait_vmcnt<17>();  // superstage 0 and scale block 0 are in (this wave's copies)
+    for (int i = 0; i < C::kCodeCopies; ++i) issue_code(1, i);
+    wait_vmcnt<C::kCodeCopies + C::kScPerWave>();  // superstage 0 and scale block 0 are in
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
 
-    uint32_t wsc[4], xsc[4];
-    v4u r0w[4], r0x[4], r1w[4], r1x[4], r2w[4], r2x[4], r3w[4], r3x[4];
+    uint32_t wsc[FW], xsc[FW];
+    v4u r0w[FW], r0x[FW], r1w[FW], r1x[FW], r2w[FW], r2x[FW], r3w[FW], r3x[FW];
     rd_scales(wsc, xsc, 0);
     rd_step(r0w, r0x, 0, 0);
     rd_step(r1w, r1x, 0, 1);
 
 #define MX_STEP(RW, RX, T)                                                                                           \
-    _Pragma("unroll") for (int f = 0; f < 4; ++f) _Pragma("unroll") for (int g = 0; g < 4; ++g) acc[f][g] =          \
+    _Pragma("unroll") for (int f = 0; f < FW; ++f) _Pragma("unroll") for (int g = 0; g < FW; ++g) acc[f][g] =         \
         mfma32<kFmtFP4, T>(fp4_operand(RW[f]), fp4_operand(RX[g]), acc[f][g], (int)wsc[f], (int)xsc[g]);
 
     for (int u = 0; u < nsup; ++u) {
         // in flight: scales + k-steps 0, 1 of u (LDS reads); the copies of u + 1
-        lds_wait_first(r0w, r0x, wsc, xsc);  // lgkmcnt(8): scales and k-step 0
+        lds_wait_first_n<FW>(r0w, r0x, wsc, xsc);  // scales and k-step 0
         MX_STEP(r0w, r0x, 0)
         __builtin_amdgcn_sched_barrier(0);
         rd_step(r2w, r2x, u, 2);
-        lds_wait_n<8>(r1w, r1x);
+        lds_wait_n_of<2 * FW, FW>(r1w, r1x);
         MX_STEP(r1w, r1x, 1)
         __builtin_amdgcn_sched_barrier(0);
         rd_step(r3w, r3x, u, 3);
-        lds_wait_n<0>(r2w, r2x);
-        lds_wait_n<0>(r3w, r3x);
+        lds_wait_n_of<0, FW>(r2w, r2x);
+        lds_wait_n_of<0, FW>(r3w, r3x);
         wait_vmcnt<0>();  // this wave's copies of u + 1 (and of the scale part) have landed
         __builtin_amdgcn_s_barrier();  // every wave: done reading u, copies of u + 1 complete
         __builtin_amdgcn_sched_barrier(0);
-        const uint32_t wsu[4] = {wsc[0], wsc[1], wsc[2], wsc[3]};
-        const uint32_t xsu[4] = {xsc[0], xsc[1], xsc[2], xsc[3]};
+        uint32_t wsk[FW], xsk[FW];  // the scales of u, still needed for k-steps 2 and 3
+#pragma unroll
+        for (int f = 0; f < FW; ++f) {
+            wsk[f] = wsc[f];
+            xsk[f] = xsc[f];
+        }
         rd_scales(wsc, xsc, u + 1);  // past the end these read the repeated last superstage: unused
         rd_step(r0w, r0x, u + 1, 0);
         rd_step(r1w, r1x, u + 1, 1);
         issue_scale(u + 2);
+        // k-steps 2 and 3 of u (2 FW^2 MFMAs) with the kCodeCopies copies of u + 2 spread between them
+        constexpr int kMf = 2 * FW * FW;
+        constexpr int kEvery = kMf / C::kCodeCopies > 0 ? kMf / C::kCodeCopies : 1;
 #pragma unroll
         for (int t = 2; t < 4; ++t)
 #pragma unroll
-            for (int f = 0; f < 4; ++f)
+            for (int f = 0; f < FW; ++f)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
+                for (int g = 0; g < FW; ++g) {
+                    const int i = (t - 2) * FW * FW + f * FW + g;
                     if (t == 2)
-                        acc[f][g] = mfma32<kFmtFP4, 2>(fp4_operand(r2w[f]), fp4_operand(r2x[g]), acc[f][g], (int)wsu[f],
-                                                       (int)xsu[g]);
+                        acc[f][g] = mfma32<kFmtFP4, 2>(fp4_operand(r2w[f]), fp4_operand(r2x[g]), acc[f][g], (int)wsk[f],
+                                                       (int)xsk[g]);
                     else
-                        acc[f][g] = mfma32<kFmtFP4, 3>(fp4_operand(r3w[f]), fp4_operand(r3x[g]), acc[f][g], (int)wsu[f],
-                                                       (int)xsu[g]);
-                    if ((f * 4 + g) & 1) issue_code(u + 2, 8 * (t - 2) + ((f * 4 + g) >> 1));
+                        acc[f][g] = mfma32<kFmtFP4, 3>(fp4_operand(r3w[f]), fp4_operand(r3x[g]), acc[f][g], (int)wsk[f],
+                                                       (int)xsk[g]);
+                    if ((i % kEvery) == kEvery - 1 && i / kEvery < C::kCodeCopies) issue_code(u + 2, i / kEvery);
                 }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // then one global -> LDS copy
+        for (int i = 0; i < C::kCodeCopies; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, kEvery, 0);  // kEvery MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);       // then one global -> LDS copy
         }
         __builtin_amdgcn_sched_barrier(0);
     }
 #undef MX_STEP
     wait_vmcnt<0>();
-    lds_wait_n<0>(r0w, r0x);
-    lds_wait_n<0>(r1w, r1x);
+    lds_wait_n_of<0, FW>(r0w, r0x);
+    lds_wait_n_of<0, FW>(r1w, r1x);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
 
     // Epilogue through LDS: each wave writes its BF16 sub-tile row-major (padded pitch), then the
-    // workgroup stores whole 512-byte tile rows.
+    // workgroup stores whole tile rows (2 TM bytes each).
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        const int ml = 128 * wm + 32 * g + l32;
+    for (int g = 0; g < FW; ++g) {
+        const int ml = (TM / 2) * wm + 32 * g + l32;
 #pragma unroll
-        for (int f = 0; f < 4; ++f)
+        for (int f = 0; f < FW; ++f)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int nl = 128 * wn + 32 * f + 8 * j + 4 * h;
+                const int nl = (TM / 2) * wn + 32 * f + 8 * j + 4 * h;
                 uint2 pk;
                 pk.x = bf16x2_rne(acc[f][g][4 * j], acc[f][g][4 * j + 1]);
                 pk.y = bf16x2_rne(acc[f][g][4 * j + 2], acc[f][g][4 * j + 3]);
-                *reinterpret_cast<uint2*>(lds + ml * kOutPitch + 2 * nl) = pk;
+                *reinterpret_cast<uint2*>(lds + ml * C::kOutPitch + 2 * nl) = pk;
             }
     }
     __syncthreads();
-    // wave w stores tile rows 64 w .. 64 w + 63, two rows per instruction (32 lanes x 16 bytes each)
+    constexpr int kLanesPerRow = TM / 8;          // 16-byte pieces per tile row
+    constexpr int kRowsPerStore = 64 / kLanesPerRow;
+    const int lr = lane / kLanesPerRow, lc = lane % kLanesPerRow;
 #pragma unroll 4
-    for (int r = 0; r < 32; ++r) {
-        const int ml = 64 * wave + 2 * r + h;
+    for (int r = 0; r < TM / 4 / kRowsPerStore; ++r) {
+        const int ml = (TM / 4) * wave + kRowsPerStore * r + lr;
         const int m = m0 + ml;
-        const int n = n0 + 8 * l32;
-        const uint4 v = *reinterpret_cast<const uint4*>(lds + ml * kOutPitch + 16 * l32);
+        const int n = n0 + 8 * lc;
+        const uint4 v = *reinterpret_cast<const uint4*>(lds + ml * C::kOutPitch + 16 * lc);
         if (m >= M) continue;
         uint16_t* dst = y + (int64_t)m * N + n;
         if (VEC && n + 7 < N) {
@@ -1424,12 +1454,25 @@ inline hipError_t launch_gemm(const void* qa, const void* sa, const void* qw, co
             hipLaunchKernelGGL(gemm_tile_fp8<false>, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, st, a,
                                reinterpret_cast<const float*>(sa), w, reinterpret_cast<const float*>(sw), out, m, n, k,
                                tiles_m, tiles_n);
-        else if (!FP8 && K % 512 == 0 && scales16 && vec16)
-            hipLaunchKernelGGL(gemm_tile_fp4<true>, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, st, a, sa8, w,
-                               sw8, out, m, n, k, tiles_m, tiles_n);
-        else if (!FP8 && K % 512 == 0 && scales16)
-            hipLaunchKernelGGL(gemm_tile_fp4<false>, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, st, a, sa8, w,
-                               sw8, out, m, n, k, tiles_m, tiles_n);
+        else if (!FP8 && K % 512 == 0 && scales16) {
+            // 128-row tiles when 256-row tiles would leave many CUs idle: up to about 160 256-tiles
+            // (on 256 CUs) four times as many 128-tiles finish sooner
+            const bool small = (int64_t)tiles_m * tiles_n <= 160;
+            const int tm128 = (int)((M + 127) / 128), tn128 = (int)((N + 127) / 128);
+            const dim3 g256((unsigned)(tiles_m * tiles_n)), g128((unsigned)(tm128 * tn128));
+            if (small && vec16)
+                hipLaunchKernelGGL((gemm_tile_fp4<true, 128>), g128, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k,
+                                   tm128, tn128);
+            else if (small)
+                hipLaunchKernelGGL((gemm_tile_fp4<false, 128>), g128, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k,
+                                   tm128, tn128);
+            else if (vec16)
+                hipLaunchKernelGGL((gemm_tile_fp4<true, 256>), g256, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k,
+                                   tiles_m, tiles_n);
+            else
+                hipLaunchKernelGGL((gemm_tile_fp4<false, 256>), g256, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k,
+                                   tiles_m, tiles_n);
+        }
         else if (!FP8 && K % 256 == 0)
             hipLaunchKernelGGL(gemm_tile_dma_fp4<4>, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, st, a,
                                reinterpret_cast<const uint8_t*>(sa), w, reinterpret_cast<const uint8_t*>(sw), out, m, n,

@@ -155,6 +155,22 @@ __device__ __forceinline__ void lds_wait_dec(v4u (&w)[4], v4u (&x)[4][MF], uint3
     for (int g = 0; g < MF; ++g) asm volatile("" : "+v"(xs[g]));
 }
 
+// lgkmcnt(2 FW): scales (2 FW dwords) and the first FW + FW operands done, tied to them.
+template <int FW>
+__device__ __forceinline__ void lds_wait_first_n(v4u (&a)[FW], v4u (&b)[FW], uint32_t (&c)[FW], uint32_t (&d)[FW]) {
+    asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(2 * FW));
+#pragma unroll
+    for (int i = 0; i < FW; ++i) asm volatile("" : "+v"(a[i]), "+v"(b[i]), "+v"(c[i]), "+v"(d[i]));
+}
+// lgkmcnt(N) tied to FW 16-byte results of each of two groups.
+template <int N, int FW>
+__device__ __forceinline__ void lds_wait_n_of(v4u (&a)[FW], v4u (&b)[FW]) {
+    static_assert(N >= 0 && N < 16, "lgkmcnt range");
+    asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N));
+#pragma unroll
+    for (int i = 0; i < FW; ++i) asm volatile("" : "+v"(a[i]), "+v"(b[i]));
+}
+
 __device__ __forceinline__ uint4 ldg16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
 // 16-byte load of data used once (non-temporal hint: evict first from the caches).
 __device__ __forceinline__ uint4 ldg16_stream(const uint8_t* p) {
