@@ -375,7 +375,7 @@ def profile_pass(ctx):
 # Kernels whose HBM traffic the bench reports: key -> (name fragment, grid size in threads or None)
 PMC_KERNELS = {
     "gemm_decode_fp4_m64": ("gemm_decode_fp4<2, 2>", None),
-    "gemm_tile_fp4_m8192": ("gemm_tile_fp4<true>", 896 * 256),
+    "gemm_tile_fp4_m8192": ("gemm_tile_fp4<true, 256>", 896 * 256),
 }
 COPY_BYTES = 256 << 20  # the profile pass copies 256 MiB device -> device
 
