@@ -558,6 +558,169 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_fp4(const uint8_t* __restr
 }
 
 // ============================================================================
+// Decode path, FP8 (E4M3 codes, FP32 per-row scales; M <= 64, K % 512 == 0).
+// The FP4 decode design above on byte codes: one workgroup (4 waves) per 32
+// output columns, wave w owns a quarter of K and streams its K = 128 slabs
+// (128 code bytes per row: the 32*MF activation rows, then the 32 weight rows)
+// into a private ring of S slots with whole-line global -> LDS copies, waiting
+// only for its own copies.  There are no block scales, so the ring is deeper.
+// Each 16-byte chunk a lane reads is widened exactly to two 8 x FP16 MFMA
+// operands (every E4M3 value is an FP16 normal) for v_mfma_f32_32x32x16_f16:
+// lane group h takes chunks 4h .. 4h+3, chunk 4h+t half u feeding k-step
+// (t, u) of both operands.  The four partial tiles are summed through LDS in a
+// fixed order; the epilogue applies (sum * sA[m]) * sW[n] and rounds to BF16.
+// ============================================================================
+namespace dec8 {
+constexpr int kNT = 32;             // output columns per workgroup
+constexpr int kSlab = 128;          // code bytes per row per slab (K = 128)
+template <int MF, int S>
+struct Cfg {
+    static constexpr int kArows = 32 * MF;
+    static constexpr int kRows = kArows + kNT;              // activation rows, then weight rows
+    static constexpr int kSlabBytes = kRows * kSlab;         // 12 KB (MF = 2) or 8 KB
+    static constexpr int kCopies = kSlabBytes / 1024;        // copies per wave per slab
+    static constexpr int kLds = 4 * S * kSlabBytes;
+    static_assert(S * kCopies <= 63, "vmcnt");
+    static_assert(kLds <= 160 * 1024, "LDS");
+    static_assert(4 * MF * 16 * 64 * 4 <= kLds, "reduction staging");
+};
+}  // namespace dec8
+
+template <int MF, int S>
+__global__ __launch_bounds__(256, 1) void gemm_decode_fp8(const uint8_t* __restrict__ qa, const float* __restrict__ sa,
+                                                          const uint8_t* __restrict__ qw, const float* __restrict__ sw,
+                                                          uint16_t* __restrict__ y, int M, int N, int K) {
+    using C = dec8::Cfg<MF, S>;
+    using namespace dec8;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[C::kLds];
+    const int n0 = blockIdx.x * kNT;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l32 = lane & 31, h = lane >> 5;
+    const int nmine = K / 512;              // slabs per wave
+    const int s0 = wave * nmine;            // first slab of this wave
+    uint8_t* const ring = lds + wave * S * C::kSlabBytes;
+
+    // code copies: copy i moves rows 8i .. 8i+7 (lane / 8) of the slab, the lane filling chunk
+    // lane % 8 with logical chunk (lane % 8) ^ ((row / 2) % 8).  An activation copy whose 8 rows
+    // all lie at or past M reads one address in every lane (one cache line): those rows only feed
+    // outputs that are never stored.  A batch for a slab past the wave's last one also reads a
+    // single address, so every wave issues the same number of copies and the waits are fixed.
+    const uint8_t* rowp[C::kCopies];
+#pragma unroll
+    for (int i = 0; i < C::kCopies; ++i) {
+        const int r = 8 * i + (lane >> 3);
+        const int chunk = (lane & 7) ^ ((r >> 1) & 7);
+        if (r < C::kArows)
+            rowp[i] = 8 * i < M ? qa + (int64_t)min(r, M - 1) * K + 16 * chunk : qa;
+        else
+            rowp[i] = qw + (int64_t)min(n0 + r - C::kArows, N - 1) * K + 16 * chunk;
+    }
+    auto issue = [&](int j) {  // slab s0 + j into slot j % S
+        uint8_t* slot = ring + (j % S) * C::kSlabBytes;
+        const bool real = j < nmine;
+        const int64_t koff = (int64_t)(s0 + (real ? j : 0)) * kSlab;
+#pragma unroll
+        for (int i = 0; i < C::kCopies; ++i) {
+            const uint8_t* src = real ? rowp[i] + koff : qw;
+            if (8 * i < C::kArows) g2lds16(src, slot + 1024 * i);    // activations: reused by every CU
+            else g2lds16_nt(src, slot + 1024 * i);                   // weights: streamed once
+        }
+    };
+#pragma unroll
+    for (int j = 0; j < S; ++j) issue(j);
+
+    const uint32_t rbase = lds_addr(ring);
+    int xoff[MF], xsw[MF];
+#pragma unroll
+    for (int g = 0; g < MF; ++g) {
+        const int r = 32 * g + l32;
+        xoff[g] = r * kSlab;
+        xsw[g] = (r >> 1) & 7;
+    }
+    const int wr = C::kArows + l32;
+    const int woff = wr * kSlab, wsw = (wr >> 1) & 7;
+
+    v16f acc[MF];
+#pragma unroll
+    for (int g = 0; g < MF; ++g)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[g][r] = 0.f;
+
+    for (int j = 0; j < nmine; ++j) {
+        // slab j has landed once only the later S - 1 batches may still be in flight
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<(S - 1) * C::kCopies>();
+        __builtin_amdgcn_sched_barrier(0);
+        const uint32_t sb = rbase + (j % S) * C::kSlabBytes;
+        v4u wv[4], xv[4][MF];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            wv[t] = lds_read16(sb + woff + 16 * ((4 * h + t) ^ wsw));
+#pragma unroll
+            for (int g = 0; g < MF; ++g) xv[t][g] = lds_read16(sb + xoff[g] + 16 * ((4 * h + t) ^ xsw[g]));
+        }
+        lds_wait_codes<MF>(wv, xv);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(j + S);  // the slot is read: refill it
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const v8h w0 = e4m3x8_to_f16x8(wv[t][0], wv[t][1]);
+            const v8h w1 = e4m3x8_to_f16x8(wv[t][2], wv[t][3]);
+#pragma unroll
+            for (int g = 0; g < MF; ++g) {
+                acc[g] = mfma32_f16(w0, e4m3x8_to_f16x8(xv[t][g][0], xv[t][g][1]), acc[g]);
+                acc[g] = mfma32_f16(w1, e4m3x8_to_f16x8(xv[t][g][2], xv[t][g][3]), acc[g]);
+            }
+        }
+    }
+
+    // fixed-order reduction of the four partial tiles through LDS, then the row and column scales
+    wait_vmcnt<0>();  // the trailing refills
+    __syncthreads();  // every wave is done with its ring
+    float* red = reinterpret_cast<float*>(lds);  // [wave][g][reg][lane]
+#pragma unroll
+    for (int g = 0; g < MF; ++g)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) red[((wave * MF + g) * 16 + r) * 64 + lane] = acc[g][r];
+    __syncthreads();
+    // wave w finalizes register quad w of every fragment: D rows (n) 8w + 4h + e, column (m) l32
+    const bool vec_ok = (N & 3) == 0 && (reinterpret_cast<uintptr_t>(y) & 7) == 0;
+    const int n = n0 + 8 * wave + 4 * h;
+    float swn[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) swn[e] = sw[min(n + e, N - 1)];
+#pragma unroll
+    for (int g = 0; g < MF; ++g) {
+        const int m = 32 * g + l32;
+        if (m >= M) continue;
+        const float sam = sa[m];
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 4 * wave + e;
+            float t = red[((0 * MF + g) * 16 + r) * 64 + lane];
+            t += red[((1 * MF + g) * 16 + r) * 64 + lane];
+            t += red[((2 * MF + g) * 16 + r) * 64 + lane];
+            t += red[((3 * MF + g) * 16 + r) * 64 + lane];
+            v[e] = t * sam * swn[e];
+        }
+        uint16_t* dst = y + (int64_t)m * N + n;
+        if (vec_ok && n + 3 < N) {
+            uint2 pk;
+            pk.x = bf16x2_rne(v[0], v[1]);
+            pk.y = bf16x2_rne(v[2], v[3]);
+            *reinterpret_cast<uint2*>(dst) = pk;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (n + e < N) dst[e] = (uint16_t)(bf16x2_rne(v[e], 0.f) & 0xffffu);
+        }
+    }
+}
+
+// ============================================================================
 // Tile path (large M, MFMA-bound).
 // 256 x 256 output tile per workgroup of 4 waves (2 x 2, 128 x 128 each, 4 x 4
 // fragments of 32 x 32).  Each K-stage moves 128 code bytes per row of both
@@ -1431,6 +1594,14 @@ inline hipError_t launch_gemm(const void* qa, const void* sa, const void* qw, co
             hipLaunchKernelGGL(gemm_decode_lds_fp4<4>, grid, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k);
         else
             hipLaunchKernelGGL(gemm_decode_lds_fp4<8>, grid, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k);
+    } else if (FP8 && M <= 64 && K % 512 == 0) {
+        const dim3 grid((unsigned)((N + dec8::kNT - 1) / dec8::kNT));
+        const float* sa32 = reinterpret_cast<const float*>(sa);
+        const float* sw32 = reinterpret_cast<const float*>(sw);
+        if (M <= 32)
+            hipLaunchKernelGGL((gemm_decode_fp8<1, 5>), grid, dim3(256), 0, st, a, sa32, w, sw32, out, m, n, k);
+        else
+            hipLaunchKernelGGL((gemm_decode_fp8<2, 3>), grid, dim3(256), 0, st, a, sa32, w, sw32, out, m, n, k);
     } else if (M <= 128) {
         const dim3 grid((unsigned)((N + 31) / 32));
         if (M <= 16)

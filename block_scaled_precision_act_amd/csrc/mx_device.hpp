@@ -155,6 +155,16 @@ __device__ __forceinline__ void lds_wait_dec(v4u (&w)[4], v4u (&x)[4][MF], uint3
     for (int g = 0; g < MF; ++g) asm volatile("" : "+v"(xs[g]));
 }
 
+// lgkmcnt(0) tied to the FP8 decode kernel's per-slab operands.
+template <int MF>
+__device__ __forceinline__ void lds_wait_codes(v4u (&w)[4], v4u (&x)[4][MF]) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]));
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int g = 0; g < MF; ++g) asm volatile("" : "+v"(x[t][g]));
+}
+
 // lgkmcnt(2 FW): scales (2 FW dwords) and the first FW + FW operands done, tied to them.
 template <int FW>
 __device__ __forceinline__ void lds_wait_first_n(v4u (&a)[FW], v4u (&b)[FW], uint32_t (&c)[FW], uint32_t (&d)[FW]) {
