@@ -369,42 +369,45 @@ __global__ __launch_bounds__(256) void gemm_decode_lds_fp4(const uint8_t* __rest
 // global -> LDS (global_load_lds) 8 whole rows (whole cache lines) per wave
 // instruction.  Wave w owns the w-th quarter of K (nmine = K / 1024
 // consecutive slabs, an even count) and a private ring of S slab slots, so it
-// waits only for its own copies; the scale bytes of its quarter of K (8 bytes
-// per row and slab) go to a private LDS block the same way.  No wave waits for another
-// until the end, when the four partial tiles are summed through LDS in a fixed
-// order (deterministic).
+// waits only for its own copies.  The workgroup's scale rows (K/32 bytes each:
+// 64 activation rows, then 32 weight rows, contiguous in memory) are copied
+// once, up front, as whole lines into one shared block; after that single
+// barrier no wave waits for another until the end, when the four partial
+// tiles are summed through LDS in a fixed order (deterministic).
 // MFMA: 32 x 32 x 64, operand A = 32 weight rows (n), operand B = 32
 // activation rows (m); k-step t of a slab uses the row's chunks 4h + t in lane
 // group h (the K-permutation and (row / 2) % 8 chunk swizzle of the tile
 // path), so one scale dword per row and slab serves all four k-steps.  In the
-// scale block, row r's 16-byte pieces are rotated by r / 4, which spreads the
-// 32 rows of a fragment over the LDS banks.
+// scale block, row r's 16-byte pieces are rotated by r (position p holds piece
+// (p + r) mod P), which spreads the 32 rows of a fragment over the LDS banks.
 // ============================================================================
 namespace dec4 {
 constexpr int kNT = 32;             // output columns per workgroup
 constexpr int kSlab = 128;          // code bytes per row per slab (K = 256)
 constexpr int kMaxMine = 16;        // slabs per wave supported (K <= 16384)
-template <int MF, int S>
+// KSMAX: scale bytes per row the shared block holds (256: K <= 8192, 512: K <= 16384)
+template <int MF, int S, int KSMAX>
 struct Cfg {
     static constexpr int kArows = 32 * MF;
     static constexpr int kRows = kArows + kNT;              // activation rows, then weight rows
     static constexpr int kSlabBytes = kRows * kSlab;         // 12 KB (MF = 2) or 8 KB
     static constexpr int kCopies = kSlabBytes / 1024;        // copies per wave per slab
-    static constexpr int kScCopies = kRows * kMaxMine * 8 / 1024;  // scale copies per wave
+    static constexpr int kScBytes = kRows * KSMAX;           // shared scale block
+    static constexpr int kScCopies = kScBytes / 1024 / 4;    // scale copies per wave
     static constexpr int kRing = 4 * S * kSlabBytes;
-    static constexpr int kScBlock = kScCopies * 1024;       // private scale block per wave
-    static constexpr int kLds = kRing + 4 * kScBlock;
+    static constexpr int kLds = kRing + kScBytes;
+    static_assert(kScCopies * 4096 == kScBytes, "scale copies");
     static_assert(kScCopies + S * kCopies <= 63, "vmcnt");
     static_assert(kLds <= 160 * 1024, "LDS");
     static_assert(4 * MF * 16 * 64 * 4 <= kLds, "reduction staging");
 };
 }  // namespace dec4
 
-template <int MF, int S>
+template <int MF, int S, int KSMAX>
 __global__ __launch_bounds__(256, 1) void gemm_decode_fp4(const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa,
                                                           const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw,
                                                           uint16_t* __restrict__ y, int M, int N, int K) {
-    using C = dec4::Cfg<MF, S>;
+    using C = dec4::Cfg<MF, S, KSMAX>;
     using namespace dec4;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[C::kLds];
     const int n0 = blockIdx.x * kNT;
@@ -416,21 +419,24 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_fp4(const uint8_t* __restr
     const int nmine = K / 1024;             // slabs per wave (even)
     const int s0 = wave * nmine;            // first slab of this wave
     uint8_t* const ring = lds + wave * S * C::kSlabBytes;
-    uint8_t* const scb = lds + C::kRing + wave * C::kScBlock;
+    uint8_t* const scb = lds + C::kRing;
 
-    // 1. this wave's scale bytes: row r, bytes [8 s0, 8 s0 + 8 nmine), ncw = nmine / 2 pieces of 16
-    //    bytes; piece position p of row r holds piece (p + r / 4) % ncw.  Positions past the data
-    //    repeat its last piece.
-    const int ncw = nmine / 2, sctotal = C::kRows * ncw;
+    // 1. the workgroup's scale rows, whole: P = K / 512 pieces of 16 bytes per row; piece q = 64 c +
+    //    lane of copy c (wave w issues c = w kScCopies + e) is position q mod P of row q / P, which
+    //    holds piece (position + row) mod P.  Pieces past the data read one address (never used).
+    const int P = KS / 16;
 #pragma unroll
-    for (int it = 0; it < C::kScCopies; ++it) {
-        const int idx = min(64 * it + lane, sctotal - 1);
-        const int r = idx / ncw, p = idx - r * ncw;
-        const int c = (p + (r >> 2)) % ncw;
-        const int64_t off = 8 * (int64_t)s0 + 16 * c;
-        g2lds16(r < C::kArows ? sa + (int64_t)min(r, M - 1) * KS + off
-                              : sw + (int64_t)min(n0 + r - C::kArows, N - 1) * KS + off,
-                scb + 1024 * it);
+    for (int e = 0; e < C::kScCopies; ++e) {
+        const int c = wave * C::kScCopies + e;
+        const int q = 64 * c + lane;
+        const int r = q / P, p = q - r * P;
+        const uint8_t* src = sa;
+        if (r < C::kRows) {
+            const int64_t off = 16 * ((p + r) % P);
+            src = r < C::kArows ? sa + (int64_t)min(r, M - 1) * KS + off
+                                : sw + (int64_t)min(n0 + r - C::kArows, N - 1) * KS + off;
+        }
+        g2lds16(src, scb + 1024 * c);
     }
     // 2. code copies: copy i moves rows 8i .. 8i+7 (lane / 8) of the slab, the lane filling chunk
     //    lane % 8 with logical chunk (lane % 8) ^ ((row / 2) % 8).  An activation copy whose 8 rows
@@ -461,6 +467,8 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_fp4(const uint8_t* __restr
     };
 #pragma unroll
     for (int j = 0; j < S; ++j) issue(j);
+    wait_vmcnt<S * C::kCopies>();  // this wave's scale copies have landed (its slabs may not have)
+    __builtin_amdgcn_s_barrier();  // and every other wave's
 
     // per-lane LDS offsets (rows: activation fragment g = 32 g + l32, weight rows kArows + l32)
     const uint32_t rbase = lds_addr(ring), sbase = lds_addr(scb);
@@ -475,9 +483,10 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_fp4(const uint8_t* __restr
     const int wr = C::kArows + l32;
     const int woff = wr * kSlab, wsw = (wr >> 1) & 7;
     auto scale_at = [&](int r, int j) -> uint32_t {  // dword of row r for local slab j, lane group h
-        int p = (j >> 1) - (r >> 2) % ncw;
-        if (p < 0) p += ncw;
-        return lds_read4(sbase + 16 * (r * ncw + p) + 8 * (j & 1) + 4 * h);
+        const int s = s0 + j;                            // slab index in K: bytes 8 s .. 8 s + 7 of the row
+        int p = (s >> 1) - r % P;
+        if (p < 0) p += P;
+        return lds_read4(sbase + r * KS + 16 * p + 8 * (s & 1) + 4 * h);
     };
 
     v16f acc[MF];
@@ -1578,10 +1587,14 @@ inline hipError_t launch_gemm(const void* qa, const void* sa, const void* qw, co
         const dim3 grid((unsigned)((N + dec4::kNT - 1) / dec4::kNT));
         const uint8_t* sa8 = reinterpret_cast<const uint8_t*>(sa);
         const uint8_t* sw8 = reinterpret_cast<const uint8_t*>(sw);
-        if (M <= 32)
-            hipLaunchKernelGGL((gemm_decode_fp4<1, 3>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k);
+        if (M <= 32 && K <= 8192)
+            hipLaunchKernelGGL((gemm_decode_fp4<1, 4, 256>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k);
+        else if (M <= 32)
+            hipLaunchKernelGGL((gemm_decode_fp4<1, 4, 512>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k);
+        else if (K <= 8192)
+            hipLaunchKernelGGL((gemm_decode_fp4<2, 2, 256>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k);
         else
-            hipLaunchKernelGGL((gemm_decode_fp4<2, 2>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k);
+            hipLaunchKernelGGL((gemm_decode_fp4<2, 2, 512>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k);
     } else if (!FP8 && M <= 128 && K % 512 == 0) {
         const dim3 grid((unsigned)((N + 31) / 32));
         const uint8_t* sa8 = reinterpret_cast<const uint8_t*>(sa);
