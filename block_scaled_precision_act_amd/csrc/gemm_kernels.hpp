@@ -1114,8 +1114,11 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_dma_fp4(const uint8_t* __res
 // k-steps per superstage.  One barrier per superstage, placed once every wave
 // has read all of superstage u (and its own copies of u + 1 have landed):
 // after it, each wave reads the scales and the first two k-steps of u + 1 and
-// issues the copies of u + 2 into the slot just released, both behind the
-// MFMAs of k-steps 2 and 3 of u.
+// issues the copies of u + 2 into the slot just released, both spread between
+// the MFMAs of k-steps 2 and 3 of u; the operands of k-steps 2 and 3 are read
+// between the MFMAs of k-steps 0 and 1.  Every such placement is fixed with
+// scheduling barriers, so LDS reads and copies go out while the matrix core
+// is busy, and a wave never has more than 15 LDS reads in flight.
 // K-permutation inside a superstage: lane group h multiplies the row's 16-byte
 // chunks 4h .. 4h+3 in k-steps t = 0..3, so the scale dword at byte 8q + 4h of
 // the row's bulk scale segment (q = superstage within the block) serves all
@@ -1227,6 +1230,14 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_fp4(const uint8_t* __restric
             rx[f] = lds_read16(sb + (xoff[f] & ~7) + 16 * ((4 * h + t) ^ (xoff[f] & 7)));
         }
     };
+    // one operand of k-step t of superstage u: read i (0 .. 2 FW - 1) is fragment i / 2 of W (even i)
+    // or of A (odd i), the order rd_step uses
+    auto rd_one = [&](v4u (&rw)[FW], v4u (&rx)[FW], int u, int t, int i) {
+        const uint32_t sb = base + (u & 1) * C::kSlot;
+        const int f = i >> 1;
+        if (i & 1) rx[f] = lds_read16(sb + (xoff[f] & ~7) + 16 * ((4 * h + t) ^ (xoff[f] & 7)));
+        else rw[f] = lds_read16(sb + (woff[f] & ~7) + 16 * ((4 * h + t) ^ (woff[f] & 7)));
+    };
     auto rd_scales = [&](uint32_t (&ws)[FW], uint32_t (&xs)[FW], int u) {
         const uint32_t scb = base + 2 * C::kSlot + ((u >> 2) & 1) * C::kScaleBuf + 8 * (u & 3);
 #pragma unroll
@@ -1264,20 +1275,23 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_fp4(const uint8_t* __restric
     rd_step(r0w, r0x, 0, 0);
     rd_step(r1w, r1x, 0, 1);
 
-#define MX_STEP(RW, RX, T)                                                                                           \
-    _Pragma("unroll") for (int f = 0; f < FW; ++f) _Pragma("unroll") for (int g = 0; g < FW; ++g) acc[f][g] =         \
-        mfma32<kFmtFP4, T>(fp4_operand(RW[f]), fp4_operand(RX[g]), acc[f][g], (int)wsc[f], (int)xsc[g]);
+    // The FW^2 MFMAs of k-step T, with the 2 FW operand reads of k-step TN issued between them (one
+    // after every FW / 2 MFMAs), in this order: the reads go out while the matrix core is busy.
+#define MX_STEP_RD(RW, RX, T, NW, NX, TN)                                                                          \
+    _Pragma("unroll") for (int f = 0; f < FW; ++f) _Pragma("unroll") for (int g = 0; g < FW; ++g) {               \
+        acc[f][g] = mfma32<kFmtFP4, T>(fp4_operand(RW[f]), fp4_operand(RX[g]), acc[f][g], (int)wsc[f], (int)xsc[g]); \
+        if (((f * FW + g) % (FW / 2)) == FW / 2 - 1) rd_one(NW, NX, u, TN, (f * FW + g) / (FW / 2));             \
+        __builtin_amdgcn_sched_barrier(0);                                                                         \
+    }
 
     for (int u = 0; u < nsup; ++u) {
         // in flight: scales + k-steps 0, 1 of u (LDS reads); the copies of u + 1
         lds_wait_first_n<FW>(r0w, r0x, wsc, xsc);  // scales and k-step 0
-        MX_STEP(r0w, r0x, 0)
         __builtin_amdgcn_sched_barrier(0);
-        rd_step(r2w, r2x, u, 2);
+        MX_STEP_RD(r0w, r0x, 0, r2w, r2x, 2)
         lds_wait_n_of<2 * FW, FW>(r1w, r1x);
-        MX_STEP(r1w, r1x, 1)
         __builtin_amdgcn_sched_barrier(0);
-        rd_step(r3w, r3x, u, 3);
+        MX_STEP_RD(r1w, r1x, 1, r3w, r3x, 3)
         lds_wait_n_of<0, FW>(r2w, r2x);
         lds_wait_n_of<0, FW>(r3w, r3x);
         wait_vmcnt<0>();  // this wave's copies of u + 1 (and of the scale part) have landed
@@ -1290,12 +1304,13 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_fp4(const uint8_t* __restric
             xsk[f] = xsc[f];
         }
         rd_scales(wsc, xsc, u + 1);  // past the end these read the repeated last superstage: unused
-        rd_step(r0w, r0x, u + 1, 0);
-        rd_step(r1w, r1x, u + 1, 1);
         issue_scale(u + 2);
-        // k-steps 2 and 3 of u (2 FW^2 MFMAs) with the kCodeCopies copies of u + 2 spread between them
+        // k-steps 2 and 3 of u (2 FW^2 MFMAs), in this order, with the kCodeCopies copies of u + 2 and
+        // the 4 FW operand reads of k-steps 0 and 1 of u + 1 spread between them (a wave keeps at most
+        // 15 LDS reads in flight, so a burst of them would stall it)
         constexpr int kMf = 2 * FW * FW;
         constexpr int kEvery = kMf / C::kCodeCopies > 0 ? kMf / C::kCodeCopies : 1;
+        constexpr int kRdEvery = kMf / (4 * FW);
 #pragma unroll
         for (int t = 2; t < 4; ++t)
 #pragma unroll
@@ -1310,15 +1325,15 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_fp4(const uint8_t* __restric
                         acc[f][g] = mfma32<kFmtFP4, 3>(fp4_operand(r3w[f]), fp4_operand(r3x[g]), acc[f][g], (int)wsk[f],
                                                        (int)xsk[g]);
                     if ((i % kEvery) == kEvery - 1 && i / kEvery < C::kCodeCopies) issue_code(u + 2, i / kEvery);
+                    if ((i % kRdEvery) == kRdEvery - 1) {
+                        const int ri = i / kRdEvery;
+                        if (ri < 2 * FW) rd_one(r0w, r0x, u + 1, 0, ri);
+                        else rd_one(r1w, r1x, u + 1, 1, ri - 2 * FW);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-#pragma unroll
-        for (int i = 0; i < C::kCodeCopies; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, kEvery, 0);  // kEvery MFMAs
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);       // then one global -> LDS copy
-        }
-        __builtin_amdgcn_sched_barrier(0);
     }
-#undef MX_STEP
+#undef MX_STEP_RD
     wait_vmcnt<0>();
     lds_wait_n_of<0, FW>(r0w, r0x);
     lds_wait_n_of<0, FW>(r1w, r1x);
