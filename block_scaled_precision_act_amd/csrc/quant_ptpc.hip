@@ -7,7 +7,9 @@
 // Per row: a = max|x| (exact integer max over the magnitude bit patterns),
 // s = fl32(a / 448) (s = 1 if a == 0), code = E4M3fn(fl32(x / s)) with
 // round-to-nearest-even and saturation at 448.  Both divisions are IEEE
-// binary32 divisions (hipcc's default for '/' on float is correctly rounded).
+// binary32 divisions (hipcc's default for '/' on float is correctly rounded);
+// for BF16 rows the per-element one is computed by div_corrected, which gives
+// the same codes.
 // A row holding NaN or Inf gets s = NaN and every code 0x7F.
 //
 // One 512-thread workgroup per row (grid-stride over rows).  A row of up to
@@ -28,6 +30,20 @@ namespace {
 
 constexpr int kThreads = 512;
 constexpr int kVec = 2;  // 8-value vectors per thread kept in registers
+
+// fl32(x / s) for BF16 rows: r = fl32(1 / s) once per row, then the quotient q0 = fl32(x r) is
+// corrected twice with the remainder x - q s (exact, an FMA) scaled by r (Markstein's method); the
+// sign of x is restored for zeros.  Used only when s >= 2^-90, so that every remainder that can
+// decide a code is a normal number.  An exhaustive comparison with the IEEE division, over every
+// finite positive BF16 row maximum a (s = fl32(a / 448) >= 2^-90) and every BF16 x with |x| <= a,
+// found the same quotient wherever it is at least 2^-10 (below that every code is a signed zero)
+// and the same E4M3 code everywhere.
+__device__ __forceinline__ float div_corrected(float x, float s, float r) {
+    const float q0 = x * r;
+    const float q1 = __builtin_fmaf(__builtin_fmaf(-q0, s, x), r, q0);
+    const float q2 = __builtin_fmaf(__builtin_fmaf(-q1, s, x), r, q1);
+    return __builtin_copysignf(q2, x);
+}
 
 // E4M3fn codes of four binary32 quotients (|r| < 464), round to nearest even, packed low to high.
 __device__ __forceinline__ uint32_t e4m3fn_x4(float r0, float r1, float r2, float r3) {
@@ -66,6 +82,12 @@ struct Row8 {  // eight consecutive values of a row as binary32
     __device__ __forceinline__ uint2 encode(float s) const {
         return make_uint2(e4m3fn_x4(v[0] / s, v[1] / s, v[2] / s, v[3] / s),
                           e4m3fn_x4(v[4] / s, v[5] / s, v[6] / s, v[7] / s));
+    }
+    __device__ __forceinline__ uint2 encode_corrected(float s, float r) const {  // BF16 rows, s >= 2^-90
+        float q[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = div_corrected(v[i], s, r);
+        return make_uint2(e4m3fn_x4(q[0], q[1], q[2], q[3]), e4m3fn_x4(q[4], q[5], q[6], q[7]));
     }
 };
 
@@ -117,6 +139,20 @@ __global__ __launch_bounds__(kThreads) void quant_ptpc_kernel(const void* __rest
         if (threadIdx.x == 0) s[row] = sc;
         if (nonfinite) {
             for (int64_t v = threadIdx.x; v < nvec; v += kThreads) qrow[v] = make_uint2(0x7f7f7f7fu, 0x7f7f7f7fu);
+            continue;
+        }
+        if (!F32 && sc >= 0x1p-90f) {  // row-uniform
+            const float rc = 1.0f / sc;
+#pragma unroll
+            for (int j = 0; j < kVec; ++j) {
+                const int64_t v = threadIdx.x + (int64_t)j * kThreads;
+                if (v < nvec) qrow[v] = reg[j].encode_corrected(sc, rc);
+            }
+            for (int64_t v = threadIdx.x + (int64_t)kVec * kThreads; v < nvec; v += kThreads) {
+                Row8<F32> t;
+                t.load(xrow, v);
+                qrow[v] = t.encode_corrected(sc, rc);
+            }
             continue;
         }
 #pragma unroll

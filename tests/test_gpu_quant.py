@@ -180,6 +180,29 @@ def test_ptpc_act_special_rows(mx, orc):
     _assert_same(q, qo, "codes")
 
 
+def test_ptpc_act_every_pattern_under_varied_maxima(mx, orc):
+    # Row i holds every finite BF16 value x with |x| <= a_i (both signs, zero padded), for row maxima a_i
+    # spread over the whole exponent range and packed around s = a / 448 = 2^-90, where the kernel
+    # switches between its two exact ways of forming fl32(x / s).
+    finite = np.arange(0x7F80, dtype=np.uint32)                     # positive finite BF16 patterns
+    maxima = [2.0 ** e * m for e in range(-133, 128, 5) for m in (1.0, 1.5)]
+    thr = 448.0 * 2.0 ** -90
+    maxima += [thr * f for f in (0.97, 0.99, 1.0, 1.01, 1.03)] + [448.0, 1.0, 3.3e38]
+    rows = []
+    for a in maxima:
+        a_bits = int(synth.f64_to_bf16_bits(np.array([a]))[0])
+        keep = finite[finite <= a_bits]
+        row = np.zeros(65536, np.uint16)
+        row[:keep.size] = keep
+        row[keep.size:2 * keep.size] = keep | 0x8000
+        rows.append(row)
+    bits = np.stack(rows)
+    q, s = _gpu_ptpc_bf16(mx, bits)
+    qo, so = orc.ptpc_quant_bf16(bits, nthreads=16)
+    _assert_scales(s, so)
+    _assert_same(q, qo, "codes")
+
+
 def test_ptpc_weight_f32(mx, orc):
     w = synth.make_weight(synth.CONFIGS["ptpc_a8w8_m64"])
     q, s = mx.quant_weight_ptpc(to_dev(w))
