@@ -75,9 +75,10 @@ template <bool F32>
 __device__ __forceinline__ void convert_unit(const Unit<F32>& x, uint32_t* __restrict__ q, uint8_t* __restrict__ s,
                                              int64_t u) {
     constexpr int P = F32 ? 23 : 7;
-    uint32_t mag[8];
-    uint32_t sgn = 0, emax = 0;
+    uint32_t codes, scale;
     if constexpr (F32) {
+        uint32_t mag[8];
+        uint32_t sgn = 0, emax = 0;
         const uint32_t w[8] = {x.a.x, x.a.y, x.a.z, x.a.w, x.b.x, x.b.y, x.b.z, x.b.w};
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -85,33 +86,19 @@ __device__ __forceinline__ void convert_unit(const Unit<F32>& x, uint32_t* __res
             mag[i] = w[i] & 0x7fffffffu;
             emax = max(emax, mag[i] >> 23);
         }
-    } else {
-        const uint32_t w[4] = {x.a.x, x.a.y, x.a.z, x.a.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) emax = max(emax, max((w[i] >> 7) & 0xffu, (w[i] >> 23) & 0xffu));
-    }
-    emax = max(emax, (uint32_t)__shfl_xor((int)emax, 1));
-    emax = max(emax, (uint32_t)__shfl_xor((int)emax, 2));
-    uint32_t codes, scale;
-    if (emax == 0xffu) {  // NaN or Inf in the block
-        scale = 0xffu;
-        codes = 0;
-    } else {
-        scale = emax > 2u ? emax - 2u : 0u;
-        if constexpr (F32) {
-            codes = encode8<P>(mag, scale) | sgn;
+        emax = max(emax, (uint32_t)__shfl_xor((int)emax, 1));
+        emax = max(emax, (uint32_t)__shfl_xor((int)emax, 2));
+        if (emax == 0xffu) {  // NaN or Inf in the block
+            scale = 0xffu;
+            codes = 0;
         } else {
-            // BF16: the hardware conversion divides by the (power-of-two) scale and rounds to the
-            // nearest E2M1 value, ties to the even code, saturating at 6 and keeping the sign: the
-            // same decision as the integer path, which it replaces for speed (the GPU tests compare
-            // every finite BF16 pattern with the oracle).
-            const float sc = __uint_as_float(scale ? scale << 23 : 1u << 22);  // 2^(scale - 127)
-            typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-            codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(0u, __builtin_bit_cast(bf2, x.a.x), sc, 0);
-            codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes, __builtin_bit_cast(bf2, x.a.y), sc, 1);
-            codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes, __builtin_bit_cast(bf2, x.a.z), sc, 2);
-            codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes, __builtin_bit_cast(bf2, x.a.w), sc, 3);
+            scale = emax > 2u ? emax - 2u : 0u;
+            codes = encode8<P>(mag, scale) | sgn;
         }
+    } else {
+        // BF16: the hardware conversion takes the same decisions as the integer path (the GPU tests
+        // compare every finite BF16 pattern with the oracle)
+        codes = mx_bf16x8_codes(x.a, scale);
     }
     q[u] = codes;
     if ((u & 3) == 0) s[u >> 2] = (uint8_t)scale;
