@@ -1380,6 +1380,280 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_fp4(const uint8_t* __restric
 }
 
 // ============================================================================
+// Tile path, FP4, K % 512 == 0: 256 x 224 output tiles from 16 x 16 x 128
+// scaled MFMAs.  N = 7168 is 32 tiles of 224, so M = 8192 gives 32 x 32 =
+// 1024 tiles, four full rounds on 256 CUs; 256 x 256 tiles give 896 = 3.5
+// rounds and leave half the CUs idle in the last one.  Staging as in
+// gemm_tile_fp4: superstages of K = 256 (128 code bytes per row, whole cache
+// lines) of the 224 weight and 256 activation rows, 8 rows per wave copy,
+// into two 60 KB slots; scales in bulk, 32 bytes per row (K = 1024), into two
+// 16 KB buffers, a quarter block travelling with each superstage (15 copies
+// of 32 rows per block and one dummy, so each wave carries one per
+// superstage).  4 waves in 2 x 2, each 128 (m) x 112 (n): 8 activation and 7
+// weight fragments of 16 rows, 56 accumulators of 4 values.
+// A superstage is two k-steps.  Lane group g (lanes 16g .. 16g+15) multiplies
+// the row's 16-byte chunks 2g (k-step 0) and 2g + 1 (k-step 1), so one 16-bit
+// read at byte 8q + 2g of the row's bulk scale segment (q = superstage within
+// the block) serves both k-steps with op_sel 0 and 1.  Chunks are XOR-swizzled
+// in LDS by (row / 2) % 8 as in gemm_tile_fp4.
+// Per superstage u: the MFMAs of k-step 0 with the reads of k-step 1
+// between them; a barrier once every wave has read all of u and its own
+// copies of u + 1 have landed; then the MFMAs of k-step 1 with the scale
+// reads and k-step-0 reads of u + 1 and the copies of u + 2 (into the slot
+// just released) between them.  Scheduling barriers fix every placement.
+// ============================================================================
+namespace tile224 {
+constexpr int kTM = 256, kTN = 224;            // activation rows (m), weight rows (n) per tile
+constexpr int kFA = 8, kFW = 7;                // 16-row fragments per wave: activation, weight
+constexpr int kRowBytes = 128;                 // code bytes per row per superstage
+constexpr int kWBytes = kTN * kRowBytes;       // weight rows first in a slot, then activation rows
+constexpr int kSlot = kWBytes + kTM * kRowBytes;
+constexpr int kWCopies = kTN / 32, kACopies = kTM / 32;  // code copies per wave and superstage
+constexpr int kCodeCopies = kWCopies + kACopies;
+constexpr int kScaleRow = 32;                  // bulk scale bytes per row (K = 1024)
+constexpr int kScaleBuf = 16 * 1024;           // 15 copies of 32 rows x 32 bytes, one dummy
+constexpr int kOutPitch = 2 * kTN + 16;        // epilogue staging pitch (bytes)
+constexpr int kRing = 2 * kSlot + 2 * kScaleBuf;
+constexpr int kLds = kRing > kTM * kOutPitch ? kRing : kTM * kOutPitch;
+constexpr int kMf = kFW * kFA;                 // MFMAs per wave and k-step
+static_assert(kLds <= 160 * 1024, "LDS");
+static_assert((kTN + kTM) / 32 == 15, "15 scale copies of 32 rows per block");
+}  // namespace tile224
+
+// VEC: N % 8 == 0 and y 16-byte aligned (whole 16-byte output stores allowed).
+template <bool VEC>
+__global__ __launch_bounds__(256, 1) void gemm_tile224_fp4(const uint8_t* __restrict__ qa,
+                                                           const uint8_t* __restrict__ sa,
+                                                           const uint8_t* __restrict__ qw,
+                                                           const uint8_t* __restrict__ sw, uint16_t* __restrict__ y,
+                                                           int M, int N, int K, int tiles_m, int tiles_n) {
+    using namespace tile224;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
+
+    int tm, tn;
+    tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * kTM, n0 = tn * kTN;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar registers
+    const int wn = wave & 1, wm = wave >> 1;
+    const int l16 = lane & 15, g = lane >> 4;
+    const int64_t KB = (int64_t)K / 2, KS = (int64_t)K / 32;
+    const int nsup = K / 256;
+
+    // code copy i: weight rows 8 (kWCopies wave + i) + lane / 8 for i < kWCopies, else activation
+    // rows 8 (kACopies wave + i - kWCopies) + lane / 8; the lane fills physical chunk lane % 8 with
+    // logical chunk (lane % 8) ^ ((row / 2) % 8).  The copies are buffer loads: a 32-bit offset per
+    // lane, the superstage in the scalar offset, and the operand's size as the descriptor's range, so
+    // rows past M or N read as zeros (their outputs are never stored).  The host keeps rows * K / 2
+    // below 2^31.
+    constexpr int kRawBufferWord3 = 0x00020000;
+    const __amdgpu_buffer_rsrc_t wrsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)qw, (short)0, (int)(N * KB), kRawBufferWord3);
+    const __amdgpu_buffer_rsrc_t arsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)qa, (short)0, (int)(M * KB), kRawBufferWord3);
+    uint32_t coff[kCodeCopies];
+    int cdst[kCodeCopies];
+#pragma unroll
+    for (int i = 0; i < kCodeCopies; ++i) {
+        const bool isw = i < kWCopies;
+        const int row = isw ? 8 * (kWCopies * wave + i) + (lane >> 3) : 8 * (kACopies * wave + i - kWCopies) + (lane >> 3);
+        const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+        coff[i] = (uint32_t)(((isw ? n0 : m0) + row) * KB + 16 * chunk);
+        cdst[i] = isw ? (kWCopies * wave + i) * 1024 : kWBytes + (kACopies * wave + i - kWCopies) * 1024;
+    }
+    auto issue_code = [&](int u, int i) {  // copy i of superstage min(u, nsup - 1) into the slot of u
+        const int koff = min(u, nsup - 1) * kRowBytes;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(i < kWCopies ? wrsrc : arsrc,
+                                                 (__attribute__((address_space(3))) void*)(lds + (u & 1) * kSlot + cdst[i]),
+                                                 16, coff[i], koff, 0, 0);
+    };
+    // scale copy q (0..15) of block b: q < 7 moves weight rows 32 q + lane / 2, 7 <= q < 15
+    // activation rows 32 (q - 7) + lane / 2, each lane 16 bytes of the row's 32-byte segment; copy q
+    // lands at 1024 q, so weight row r sits at 32 r and activation row r at 32 (kTN + r).  Copy 15
+    // is a dummy (an in-bounds activation row into the unused last KB).  Part j (0..3) of block b is
+    // copy 4j + wave and travels with the codes of superstage 4b - 3 + j: after every wave has read
+    // block b - 2 in the same buffer (last for superstage 4b - 5) and in time for superstage 4b.
+    auto issue_scale = [&](int u) {
+        const int b = (u + 3) >> 2, q = 4 * ((u + 3) & 3) + wave;
+        const bool isw = q < 7;
+        const int r = isw ? min(n0 + 32 * q + (lane >> 1), N - 1) : min(m0 + 32 * (q - 7) + (lane >> 1), M - 1);
+        int64_t off = 32 * (int64_t)b + 16 * (lane & 1);
+        off = off >= KS ? 0 : off;  // past the last block: any in-row address, never read
+        const uint8_t* src = (isw ? sw : sa) + (int64_t)r * KS + off;
+        g2lds16(src, lds + 2 * kSlot + (b & 1) * kScaleBuf + q * 1024);
+    };
+
+    // LDS addressing: fragment f of a wave's weight rows starts 16 f rows (2048 f bytes) after its
+    // first, so every read is a per-lane base plus an immediate.  The swizzle key of row r,
+    // (r / 2) % 8, is (l16 / 2) for every fragment (fragments start at multiples of 16 rows), so
+    // the chunk offset of k-step t, 16 ((2g + t) ^ key), is one value per lane and k-step.
+    const int key = l16 >> 1;
+    const uint32_t base = lds_addr(lds);
+    const uint32_t wrow0 = ((kTN / 2) * wn + l16) * kRowBytes, xrow0 = kWBytes + ((kTM / 2) * wm + l16) * kRowBytes;
+    const uint32_t ck0 = 16 * ((2 * g) ^ key), ck1 = 16 * ((2 * g + 1) ^ key);
+    const uint32_t wsrow0 = ((kTN / 2) * wn + l16) * kScaleRow + 2 * g;
+    const uint32_t xsrow0 = (kTN + (kTM / 2) * wm + l16) * kScaleRow + 2 * g;
+    // read i (0 .. kFW + kFA - 1) of k-step T of superstage u: weight fragment i, then activation
+    // fragment i - kFW
+    auto rd_one = [&](v4u (&rw)[kFW], v4u (&rx)[kFA], uint32_t wb, uint32_t xb, auto ic) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (i < kFW) rw[i] = lds_read16_at<i * 16 * kRowBytes>(wb);
+        else rx[i - kFW] = lds_read16_at<(i - kFW) * 16 * kRowBytes>(xb);
+    };
+    auto rd_scale = [&](uint32_t (&ws)[kFW], uint32_t (&xs)[kFA], uint32_t wb, uint32_t xb, auto ic) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (i < kFW) ws[i] = lds_read2_at<i * 16 * kScaleRow>(wb);
+        else xs[i - kFW] = lds_read2_at<(i - kFW) * 16 * kScaleRow>(xb);
+    };
+    auto slot_of = [&](int u) { return base + (u & 1) * kSlot; };
+    auto sc_of = [&](int u) { return base + 2 * kSlot + ((u >> 2) & 1) * kScaleBuf + 8 * (u & 3); };
+
+    v4f acc[kFW][kFA];
+#pragma unroll
+    for (int f = 0; f < kFW; ++f)
+#pragma unroll
+        for (int j = 0; j < kFA; ++j) {
+            acc[f][j] = v4f{0.f, 0.f, 0.f, 0.f};
+            asm volatile("" : "+a"(acc[f][j]));  // zeros in place in the AGPRs before the wait below
+        }
+    wait_states8<2>();  // VALU writes of the accumulators -> first MFMA
+
+    // prologue: scale block 0, the codes of superstage 0, then the batch of superstage 1
+#pragma unroll
+    for (int j = 0; j < 4; ++j) issue_scale(j - 3);
+#pragma unroll
+    for (int i = 0; i < kCodeCopies; ++i) issue_code(0, i);
+    issue_scale(1);
+#pragma unroll
+    for (int i = 0; i < kCodeCopies; ++i) issue_code(1, i);
+    wait_vmcnt<kCodeCopies + 1>();  // superstage 0 and scale block 0 are in
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+
+    constexpr int kRd = kFW + kFA;  // operand reads per k-step (and scale reads per superstage)
+    uint32_t wsc[kFW], xsc[kFA];
+    v4u r0w[kFW], r0x[kFA], r1w[kFW], r1x[kFA];
+    static_for<kRd>([&](auto ic) { rd_scale(wsc, xsc, sc_of(0) + wsrow0, sc_of(0) + xsrow0, ic); });
+    static_for<kRd>([&](auto ic) { rd_one(r0w, r0x, slot_of(0) + wrow0 + ck0, slot_of(0) + xrow0 + ck0, ic); });
+
+    for (int u = 0; u < nsup; ++u) {
+        // in flight: the scales and k-step 0 of u (LDS reads); the copies of u + 1
+        lds_wait<0>();
+        lds_tie(r0w);
+        lds_tie(r0x);
+        lds_tie(wsc);
+        lds_tie(xsc);
+        __builtin_amdgcn_sched_barrier(0);
+        // k-step 0 (weight-fragment-major), with the reads of k-step 1 between the MFMAs: activation
+        // fragment j after MFMA 2j; weight fragment f once row f of the MFMAs has read r0w[f] (two
+        // MFMAs later, so it can take those registers), f = 6 early
+        {
+            const uint32_t wb = slot_of(u) + wrow0 + ck1, xb = slot_of(u) + xrow0 + ck1;
+            static_for<kMf>([&](auto ic) {
+                constexpr int i = decltype(ic)::value, f = i / kFA, j = i % kFA;
+                mfma16_fp4_agpr<0>(acc[f][j], r0w[f], r0x[j], wsc[f], xsc[j]);
+                static_for<kRd>([&](auto rc) {
+                    constexpr int ri = decltype(rc)::value;  // < kFW: weight fragment ri, else activation ri - kFW
+                    constexpr int at = ri >= kFW ? 2 * (ri - kFW) : ri == kFW - 1 ? 3 : kFA * ri + kFA + 2;
+                    if constexpr (at == i) rd_one(r1w, r1x, wb, xb, rc);
+                });
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        }
+        lds_wait<0>();
+        lds_tie(r1w);
+        lds_tie(r1x);
+        wait_vmcnt<0>();  // this wave's copies of u + 1 (and of the scale part) have landed
+        __builtin_amdgcn_s_barrier();  // every wave: done reading u, copies of u + 1 complete
+        __builtin_amdgcn_sched_barrier(0);
+        uint32_t wsk[kFW], xsk[kFA];  // the scales of u, still needed for k-step 1
+#pragma unroll
+        for (int f = 0; f < kFW; ++f) wsk[f] = wsc[f];
+#pragma unroll
+        for (int j = 0; j < kFA; ++j) xsk[j] = xsc[j];
+        lds_tie(wsk);  // the copies (VALU) are done here ...
+        lds_tie(xsk);
+        issue_scale(u + 2);
+        wait_states8<1>();  // ... and some wait states before an MFMA reads them
+        __builtin_amdgcn_sched_barrier(0);
+        // k-step 1, with the kCodeCopies copies of u + 2 and the 2 kRd reads (scales, then k-step 0)
+        // of u + 1 spread between the MFMAs; past the end these read the repeated last superstage,
+        // never used
+        // k-step 1 (activation-fragment-major), with the copies of u + 2 and the reads of u + 1 between
+        // the MFMAs: the 15 scales first, the weight fragments (fresh registers), then activation
+        // fragment j once column j has read r1x[j] (two MFMAs later), j = 7 early
+        {
+            const uint32_t wb = slot_of(u + 1) + wrow0 + ck0, xb = slot_of(u + 1) + xrow0 + ck0;
+            const uint32_t wsb = sc_of(u + 1) + wsrow0, xsb = sc_of(u + 1) + xsrow0;
+            static_for<kMf>([&](auto ic) {
+                constexpr int i = decltype(ic)::value, j = i / kFW, f = i % kFW;
+                mfma16_fp4_agpr<1>(acc[f][j], r1w[f], r1x[j], wsk[f], xsk[j]);
+                static_for<kCodeCopies>([&](auto cc) {
+                    if constexpr ((decltype(cc)::value * kMf) / kCodeCopies == i) issue_code(u + 2, decltype(cc)::value);
+                });
+                static_for<kRd>([&](auto rc) {
+                    if constexpr (decltype(rc)::value == i) rd_scale(wsc, xsc, wsb, xsb, rc);
+                });
+                static_for<kRd>([&](auto rc) {
+                    constexpr int ri = decltype(rc)::value;
+                    constexpr int at = ri < kFW ? kRd + 2 * ri : ri == kRd - 1 ? kRd + 2 * kFW : kFW * (ri - kFW) + kFW + 2;
+                    if constexpr (at == i) rd_one(r0w, r0x, wb, xb, rc);
+                });
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        }
+    }
+    wait_vmcnt<0>();
+    lds_wait<0>();
+    lds_tie(r0w);
+    lds_tie(r0x);
+    lds_tie(wsc);
+    lds_tie(xsc);
+    wait_states8<3>();  // last MFMA -> reads of the accumulators (tied here, so none moves above)
+#pragma unroll
+    for (int f = 0; f < kFW; ++f)
+#pragma unroll
+        for (int j = 0; j < kFA; ++j) asm volatile("" : "+a"(acc[f][j]));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Epilogue through LDS: each lane holds 4 consecutive n of one m per fragment pair; the
+    // workgroup then stores whole 448-byte tile rows.
+#pragma unroll
+    for (int f = 0; f < kFW; ++f) {
+        const int nl = (kTN / 2) * wn + 16 * f + 4 * g;
+#pragma unroll
+        for (int j = 0; j < kFA; ++j) {
+            const int ml = (kTM / 2) * wm + 16 * j + l16;
+            uint2 pk;
+            pk.x = bf16x2_rne(acc[f][j][0], acc[f][j][1]);
+            pk.y = bf16x2_rne(acc[f][j][2], acc[f][j][3]);
+            *reinterpret_cast<uint2*>(lds + ml * kOutPitch + 2 * nl) = pk;
+        }
+    }
+    __syncthreads();
+    constexpr int kPieces = kTN / 8;  // 16-byte pieces per tile row
+#pragma unroll 4
+    for (int it = 0; it < kPieces; ++it) {  // wave w stores tile rows 64 w .. 64 w + 63
+        const int p = 64 * it + lane;
+        const int row = p / kPieces, col = p - kPieces * row;
+        const int ml = 64 * wave + row;
+        const int m = m0 + ml, n = n0 + 8 * col;
+        const uint4 v = *reinterpret_cast<const uint4*>(lds + ml * kOutPitch + 16 * col);
+        if (m >= M) continue;
+        uint16_t* dst = y + (int64_t)m * N + n;
+        if (VEC && n + 7 < N) {
+            *reinterpret_cast<uint4*>(dst) = v;
+        } else {
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (n + e < N) dst[e] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+        }
+    }
+}
+
+// ============================================================================
 // Tile path, FP8 (E4M3 widened exactly to FP16), any K % 128 == 0.
 // The structure of gemm_tile_fp4: 256 x 256 output tile, 4 waves (2 x 2,
 // 128 x 128 each, 4 x 4 fragments of 32 x 32 in AGPRs), superstages of 128
@@ -1655,16 +1929,30 @@ inline hipError_t launch_gemm(const void* qa, const void* sa, const void* qw, co
                                tiles_m, tiles_n);
         else if (!FP8 && K % 512 == 0 && scales16) {
             // 128-row tiles when 256-row tiles would leave many CUs idle: up to about 160 256-tiles
-            // (on 256 CUs) four times as many 128-tiles finish sooner
-            const bool small = (int64_t)tiles_m * tiles_n <= 160;
+            // (on 256 CUs) four times as many 128-tiles finish sooner.  Otherwise 256 x 224 tiles when
+            // they fill the CUs in fewer rounds (a round of them costs 7/8 of a round of 256 x 256
+            // tiles; N = 7168 is 32 tiles of 224), else 256 x 256.
+            constexpr int64_t kCUs = 256;
+            const int64_t t256 = (int64_t)tiles_m * tiles_n;
+            const bool small = t256 <= 160;
             const int tm128 = (int)((M + 127) / 128), tn128 = (int)((N + 127) / 128);
-            const dim3 g256((unsigned)(tiles_m * tiles_n)), g128((unsigned)(tm128 * tn128));
+            const int tn224 = (int)((N + tile224::kTN - 1) / tile224::kTN);
+            const int64_t t224 = (int64_t)tiles_m * tn224;
+            const bool use224 = 7 * ((t224 + kCUs - 1) / kCUs) < 8 * ((t256 + kCUs - 1) / kCUs) &&
+                                (M > N ? M : N) * (K / 2) < ((int64_t)1 << 31);
+            const dim3 g256((unsigned)t256), g128((unsigned)(tm128 * tn128)), g224((unsigned)t224);
             if (small && vec16)
                 hipLaunchKernelGGL((gemm_tile_fp4<true, 128>), g128, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k,
                                    tm128, tn128);
             else if (small)
                 hipLaunchKernelGGL((gemm_tile_fp4<false, 128>), g128, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k,
                                    tm128, tn128);
+            else if (use224 && vec16)
+                hipLaunchKernelGGL(gemm_tile224_fp4<true>, g224, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k,
+                                   tiles_m, tn224);
+            else if (use224)
+                hipLaunchKernelGGL(gemm_tile224_fp4<false>, g224, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k,
+                                   tiles_m, tn224);
             else if (vec16)
                 hipLaunchKernelGGL((gemm_tile_fp4<true, 256>), g256, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k,
                                    tiles_m, tiles_n);

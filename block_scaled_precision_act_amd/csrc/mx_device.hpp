@@ -4,7 +4,21 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace mx {
+
+// Calls f(std::integral_constant<int, i>{}) for i = 0 .. N-1, unrolled at compile time, so
+// indices can select registers, immediates and template arguments.
+template <int N, typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
+}
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -115,6 +129,63 @@ __device__ __forceinline__ uint32_t lds_read4(uint32_t addr) {
     uint32_t v;
     asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr));
     return v;
+}
+// ds_read_b128 at addr + OFF (OFF an immediate, < 65536).
+template <int OFF>
+__device__ __forceinline__ v4u lds_read16_at(uint32_t addr) {
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset range");
+    v4u v;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF));
+    return v;
+}
+// 16-bit LDS read at addr + OFF, zero-extended (2-byte aligned).
+template <int OFF>
+__device__ __forceinline__ uint32_t lds_read2_at(uint32_t addr) {
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset range");
+    uint32_t v;
+    asm volatile("ds_read_u16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF));
+    return v;
+}
+// D += A(16x128) . B(128x16), E2M1 operands with per-lane E8M0 scales (byte OPSEL of sa and sb),
+// written as inline asm with the accumulator tied to AGPRs: the register allocator then keeps
+// every accumulator in place (with 56 accumulators of 4 registers, the builtin's results were
+// shuffled between register files on every loop iteration).  The compiler does not know this is
+// an MFMA, so the caller owns its hazards: wait states between a VALU write of an operand or of
+// the accumulator and the MFMA, and between the last MFMA and a read of the accumulator.
+template <int OPSEL>
+__device__ __forceinline__ void mfma16_fp4_agpr(v4f& c, v4u a, v4u b, uint32_t sa, uint32_t sb) {
+    static_assert(OPSEL == 0 || OPSEL == 1, "scale byte 0 or 1");
+    if constexpr (OPSEL == 0)
+        asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0] cbsz:4 blgp:4"
+                     : "+a"(c)
+                     : "v"(a), "v"(b), "v"(sa), "v"(sb));
+    else
+        asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[1,1,0] op_sel_hi:[0,0,0] cbsz:4 blgp:4"
+                     : "+a"(c)
+                     : "v"(a), "v"(b), "v"(sa), "v"(sb));
+}
+// s_nop 7, N times (8 N wait states).
+template <int N>
+__device__ __forceinline__ void wait_states8() {
+#pragma unroll
+    for (int i = 0; i < N; ++i) asm volatile("s_nop 7");
+}
+// s_waitcnt lgkmcnt(N) (N < 16); the caller ties the results it waited for with lds_tie.
+template <int N>
+__device__ __forceinline__ void lds_wait() {
+    static_assert(N >= 0 && N < 16, "lgkmcnt range");
+    asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N));
+}
+// After an lds_wait: marks LDS-read results as produced here, so no use of them moves above the wait.
+template <int L>
+__device__ __forceinline__ void lds_tie(v4u (&a)[L]) {
+#pragma unroll
+    for (int i = 0; i < L; ++i) asm volatile("" : "+v"(a[i]));
+}
+template <int L>
+__device__ __forceinline__ void lds_tie(uint32_t (&a)[L]) {
+#pragma unroll
+    for (int i = 0; i < L; ++i) asm volatile("" : "+v"(a[i]));
 }
 // 4-byte global -> LDS (lane i writes lds_base + 4 * i).
 __device__ __forceinline__ void g2lds4(const void* g, void* lds_base) {

@@ -57,13 +57,15 @@ def _random_mx(orc, seed, M, N, K, w_std=0.02):
 
 # Decode paths: M <= 64 with K % 2048 == 0 (scale rows up to 256 or up to 512 bytes) and not; M <= 128.
 # Tile paths (M > 128): K % 512, % 256 or neither; 128-row tiles when there would be at most 160 tiles of
-# 256 rows, else 256-row tiles.  Ragged M and N, several tiles.
+# 256 rows, else 256 x 224 tiles when they take fewer rounds (1300 x 7000, 2600 x 4001, the prefill and
+# M = 2048 configurations), else 256 x 256.  Ragged M and N, several tiles.
 # A8W8 runs the same shapes: decode ring for M <= 64 with K % 512 == 0, tile kernel for K % 512 == 0.
 SHAPES = [(1, 256, 128), (3, 100, 384), (16, 7168, 1024), (17, 33, 256), (37, 1000, 1024), (64, 512, 512),
           (100, 300, 2048), (128, 1024, 8192), (129, 300, 384), (300, 700, 1024), (512, 512, 512),
           (600, 1100, 2176), (257, 257, 128), (259, 1030, 256), (1000, 800, 4096), (777, 520, 768),
           (1, 256, 2048), (33, 520, 4096), (64, 100, 2048), (7, 300, 16384), (48, 77, 6144),
-          (2200, 3896, 512), (2200, 3900, 1024), (40, 129, 16384), (64, 96, 10240)]
+          (2200, 3896, 512), (2200, 3900, 1024), (40, 129, 16384), (64, 96, 10240),
+          (1300, 7000, 512), (2600, 4001, 512)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
