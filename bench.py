@@ -375,7 +375,7 @@ def profile_pass(ctx):
 # Kernels whose HBM traffic the bench reports: key -> (name fragment, grid size in threads or None)
 PMC_KERNELS = {
     "gemm_decode_fp4_m64": ("gemm_decode_fp4<2, 2, 256>", None),
-    "gemm_tile_fp4_m8192": ("gemm_tile_fp4<true, 256>", 896 * 256),
+    "gemm_tile224_fp4_m8192": ("gemm_tile224_fp4<true>", 1024 * 256),
 }
 COPY_BYTES = 256 << 20  # the profile pass copies 256 MiB device -> device
 
@@ -484,7 +484,8 @@ def main():
         log("prefill A4W4 (M = 8192)")
         pre = make_a4w4(ctx, "oproj_prefill_a4w4", rotate=2)
         also["a4w4_prefill_m8192"] = layer_entry(ctx, pre, "a4w4", args, "oproj_prefill_a4w4")
-        also["a4w4_prefill_m8192"]["gemm"]["traffic"] = pmc_traffic("gemm_tile_fp4_m8192")
+        also["a4w4_prefill_m8192"]["gemm"]["traffic"] = pmc_traffic("gemm_tile224_fp4_m8192")
+        also["a4w4_prefill_m8192"]["gemm"]["kernel"] = "gemm_tile224_fp4<true>"
         del pre
         ctx.weights.clear()
         torch.cuda.empty_cache()
