@@ -1106,15 +1106,17 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_dma_fp4(const uint8_t* __res
 // request for part of a 128-byte line costs as much as the whole line, so
 // every global -> LDS copy here moves whole lines: a superstage is K = 256
 // (128 code bytes per row) of both TM-row operands, 8 rows per wave
-// instruction, into one of two slots.  Scales are fetched in bulk, 32 bytes
-// per row (K = 1024, four superstages), into one of two buffers, a quarter of
-// a block with every superstage's copies.
+// instruction, into a ring of S slots (S = 2 for 256-row tiles; S = 4 for
+// 128-row tiles, whose small superstages would otherwise wait on copy
+// latency).  Scales are fetched in bulk, 32 bytes per row (K = 1024, four
+// superstages), into a ring of NB buffers, a quarter of a block with every
+// superstage's copies.
 // Output tile TM x TM (256, or 128 for shapes with too few 256-tiles to fill
 // the CUs), 4 waves (2 x 2, each TM/2 x TM/2 from 32 x 32 x 64 MFMAs), four
 // k-steps per superstage.  One barrier per superstage, placed once every wave
 // has read all of superstage u (and its own copies of u + 1 have landed):
 // after it, each wave reads the scales and the first two k-steps of u + 1 and
-// issues the copies of u + 2 into the slot just released, both spread between
+// issues the copies of u + S into the slot just released, both spread between
 // the MFMAs of k-steps 2 and 3 of u; the operands of k-steps 2 and 3 are read
 // between the MFMAs of k-steps 0 and 1.  Every such placement is fixed with
 // scheduling barriers, so LDS reads and copies go out while the matrix core
@@ -1126,7 +1128,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_dma_fp4(const uint8_t* __res
 // which spreads the 16 lanes of every ds_read_b128 phase over all banks.
 // ============================================================================
 namespace tile_fp4 {
-template <int TM>
+template <int TM, int S>
 struct Cfg {
     static constexpr int kRows = TM;                          // rows of each operand
     static constexpr int kFW = TM / 64;                       // 32 x 32 fragments per wave and dimension
@@ -1143,20 +1145,31 @@ struct Cfg {
     static constexpr int kScaleCopies = kScaleBuf / (64 * kScLane);  // copies per block
     static constexpr int kScPerWave = kScaleCopies / 16;             // per wave and superstage
     static constexpr int kOutPitch = 2 * TM + 16;             // epilogue staging pitch (bytes), odd in 16 bytes
-    static constexpr int kRing = 2 * kSlot + 2 * kScaleBuf;
+    // Code slots and scale buffers of the ring.  The codes of superstage v are copied S superstages
+    // ahead, after the barrier of superstage v - S; part j of scale block b travels with the codes of
+    // superstage 4b - 3 + j.  Block b lands in buffer b mod NB, which block b - NB (read last for
+    // superstage 4b - 4 NB + 3) frees in time when S <= 4 NB - 6.  S = 4 (152 KB of LDS at 128-row
+    // tiles) hides L2 / HBM latency when there is one workgroup per CU; S = 2 (80 KB) lets two
+    // workgroups share a CU instead.
+    static constexpr int kS = S;
+    static constexpr int kNB = S == 2 ? 2 : 3;
+    static_assert(kS <= 4 * kNB - 6, "scale ring too shallow for the code ring");
+    static constexpr int kRing = kS * kSlot + kNB * kScaleBuf;
     static constexpr int kLds = kRing > TM * kOutPitch ? kRing : TM * kOutPitch;
     static_assert(kScPerWave >= 1 && kScaleCopies == 16 * kScPerWave && kFW >= 1, "tile shape");
+    static_assert((kS - 1) * (kCodeCopies + kScPerWave) < 64, "vmcnt range");
     static_assert(kLds <= 160 * 1024, "LDS");
 };
 }  // namespace tile_fp4
 
-// VEC: N % 8 == 0 and y 16-byte aligned (whole 16-byte output stores allowed).
-template <bool VEC, int TM>
+// VEC: N % 8 == 0 and y 16-byte aligned (whole 16-byte output stores allowed).  S: code slots of
+// the ring (2, or 4 for 128-row tiles when there is at most one tile per CU).
+template <bool VEC, int TM, int S = 2>
 __global__ __launch_bounds__(256, 1) void gemm_tile_fp4(const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa,
                                                         const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw,
                                                         uint16_t* __restrict__ y, int M, int N, int K, int tiles_m,
                                                         int tiles_n) {
-    using C = tile_fp4::Cfg<TM>;
+    using C = tile_fp4::Cfg<TM, S>;
     constexpr int FW = C::kFW;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[C::kLds];
 
@@ -1182,7 +1195,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_fp4(const uint8_t* __restric
         xrow[i] = qa + (int64_t)min(m0 + row, M - 1) * KB + 16 * chunk;
     }
     auto issue_code = [&](int u, int i) {  // copy i of superstage min(u, nsup - 1) into the slot of u
-        uint8_t* slot = lds + (u & 1) * C::kSlot;
+        uint8_t* slot = lds + (u % C::kS) * C::kSlot;
         const int64_t koff = (int64_t)min(u, nsup - 1) * C::kRowBytes;
         if (i < C::kHalfCopies) g2lds16(wrow[i] + koff, slot + (C::kHalfCopies * wave + i) * 1024);
         else g2lds16(xrow[i - C::kHalfCopies] + koff, slot + C::kOpBytes + (C::kHalfCopies * wave + i - C::kHalfCopies) * 1024);
@@ -1201,7 +1214,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_fp4(const uint8_t* __restric
         if (off >= KS) off = 0;  // past the last block: any in-row address, never read
         const uint8_t* src = q < half ? sw + (int64_t)min(n0 + row, N - 1) * KS + off
                                       : sa + (int64_t)min(m0 + row, M - 1) * KS + off;
-        uint8_t* dst = lds + 2 * C::kSlot + (b & 1) * C::kScaleBuf + q * 64 * C::kScLane;
+        uint8_t* dst = lds + C::kS * C::kSlot + (b % C::kNB) * C::kScaleBuf + q * 64 * C::kScLane;
         if constexpr (C::kScLane == 16) g2lds16(src, dst);
         else g2lds4(src, dst);
     };
@@ -1223,7 +1236,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_fp4(const uint8_t* __restric
     }
     const uint32_t base = lds_addr(lds);
     auto rd_step = [&](v4u (&rw)[FW], v4u (&rx)[FW], int u, int t) {
-        const uint32_t sb = base + (u & 1) * C::kSlot;
+        const uint32_t sb = base + (u % C::kS) * C::kSlot;
 #pragma unroll
         for (int f = 0; f < FW; ++f) {
             rw[f] = lds_read16(sb + (woff[f] & ~7) + 16 * ((4 * h + t) ^ (woff[f] & 7)));
@@ -1233,13 +1246,13 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_fp4(const uint8_t* __restric
     // one operand of k-step t of superstage u: read i (0 .. 2 FW - 1) is fragment i / 2 of W (even i)
     // or of A (odd i), the order rd_step uses
     auto rd_one = [&](v4u (&rw)[FW], v4u (&rx)[FW], int u, int t, int i) {
-        const uint32_t sb = base + (u & 1) * C::kSlot;
+        const uint32_t sb = base + (u % C::kS) * C::kSlot;
         const int f = i >> 1;
         if (i & 1) rx[f] = lds_read16(sb + (xoff[f] & ~7) + 16 * ((4 * h + t) ^ (xoff[f] & 7)));
         else rw[f] = lds_read16(sb + (woff[f] & ~7) + 16 * ((4 * h + t) ^ (woff[f] & 7)));
     };
     auto rd_scales = [&](uint32_t (&ws)[FW], uint32_t (&xs)[FW], int u) {
-        const uint32_t scb = base + 2 * C::kSlot + ((u >> 2) & 1) * C::kScaleBuf + 8 * (u & 3);
+        const uint32_t scb = base + C::kS * C::kSlot + ((u >> 2) % C::kNB) * C::kScaleBuf + 8 * (u & 3);
 #pragma unroll
         for (int f = 0; f < FW; ++f) {
             ws[f] = lds_read4(scb + wsoff[f]);
@@ -1262,10 +1275,13 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_fp4(const uint8_t* __restric
         for (int c = 0; c < C::kScPerWave; ++c) issue_scale_copy(4 * C::kScPerWave * j + C::kScPerWave * wave + c, 0);
 #pragma unroll
     for (int i = 0; i < C::kCodeCopies; ++i) issue_code(0, i);
-    issue_scale(1);
 #pragma unroll
-    for (int i = 0; i < C::kCodeCopies; ++i) issue_code(1, i);
-    wait_vmcnt<C::kCodeCopies + C::kScPerWave>();  // superstage 0 and scale block 0 are in
+    for (int v = 1; v < C::kS; ++v) {
+        issue_scale(v);
+#pragma unroll
+        for (int i = 0; i < C::kCodeCopies; ++i) issue_code(v, i);
+    }
+    wait_vmcnt<(C::kS - 1) * (C::kCodeCopies + C::kScPerWave)>();  // superstage 0 and scale block 0 are in
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
 
@@ -1294,7 +1310,9 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_fp4(const uint8_t* __restric
         MX_STEP_RD(r1w, r1x, 1, r3w, r3x, 3)
         lds_wait_n_of<0, FW>(r2w, r2x);
         lds_wait_n_of<0, FW>(r3w, r3x);
-        wait_vmcnt<0>();  // this wave's copies of u + 1 (and of the scale part) have landed
+        // this wave's copies of u + 1 (and of the scale part) have landed; those of u + 2 .. u + S - 1
+        // may still be in flight
+        wait_vmcnt<(C::kS - 2) * (C::kCodeCopies + C::kScPerWave)>();
         __builtin_amdgcn_s_barrier();  // every wave: done reading u, copies of u + 1 complete
         __builtin_amdgcn_sched_barrier(0);
         uint32_t wsk[FW], xsk[FW];  // the scales of u, still needed for k-steps 2 and 3
@@ -1304,8 +1322,8 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_fp4(const uint8_t* __restric
             xsk[f] = xsc[f];
         }
         rd_scales(wsc, xsc, u + 1);  // past the end these read the repeated last superstage: unused
-        issue_scale(u + 2);
-        // k-steps 2 and 3 of u (2 FW^2 MFMAs), in this order, with the kCodeCopies copies of u + 2 and
+        issue_scale(u + C::kS);
+        // k-steps 2 and 3 of u (2 FW^2 MFMAs), in this order, with the kCodeCopies copies of u + S and
         // the 4 FW operand reads of k-steps 0 and 1 of u + 1 spread between them (a wave keeps at most
         // 15 LDS reads in flight, so a burst of them would stall it)
         constexpr int kMf = 2 * FW * FW;
@@ -1324,7 +1342,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_fp4(const uint8_t* __restric
                     else
                         acc[f][g] = mfma32<kFmtFP4, 3>(fp4_operand(r3w[f]), fp4_operand(r3x[g]), acc[f][g], (int)wsk[f],
                                                        (int)xsk[g]);
-                    if ((i % kEvery) == kEvery - 1 && i / kEvery < C::kCodeCopies) issue_code(u + 2, i / kEvery);
+                    if ((i % kEvery) == kEvery - 1 && i / kEvery < C::kCodeCopies) issue_code(u + C::kS, i / kEvery);
                     if ((i % kRdEvery) == kRdEvery - 1) {
                         const int ri = i / kRdEvery;
                         if (ri < 2 * FW) rd_one(r0w, r0x, u + 1, 0, ri);
@@ -1941,7 +1959,15 @@ inline hipError_t launch_gemm(const void* qa, const void* sa, const void* qw, co
             const bool use224 = 7 * ((t224 + kCUs - 1) / kCUs) < 8 * ((t256 + kCUs - 1) / kCUs) &&
                                 (M > N ? M : N) * (K / 2) < ((int64_t)1 << 31);
             const dim3 g256((unsigned)t256), g128((unsigned)(tm128 * tn128)), g224((unsigned)t224);
-            if (small && vec16)
+            // at most one 128-tile per CU: the deeper ring (152 KB of LDS); more: two workgroups per CU
+            const bool deep = (int64_t)tm128 * tn128 <= kCUs;
+            if (small && deep && vec16)
+                hipLaunchKernelGGL((gemm_tile_fp4<true, 128, 4>), g128, dim3(256), 0, st, a, sa8, w, sw8, out, m, n,
+                                   k, tm128, tn128);
+            else if (small && deep)
+                hipLaunchKernelGGL((gemm_tile_fp4<false, 128, 4>), g128, dim3(256), 0, st, a, sa8, w, sw8, out, m, n,
+                                   k, tm128, tn128);
+            else if (small && vec16)
                 hipLaunchKernelGGL((gemm_tile_fp4<true, 128>), g128, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k,
                                    tm128, tn128);
             else if (small)
