@@ -104,24 +104,18 @@ __device__ __forceinline__ void convert_unit(const Unit<F32>& x, uint32_t* __res
     if ((u & 3) == 0) s[u >> 2] = (uint8_t)scale;
 }
 
-// Each thread takes units u, u + stride, ...: kUnroll of them are loaded before any is
-// converted, so a wave keeps kUnroll kilobytes (BF16) of loads in flight.
-constexpr int kUnroll = 4;
-constexpr int64_t kMaxBlocks = 2048;
+// One 16-byte unit (8 values) per thread, on a grid as large as the input (capped, then
+// grid-stride): the dispatcher keeps every CU streaming as workgroups retire, which measured faster
+// (M = 8192, K = 8192: 33.7 -> 30.6 us) than 2048 workgroups each keeping four loads per thread in
+// flight.
+constexpr int64_t kMaxBlocks = 1 << 20;
 
 template <bool F32>
 __global__ __launch_bounds__(256) void quant_mx_kernel(const void* __restrict__ xin, uint32_t* __restrict__ q,
                                                         uint8_t* __restrict__ s, int64_t units) {
     const int64_t stride = (int64_t)gridDim.x * 256;
-    int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    for (; u + (kUnroll - 1) * stride < units; u += kUnroll * stride) {
-        Unit<F32> x[kUnroll];
-#pragma unroll
-        for (int k = 0; k < kUnroll; ++k) x[k] = load_unit<F32>(xin, u + k * stride);
-#pragma unroll
-        for (int k = 0; k < kUnroll; ++k) convert_unit<F32>(x[k], q, s, u + k * stride);
-    }
-    for (; u < units; u += stride) convert_unit<F32>(load_unit<F32>(xin, u), q, s, u);
+    for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < units; u += stride)
+        convert_unit<F32>(load_unit<F32>(xin, u), q, s, u);
 }
 
 template <bool F32>
