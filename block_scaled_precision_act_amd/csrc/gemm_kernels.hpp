@@ -1879,6 +1879,274 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_fp8(const uint8_t* __restric
     }
 }
 
+// ============================================================================
+// Tile path, FP8 (E4M3 widened exactly to FP16), K % 128 == 0: 256 x 224
+// output tiles from 16 x 16 x 32 FP16 MFMAs, four full rounds at N = 7168
+// and M = 8192 (as gemm_tile224_fp4).  Same staging: a superstage is K = 128
+// (128 code bytes per row) of the 224 weight and 256 activation rows, copied
+// with whole-line buffer loads into two 60 KB slots; rows past M or N read as
+// zeros.  4 waves in 2 x 2, each 128 (m) x 112 (n), 56 accumulators of 4.
+// A superstage is two read steps of four MFMA k-steps: lane group g reads the
+// row's chunks 2g (read step 0) and 2g + 1 (read step 1); bytes 0..7 of a
+// chunk widen to the 8 FP16 operand values of one k-step, bytes 8..15 to the
+// next.  Every E4M3 value is an FP16 normal, and the FP16 MFMA is exact up to
+// the FP32 accumulation (the FP8 MFMA drops small products next to large
+// ones within groups of 8).  The MFMAs run weight-fragment-major: the 8
+// activation operands of a k-step are widened during the k-step before, the
+// weight operand of row f + 1 during row f, each tied a row or more before
+// its MFMA (the MFMA is inline asm, so these distances are the VALU -> MFMA
+// wait states).  Per superstage u: read step 0 with the LDS reads of read
+// step 1 between its MFMAs; a barrier once every wave has read all of u and
+// its own copies of u + 1 have landed; read step 1 with the copies of u + 2
+// and the reads of read step 0 of u + 1 between its MFMAs.  The per-row FP32
+// scales are applied in the epilogue, (acc * sA) * sW, before rounding.
+// ============================================================================
+namespace tile224_fp8 {
+constexpr int kTM = 256, kTN = 224;            // activation rows (m), weight rows (n) per tile
+constexpr int kFA = 8, kFW = 7;                // 16-row fragments per wave: activation, weight
+constexpr int kRowBytes = 128;                 // code bytes (K values) per row per superstage
+constexpr int kWBytes = kTN * kRowBytes;       // weight rows first in a slot, then activation rows
+constexpr int kSlot = kWBytes + kTM * kRowBytes;
+constexpr int kWCopies = kTN / 32, kACopies = kTM / 32;  // code copies per wave and superstage
+constexpr int kCodeCopies = kWCopies + kACopies;
+constexpr int kOutPitch = 2 * kTN + 16;        // epilogue staging pitch (bytes)
+constexpr int kLds = 2 * kSlot > kTM * kOutPitch ? 2 * kSlot : kTM * kOutPitch;
+constexpr int kMf = kFW * kFA;                 // MFMAs per wave and k-step
+constexpr int kRd = kFW + kFA;                 // LDS reads per wave and read step
+static_assert(kLds <= 160 * 1024, "LDS");
+}  // namespace tile224_fp8
+
+// VEC: N % 8 == 0 and y 16-byte aligned (whole 16-byte output stores allowed).
+template <bool VEC>
+__global__ __launch_bounds__(256, 1) void gemm_tile224_fp8(const uint8_t* __restrict__ qa,
+                                                           const float* __restrict__ sa,
+                                                           const uint8_t* __restrict__ qw,
+                                                           const float* __restrict__ sw, uint16_t* __restrict__ y,
+                                                           int M, int N, int K, int tiles_m, int tiles_n) {
+    using namespace tile224_fp8;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
+
+    int tm, tn;
+    tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * kTM, n0 = tn * kTN;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar registers
+    const int wn = wave & 1, wm = wave >> 1;
+    const int l16 = lane & 15, g = lane >> 4;
+    const int KB = K;  // code bytes per row
+    const int nsup = K / 128;
+
+    // code copies as in gemm_tile224_fp4: buffer loads with the operand's size as the range (the
+    // host keeps rows * K below 2^31), rows 8 (copies per wave * wave + i) + lane / 8, physical chunk
+    // lane % 8 holding logical chunk (lane % 8) ^ ((row / 2) % 8)
+    constexpr int kRawBufferWord3 = 0x00020000;
+    const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)qw, (short)0, N * KB, kRawBufferWord3);
+    const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc((void*)qa, (short)0, M * KB, kRawBufferWord3);
+    uint32_t coff[kCodeCopies];
+    int cdst[kCodeCopies];
+#pragma unroll
+    for (int i = 0; i < kCodeCopies; ++i) {
+        const bool isw = i < kWCopies;
+        const int row = isw ? 8 * (kWCopies * wave + i) + (lane >> 3) : 8 * (kACopies * wave + i - kWCopies) + (lane >> 3);
+        const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+        coff[i] = (uint32_t)(((isw ? n0 : m0) + row) * KB + 16 * chunk);
+        cdst[i] = isw ? (kWCopies * wave + i) * 1024 : kWBytes + (kACopies * wave + i - kWCopies) * 1024;
+    }
+    auto issue_code = [&](int u, int i) {  // copy i of superstage min(u, nsup - 1) into the slot of u
+        const int koff = min(u, nsup - 1) * kRowBytes;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(i < kWCopies ? wrsrc : arsrc,
+                                                 (__attribute__((address_space(3))) void*)(lds + (u & 1) * kSlot + cdst[i]),
+                                                 16, coff[i], koff, 0, 0);
+    };
+
+    // LDS addressing: per-lane bases plus immediates (the swizzle key is l16 / 2 for every fragment)
+    const int key = l16 >> 1;
+    const uint32_t base = lds_addr(lds);
+    const uint32_t wrow0 = ((kTN / 2) * wn + l16) * kRowBytes, xrow0 = kWBytes + ((kTM / 2) * wm + l16) * kRowBytes;
+    const uint32_t ck0 = 16 * ((2 * g) ^ key), ck1 = 16 * ((2 * g + 1) ^ key);
+    auto slot_of = [&](int u) { return base + (u & 1) * kSlot; };
+    // read i (0 .. kRd - 1) of a read step: weight fragment i, then activation fragment i - kFW
+    auto rd_one = [&](v4u (&rw)[kFW], v4u (&rx)[kFA], uint32_t wb, uint32_t xb, auto ic) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (i < kFW) rw[i] = lds_read16_at<i * 16 * kRowBytes>(wb);
+        else rx[i - kFW] = lds_read16_at<(i - kFW) * 16 * kRowBytes>(xb);
+    };
+    // half HF of a raw 16-byte chunk widened to one 8 x FP16 operand
+    auto widen = [](const v4u& r, auto hc) -> v8h {
+        constexpr int hf = decltype(hc)::value;
+        return hf == 0 ? e4m3x8_to_f16x8(r[0], r[1]) : e4m3x8_to_f16x8(r[2], r[3]);
+    };
+
+    v4f acc[kFW][kFA];
+#pragma unroll
+    for (int f = 0; f < kFW; ++f)
+#pragma unroll
+        for (int j = 0; j < kFA; ++j) {
+            acc[f][j] = v4f{0.f, 0.f, 0.f, 0.f};
+            asm volatile("" : "+a"(acc[f][j]));
+        }
+    wait_states8<2>();  // VALU writes of the accumulators -> first MFMA
+
+    // prologue: superstages 0 and 1
+#pragma unroll
+    for (int i = 0; i < kCodeCopies; ++i) issue_code(0, i);
+#pragma unroll
+    for (int i = 0; i < kCodeCopies; ++i) issue_code(1, i);
+    wait_vmcnt<kCodeCopies>();  // superstage 0 is in
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+
+    v4u r0w[kFW], r0x[kFA], r1w[kFW], r1x[kFA];  // raw chunks of read steps 0 and 1
+    v8h xa[kFA], xb_[kFA], wa[2];                 // widened activation operands (this / next k-step), weight
+    static_for<kRd>([&](auto ic) { rd_one(r0w, r0x, slot_of(0) + wrow0 + ck0, slot_of(0) + xrow0 + ck0, ic); });
+    lds_wait<0>();
+    lds_tie(r0w);
+    lds_tie(r0x);
+    static_for<kFA>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        xa[j] = widen(r0x[j], std::integral_constant<int, 0>{});
+        vgpr_tie(xa[j]);
+    });
+    wa[0] = widen(r0w[0], std::integral_constant<int, 0>{});
+    vgpr_tie(wa[0]);
+    wait_states8<1>();
+    __builtin_amdgcn_sched_barrier(0);
+
+    // One MFMA k-step (half HF of the raw sets RW / RX), weight-fragment-major.  Row f uses the
+    // weight operand wa[(f + P) % 2] and every activation operand XC.  Between the MFMAs it widens the
+    // weight operand of row f + 1 (after MFMA 1 of row f; for the last row, row 0 of the next k-step
+    // from NW, half NHF, into wa[P ^ 1], the register that k-step's row 0 uses with parity P ^ 1) and
+    // activation operand f of the next k-step into XN (after MFMA 4 of row f; operand 7 after MFMA 6
+    // of row 6), from NX half NHF.  Each widened operand is tied at least 7 MFMAs before its first
+    // use.  EXTRA(i) adds the k-step's other work after MFMA i.
+    auto kstep = [&](const v8h (&XC)[kFA], v8h (&XN)[kFA], const v4u (&RW)[kFW], const v4u (&NW)[kFW],
+                     const v4u (&NX)[kFA], auto hc, auto nhc, auto pc, auto&& extra) {
+        constexpr int nhf = decltype(nhc)::value, P = decltype(pc)::value;
+        static_for<kMf>([&](auto ic) {
+            constexpr int i = decltype(ic)::value, f = i / kFA, j = i % kFA;
+            mfma16_f16_agpr(acc[f][j], wa[(f + P) & 1], XC[j]);
+            if constexpr (j == 1) {
+                constexpr int r = (f + 1 + P) & 1;
+                if constexpr (f + 1 < kFW) wa[r] = widen(RW[f + 1], hc);
+                else wa[r] = widen(NW[0], nhc);
+                vgpr_tie(wa[r]);
+            }
+            if constexpr (j == 4 || (f == kFW - 1 && j == 6)) {
+                constexpr int x = j == 4 ? f : kFA - 1;
+                XN[x] = widen(NX[x], std::integral_constant<int, nhf>{});
+                vgpr_tie(XN[x]);
+            }
+            extra(ic);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+    static_assert(kFW % 2 == 1 && kFA == kFW + 1, "the operand schedule assumes 7 x 8 fragments");
+    auto none = [](auto) {};
+
+    for (int u = 0; u < nsup; ++u) {
+        // read step 0 (chunk 2g): k-step (0, 0) from xa, widening (0, 1) into xb_; k-step (0, 1) from
+        // xb_, widening (1, 0) into xa once the reads of read step 1 are in.  The reads of read step 1
+        // go out during k-step (0, 0).
+        {
+            const uint32_t wb = slot_of(u) + wrow0 + ck1, xb = slot_of(u) + xrow0 + ck1;
+            kstep(xa, xb_, r0w, r0w, r0x, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{},
+                  std::integral_constant<int, 0>{},
+                  [&](auto ic) {
+                      constexpr int i = decltype(ic)::value;
+                      static_for<kRd>([&](auto rc) {
+                          if constexpr ((decltype(rc)::value * kMf) / kRd == i) rd_one(r1w, r1x, wb, xb, rc);
+                      });
+                  });
+        }
+        lds_wait<0>();
+        lds_tie(r1w);
+        lds_tie(r1x);
+        __builtin_amdgcn_sched_barrier(0);
+        // widening for k-step (1, 0) reads xa's registers; the MFMAs of (0, 1) read xb_ (not xa)
+        kstep(xb_, xa, r0w, r1w, r1x, std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{},
+              std::integral_constant<int, 1>{}, none);
+        wait_vmcnt<0>();  // this wave's copies of u + 1 have landed
+        __builtin_amdgcn_s_barrier();  // every wave: done reading u, copies of u + 1 complete
+        __builtin_amdgcn_sched_barrier(0);
+        // read step 1 (chunk 2g + 1): k-step (1, 0) from xa, widening (1, 1) into xb_, with the copies
+        // of u + 2 and the reads of read step 0 of u + 1; k-step (1, 1) from xb_, widening (0, 0) of
+        // u + 1 into xa (past the end these read the repeated last superstage, never used)
+        {
+            const uint32_t wb = slot_of(u + 1) + wrow0 + ck0, xb = slot_of(u + 1) + xrow0 + ck0;
+            kstep(xa, xb_, r1w, r1w, r1x, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{},
+                  std::integral_constant<int, 0>{},
+                  [&](auto ic) {
+                      constexpr int i = decltype(ic)::value;
+                      static_for<kCodeCopies>([&](auto cc) {
+                          if constexpr ((decltype(cc)::value * kMf) / kCodeCopies == i)
+                              issue_code(u + 2, decltype(cc)::value);
+                      });
+                      static_for<kRd>([&](auto rc) {
+                          if constexpr ((decltype(rc)::value * kMf) / kRd == i) rd_one(r0w, r0x, wb, xb, rc);
+                      });
+                  });
+        }
+        lds_wait<0>();
+        lds_tie(r0w);
+        lds_tie(r0x);
+        __builtin_amdgcn_sched_barrier(0);
+        kstep(xb_, xa, r1w, r0w, r0x, std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{},
+              std::integral_constant<int, 1>{}, none);
+    }
+    wait_vmcnt<0>();
+    wait_states8<3>();  // last MFMA -> reads of the accumulators (tied here, so none moves above)
+#pragma unroll
+    for (int f = 0; f < kFW; ++f)
+#pragma unroll
+        for (int j = 0; j < kFA; ++j) asm volatile("" : "+a"(acc[f][j]));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Epilogue through LDS: (acc * sA[m]) * sW[n] rounded to BF16, each lane 4 consecutive n of one
+    // m per fragment pair; then whole 448-byte tile rows.
+    float sxm[kFA];
+#pragma unroll
+    for (int j = 0; j < kFA; ++j) sxm[j] = sa[min(m0 + (kTM / 2) * wm + 16 * j + l16, M - 1)];
+#pragma unroll
+    for (int f = 0; f < kFW; ++f) {
+        const int nl = (kTN / 2) * wn + 16 * f + 4 * g;
+        float swn[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) swn[e] = sw[min(n0 + nl + e, N - 1)];
+#pragma unroll
+        for (int j = 0; j < kFA; ++j) {
+            const int ml = (kTM / 2) * wm + 16 * j + l16;
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = acc[f][j][e] * sxm[j] * swn[e];
+            uint2 pk;
+            pk.x = bf16x2_rne(v[0], v[1]);
+            pk.y = bf16x2_rne(v[2], v[3]);
+            *reinterpret_cast<uint2*>(lds + ml * kOutPitch + 2 * nl) = pk;
+        }
+    }
+    __syncthreads();
+    constexpr int kPieces = kTN / 8;  // 16-byte pieces per tile row
+#pragma unroll 4
+    for (int it = 0; it < kPieces; ++it) {  // wave w stores tile rows 64 w .. 64 w + 63
+        const int p = 64 * it + lane;
+        const int row = p / kPieces, col = p - kPieces * row;
+        const int ml = 64 * wave + row;
+        const int m = m0 + ml, n = n0 + 8 * col;
+        const uint4 v = *reinterpret_cast<const uint4*>(lds + ml * kOutPitch + 16 * col);
+        if (m >= M) continue;
+        uint16_t* dst = y + (int64_t)m * N + n;
+        if (VEC && n + 7 < N) {
+            *reinterpret_cast<uint4*>(dst) = v;
+        } else {
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (n + e < N) dst[e] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+        }
+    }
+}
+
 // ----------------------------------------------------------------------------
 // Host-side dispatch shared by the FP4 and FP8 entry points.
 // ----------------------------------------------------------------------------
@@ -1937,7 +2205,20 @@ inline hipError_t launch_gemm(const void* qa, const void* sa, const void* qw, co
         const uint8_t* sa8 = reinterpret_cast<const uint8_t*>(sa);
         const uint8_t* sw8 = reinterpret_cast<const uint8_t*>(sw);
         const bool vec16 = N % 8 == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0;
-        if (FP8 && vec16)
+        // FP8: 256 x 224 tiles when they take fewer rounds on 256 CUs (see the FP4 branch)
+        const int tn224 = (int)((N + tile224_fp8::kTN - 1) / tile224_fp8::kTN);
+        const int64_t t256 = (int64_t)tiles_m * tiles_n, t224 = (int64_t)tiles_m * tn224;
+        const bool fp8_224 = FP8 && 7 * ((t224 + 255) / 256) < 8 * ((t256 + 255) / 256) &&
+                             (M > N ? M : N) * K < ((int64_t)1 << 31);
+        if (fp8_224 && vec16)
+            hipLaunchKernelGGL(gemm_tile224_fp8<true>, dim3((unsigned)t224), dim3(256), 0, st, a,
+                               reinterpret_cast<const float*>(sa), w, reinterpret_cast<const float*>(sw), out, m, n, k,
+                               tiles_m, tn224);
+        else if (fp8_224)
+            hipLaunchKernelGGL(gemm_tile224_fp8<false>, dim3((unsigned)t224), dim3(256), 0, st, a,
+                               reinterpret_cast<const float*>(sa), w, reinterpret_cast<const float*>(sw), out, m, n, k,
+                               tiles_m, tn224);
+        else if (FP8 && vec16)
             hipLaunchKernelGGL(gemm_tile_fp8<true>, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, st, a,
                                reinterpret_cast<const float*>(sa), w, reinterpret_cast<const float*>(sw), out, m, n, k,
                                tiles_m, tiles_n);

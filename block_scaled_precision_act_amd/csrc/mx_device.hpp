@@ -164,6 +164,15 @@ __device__ __forceinline__ void mfma16_fp4_agpr(v4f& c, v4u a, v4u b, uint32_t s
                      : "+a"(c)
                      : "v"(a), "v"(b), "v"(sa), "v"(sb));
 }
+// D += A(16x32) . B(32x16), FP16 operands, FP32 accumulation, as inline asm with the accumulator
+// tied to AGPRs (see mfma16_fp4_agpr: the caller owns the wait states around it).
+__device__ __forceinline__ void mfma16_f16_agpr(v4f& c, v8h a, v8h b) {
+    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+// Marks a VALU result as produced here (volatile asm statements keep their order), so it cannot
+// be computed any later: a caller places this a few instructions before an inline-asm MFMA that
+// reads the value.
+__device__ __forceinline__ void vgpr_tie(v8h& x) { asm volatile("" : "+v"(x)); }
 // s_nop 7, N times (8 N wait states).
 template <int N>
 __device__ __forceinline__ void wait_states8() {
