@@ -376,8 +376,9 @@ __global__ __launch_bounds__(256) void gemm_decode_lds_fp4(const uint8_t* __rest
 // tiles are summed through LDS in a fixed order (deterministic).
 // MFMA: 32 x 32 x 64, operand A = 32 weight rows (n), operand B = 32
 // activation rows (m); k-step t of a slab uses the row's chunks 4h + t in lane
-// group h (the K-permutation and (row / 2) % 8 chunk swizzle of the tile
-// path), so one scale dword per row and slab serves all four k-steps.  In the
+// group h (the K-permutation of the tile path; chunks are XOR-swizzled by
+// (row % 8) ^ ((row / 8) % 2), conflict-free for the MFMA-layout reads), so
+// one scale dword per row and slab serves all four k-steps.  In the
 // scale block, row r's 16-byte pieces are rotated by r (position p holds piece
 // (p + r) mod P), which spreads the 32 rows of a fragment over the LDS banks.
 // ============================================================================
@@ -439,8 +440,11 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_fp4(const uint8_t* __restr
         g2lds16(src, scb + 1024 * c);
     }
     // 2. code copies: copy i moves rows 8i .. 8i+7 (lane / 8) of the slab, the lane filling chunk
-    //    lane % 8 with logical chunk (lane % 8) ^ ((row / 2) % 8).  An activation copy whose 8 rows
-    //    all lie at or past M reads one address in every lane (one cache line): those rows only
+    //    lane % 8 with logical chunk (lane % 8) ^ swz(row), swz(r) = (r % 8) ^ ((r / 8) % 2): any 8
+    //    consecutive rows get 8 distinct chunks, so the 8 lanes an LDS cycle serves of a
+    //    ds_read_b128 (32 four-byte banks) hit distinct banks, and so do 16 lanes over 64 banks.
+    //    An activation copy whose 8 rows all lie at or past M reads one address in every lane (one
+    //    cache line): those rows only
     //    feed output columns that are never stored.  A batch for a slab past the wave's last one
     //    also reads a single address (one line, data unused), so every wave issues the same
     //    number of copies and the wait counts below are fixed.
@@ -448,7 +452,7 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_fp4(const uint8_t* __restr
 #pragma unroll
     for (int i = 0; i < C::kCopies; ++i) {
         const int r = 8 * i + (lane >> 3);
-        const int chunk = (lane & 7) ^ ((r >> 1) & 7);
+        const int chunk = (lane & 7) ^ ((r & 7) ^ ((r >> 3) & 1));
         if (r < C::kArows)
             rowp[i] = 8 * i < M ? qa + (int64_t)min(r, M - 1) * KB + 16 * chunk : qa;
         else
@@ -477,11 +481,11 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_fp4(const uint8_t* __restr
     for (int g = 0; g < MF; ++g) {
         const int r = 32 * g + l32;
         xoff[g] = r * kSlab;
-        xsw[g] = (r >> 1) & 7;
+        xsw[g] = (r & 7) ^ ((r >> 3) & 1);
         xsr[g] = r;
     }
     const int wr = C::kArows + l32;
-    const int woff = wr * kSlab, wsw = (wr >> 1) & 7;
+    const int woff = wr * kSlab, wsw = (wr & 7) ^ ((wr >> 3) & 1);
     auto scale_at = [&](int r, int j) -> uint32_t {  // dword of row r for local slab j, lane group h
         const int s = s0 + j;                            // slab index in K: bytes 8 s .. 8 s + 7 of the row
         int p = (s >> 1) - r % P;
