@@ -615,7 +615,8 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_fp8(const uint8_t* __restr
     uint8_t* const ring = lds + wave * S * C::kSlabBytes;
 
     // code copies: copy i moves rows 8i .. 8i+7 (lane / 8) of the slab, the lane filling chunk
-    // lane % 8 with logical chunk (lane % 8) ^ ((row / 2) % 8).  An activation copy whose 8 rows
+    // lane % 8 with logical chunk (lane % 8) ^ (row % 8) ^ ((row / 8) % 2) (the conflict-free swizzle
+    // of gemm_decode_fp4).  An activation copy whose 8 rows
     // all lie at or past M reads one address in every lane (one cache line): those rows only feed
     // outputs that are never stored.  A batch for a slab past the wave's last one also reads a
     // single address, so every wave issues the same number of copies and the waits are fixed.
@@ -623,7 +624,7 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_fp8(const uint8_t* __restr
 #pragma unroll
     for (int i = 0; i < C::kCopies; ++i) {
         const int r = 8 * i + (lane >> 3);
-        const int chunk = (lane & 7) ^ ((r >> 1) & 7);
+        const int chunk = (lane & 7) ^ ((r & 7) ^ ((r >> 3) & 1));
         if (r < C::kArows)
             rowp[i] = 8 * i < M ? qa + (int64_t)min(r, M - 1) * K + 16 * chunk : qa;
         else
@@ -649,10 +650,10 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_fp8(const uint8_t* __restr
     for (int g = 0; g < MF; ++g) {
         const int r = 32 * g + l32;
         xoff[g] = r * kSlab;
-        xsw[g] = (r >> 1) & 7;
+        xsw[g] = (r & 7) ^ ((r >> 3) & 1);
     }
     const int wr = C::kArows + l32;
-    const int woff = wr * kSlab, wsw = (wr >> 1) & 7;
+    const int woff = wr * kSlab, wsw = (wr & 7) ^ ((wr >> 3) & 1);
 
     v16f acc[MF];
 #pragma unroll
