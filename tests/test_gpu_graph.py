@@ -35,7 +35,9 @@ def _replays_match(mx, torch, thunk, outs):
         del junk
 
 
-@pytest.mark.parametrize("M,N,K", [(64, 512, 1024), (300, 512, 1024), (64, 7168, 8192), (16, 2000, 4096)])
+# decode rings (64, 16 rows), the 128-row tile with the 4-slot ring (300), the 256 x 224 tile (1300 x 7000)
+@pytest.mark.parametrize("M,N,K", [(64, 512, 1024), (300, 512, 1024), (64, 7168, 8192), (16, 2000, 4096),
+                                   (1300, 7000, 512)])
 def test_a4w4_layer_graph_replay(mx, M, N, K):
     import torch
     x = bf16_dev(synth.act_normal(61, M, K))
@@ -55,6 +57,7 @@ def test_a4w4_layer_graph_replay(mx, M, N, K):
     _replays_match(mx, torch, layer, [qa, sa, y])
 
 
+# the decode ring (64) and the 256 x 224 FP8 tile (300)
 @pytest.mark.parametrize("M", [64, 300])
 def test_a8w8_layer_graph_replay(mx, M):
     import torch
