@@ -16,7 +16,8 @@ Steps are replayed from a HIP graph.  The printed JSON line also carries:
                 launch / average launch time, HIP events on the launch stream)
   cpu_baseline  the CPU oracle timed on the same layer on the host cores
   also          the prefill layer (M = 8192), the PTPC FP8 A8W8 layers, the
-                M sweep and the quantizer kernels, each with its roofline.
+                M sweep, the quantizer kernels and the offline weight
+                conversions, each with its roofline.
 """
 from __future__ import annotations
 
@@ -68,6 +69,10 @@ def algorithmic_bytes(kind, M, N, K):
         return 2 * M * K + M * K // 2 + M * K // 32
     if kind == "ptpcq":
         return 2 * M * K + M * K + 4 * M
+    if kind == "mxw":  # offline weight conversion, FP32 in
+        return 4 * M * K + M * K // 2 + M * K // 32
+    if kind == "ptpcw":
+        return 4 * M * K + M * K + 4 * M
     raise ValueError(kind)
 
 
@@ -324,6 +329,37 @@ def layer_entry(ctx, layer, kind, args, label):
     return e
 
 
+def weight_conversion_entry(ctx, args):
+    """The offline weight conversions (FP32 -> MXFP4 + E8M0, FP32 -> E4M3 + FP32 channel scale) on the
+    o_proj weight [7168, 8192], two rotated copies, graph-replayed."""
+    torch, mx = ctx.torch, ctx.mx
+    from block_scaled_precision_act_amd import synth
+    cfg = synth.CONFIGS["oproj_decode_a4w4"]
+    N, K = cfg["N"], cfg["K"]
+    w0 = torch.from_numpy(synth.make_weight(cfg)).to(ctx.dev)
+    ws = [w0, w0.flip(0).contiguous()]
+    u8 = torch.uint8
+    q4 = [torch.empty((N, K // 2), dtype=u8, device=ctx.dev) for _ in ws]
+    s4 = [torch.empty((N, K // 32), dtype=u8, device=ctx.dev) for _ in ws]
+    q8 = [torch.empty((N, K), dtype=u8, device=ctx.dev) for _ in ws]
+    s8 = [torch.empty((N,), dtype=torch.float32, device=ctx.dev) for _ in ws]
+    out = {"workload": "offline weight conversion of W [%d, %d] FP32" % (N, K), "rotation": len(ws)}
+    for key, kind, fn, qs, ss in (("mxfp4", "mxw", mx.mx_quant_weight_f32, q4, s4),
+                                  ("ptpc_fp8", "ptpcw", mx.ptpc_quant_weight_f32, q8, s8)):
+        thunks = [(lambda i=i: ok(fn(ws[i].data_ptr(), N, K, qs[i].data_ptr(), ss[i].data_ptr(), ctx.stream()),
+                                  key)) for i in range(len(ws))]
+        g = ctx.capture(thunks)
+        ms = ctx.event_ms(g, args.kernel_reps) / len(ws)
+        byt = algorithmic_bytes(kind, N, 0, K)
+        gbs = byt / (ms * 1e-3) / 1e9
+        out[key] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(gbs / PEAK_HBM_GBS, 4), "kernel_us": round(ms * 1e3, 3),
+                    "alg_bytes_per_launch": byt}
+    del ws, w0, q4, s4, q8, s8
+    torch.cuda.empty_cache()
+    return out
+
+
 # ----------------------------------------------------------------------------- CPU baseline
 def cpu_baseline():
     import numpy as np
@@ -504,6 +540,8 @@ def main():
             also[name] = layer_entry(ctx, lay, "a8w8", args, name)
             del lay
             torch.cuda.empty_cache()
+        log("offline weight conversion")
+        also["weight_conversion"] = weight_conversion_entry(ctx, args)
         out["also"] = also
 
     if not args.no_cpu_baseline:
