@@ -16,8 +16,8 @@ Steps are replayed from a HIP graph.  The printed JSON line also carries:
                 launch / average launch time, HIP events on the launch stream)
   cpu_baseline  the CPU oracle timed on the same layer on the host cores
   also          the prefill layer (M = 8192), the PTPC FP8 A8W8 layers, the
-                M sweep, the quantizer kernels and the offline weight
-                conversions, each with its roofline.
+                M sweep, the quantizer kernels, the offline weight
+                conversions and the grouped MoE GEMM, each with its roofline.
 """
 from __future__ import annotations
 
@@ -360,6 +360,44 @@ def weight_conversion_entry(ctx, args):
     return out
 
 
+def grouped_entry(ctx, args):
+    """Grouped A4W4 GEMM over MoE experts (synthetic shapes: 64 tokens x top-8 over 32 experts of
+    [7168, 2048]), two rotated sets of expert weights, graph-replayed."""
+    import numpy as np
+    torch, mx = ctx.torch, ctx.mx
+    from block_scaled_precision_act_amd import synth
+    cfg = synth.CONFIGS["moe_grouped_a4w4"]
+    G, N, K = cfg["G"], cfg["N"], cfg["K"]
+    counts = synth.route_counts(cfg["route"], cfg["tokens"], cfg["topk"], G)
+    T, max_rows = int(counts.sum()), int(counts.max())
+    offsets = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32, device=ctx.dev)
+    x = torch.from_numpy(synth.make_activations(cfg, T).view(np.int16)).view(torch.bfloat16).to(ctx.dev)
+    qa, sa = mx.quant_act_mx(x)
+    qw1, sw1 = mx.quant_weight_mx(torch.from_numpy(synth.make_weight(cfg)).to(ctx.dev))
+    # distinct experts as row rotations of one MXFP4 draw (every expert a valid [N, K] weight)
+    R = 2
+    qws = [torch.stack([torch.roll(qw1, (37 * e + 11 * r) % N, 0) for e in range(G)]) for r in range(R)]
+    sws = [torch.stack([torch.roll(sw1, (37 * e + 11 * r) % N, 0) for e in range(G)]) for r in range(R)]
+    y = torch.empty((T, N), dtype=torch.bfloat16, device=ctx.dev)
+    thunks = [(lambda r=r: ok(mx.mx_gemm_a4w4_grouped_bf16(qa.data_ptr(), sa.data_ptr(), qws[r].data_ptr(),
+                                                           sws[r].data_ptr(), y.data_ptr(), offsets.data_ptr(), G,
+                                                           max_rows, N, K, ctx.stream()), "grouped"))
+              for r in range(R)]
+    g = ctx.capture(thunks)
+    ms = ctx.event_ms(g, args.kernel_reps) / R
+    used = counts > 0
+    byt = int(used.sum()) * (N * K // 2 + N * K // 32) + T * (K // 2 + K // 32) + 2 * T * N
+    gbs = byt / (ms * 1e-3) / 1e9
+    out = {"workload": "grouped MoE A4W4: %d tokens x top-%d over %d experts of [%d, %d], rows per expert %d..%d"
+                       % (cfg["tokens"], cfg["topk"], G, N, K, int(counts.min()), max_rows),
+           "rotation": R, "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+           "frac": round(gbs / PEAK_HBM_GBS, 4), "kernel_us": round(ms * 1e3, 3), "alg_bytes_per_launch": byt,
+           "tflops": round(2.0 * T * N * K / (ms * 1e-3) / 1e12, 2)}
+    del qws, sws, qw1, sw1, x, qa, sa, y
+    torch.cuda.empty_cache()
+    return out
+
+
 # ----------------------------------------------------------------------------- CPU baseline
 def cpu_baseline():
     import numpy as np
@@ -542,6 +580,8 @@ def main():
             torch.cuda.empty_cache()
         log("offline weight conversion")
         also["weight_conversion"] = weight_conversion_entry(ctx, args)
+        log("grouped MoE A4W4")
+        also["moe_grouped_a4w4"] = grouped_entry(ctx, args)
         out["also"] = also
 
     if not args.no_cpu_baseline:

@@ -107,6 +107,24 @@ MX_API mx_status mx_gemm_a4w4_bf16(const void* qa, const void* sa, const void* q
     return launched(mx::launch_gemm_a4w4(qa, sa, qw, sw, y_bf16, M, N, K, workspace, reinterpret_cast<hipStream_t>(stream)));
 }
 
+MX_API mx_status mx_gemm_a4w4_grouped_bf16(const void* qa, const void* sa, const void* qw, const void* sw,
+                                           void* y_bf16, const int32_t* offsets, int64_t G, int64_t max_rows,
+                                           int64_t N, int64_t K, void* stream) {
+    if (G < 0 || N < 0 || max_rows < 0) return MX_ERROR_INVALID_VALUE;
+    if (max_rows > 64 || G > 65535 || N > INT32_MAX || K <= 0 || K % 2048 != 0 || K > 16384)
+        return MX_ERROR_UNSUPPORTED_SHAPE;
+    if (N > (INT64_C(1) << 40) / K / (G > 0 ? G : 1)) return MX_ERROR_UNSUPPORTED_SHAPE;
+    if (G == 0 || N == 0 || max_rows == 0) return MX_SUCCESS;
+    if (!qa || !sa || !qw || !sw || !y_bf16 || !offsets) return MX_ERROR_INVALID_VALUE;
+    if (!aligned(qa, 16) || !aligned(qw, 16) || !aligned(sa, 16) || !aligned(sw, 16) || !aligned(y_bf16, 2) ||
+        !aligned(offsets, 4))
+        return MX_ERROR_MISALIGNED;
+    mx_status st;
+    if ((st = check_device()) != MX_SUCCESS) return st;
+    return launched(mx::launch_a4w4_grouped(qa, sa, qw, sw, y_bf16, offsets, G, max_rows, N, K,
+                                            reinterpret_cast<hipStream_t>(stream)));
+}
+
 static mx_status quant_ptpc(bool f32, const void* x, int64_t rows, int64_t K, void* q, float* s, void* stream) {
     mx_status st = check_rows(rows, K, 8);
     if (st != MX_SUCCESS) return st;

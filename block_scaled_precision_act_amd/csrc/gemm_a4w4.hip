@@ -12,6 +12,12 @@ hipError_t launch_gemm_a4w4(const void* qa, const void* sa, const void* qw, cons
     return launch_gemm<false>(qa, sa, qw, sw, y, M, N, K, st);
 }
 
+hipError_t launch_a4w4_grouped(const void* qa, const void* sa, const void* qw, const void* sw, void* y,
+                               const int32_t* offsets, int64_t G, int64_t max_rows, int64_t N, int64_t K,
+                               hipStream_t st) {
+    return launch_gemm_a4w4_grouped(qa, sa, qw, sw, y, offsets, G, max_rows, N, K, st);
+}
+
 // No kernel of the A4W4 path needs device scratch memory.
 size_t gemm_a4w4_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
 

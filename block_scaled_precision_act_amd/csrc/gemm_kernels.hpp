@@ -404,12 +404,30 @@ struct Cfg {
 };
 }  // namespace dec4
 
-template <int MF, int S, int KSMAX>
-__global__ __launch_bounds__(256, 1) void gemm_decode_fp4(const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa,
+// GROUPED: grid.y indexes groups (MoE experts).  Group e multiplies rows goff[e] .. goff[e+1]-1
+// of the packed activations with weight e of the stacked weights ([G, N, K/2] codes, [G, N, K/32]
+// scales) into the same rows of y; it takes at most 32 MF rows (the caller's bound), and an empty
+// group's workgroups return before their first barrier.
+// KSMAX = 64 (K <= 2048, 68 KB of LDS at MF = 1, S = 2) lets two workgroups share a CU: with so
+// few slabs per wave, concurrency rather than ring depth hides the memory latency.
+template <int MF, int S, int KSMAX, bool GROUPED = false>
+__global__ __launch_bounds__(256, KSMAX == 64 ? 2 : 1) void gemm_decode_fp4(const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa,
                                                           const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw,
-                                                          uint16_t* __restrict__ y, int M, int N, int K) {
+                                                          uint16_t* __restrict__ y, int M, int N, int K,
+                                                          const int32_t* __restrict__ goff) {
     using C = dec4::Cfg<MF, S, KSMAX>;
     using namespace dec4;
+    if constexpr (GROUPED) {
+        const int e = blockIdx.y;
+        const int r0 = goff[e];
+        M = min(goff[e + 1] - r0, 32 * MF);
+        if (M <= 0) return;  // the whole workgroup (M is uniform), before any barrier
+        qa += (int64_t)r0 * (K / 2);
+        sa += (int64_t)r0 * (K / 32);
+        y += (int64_t)r0 * N;
+        qw += (int64_t)e * N * (K / 2);
+        sw += (int64_t)e * N * (K / 32);
+    }
     __shared__ __attribute__((aligned(1024))) uint8_t lds[C::kLds];
     const int n0 = blockIdx.x * kNT;
     const int lane = threadIdx.x & 63;
@@ -2168,13 +2186,17 @@ inline hipError_t launch_gemm(const void* qa, const void* sa, const void* qw, co
         const uint8_t* sa8 = reinterpret_cast<const uint8_t*>(sa);
         const uint8_t* sw8 = reinterpret_cast<const uint8_t*>(sw);
         if (M <= 32 && K <= 8192)
-            hipLaunchKernelGGL((gemm_decode_fp4<1, 4, 256>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k);
+            hipLaunchKernelGGL((gemm_decode_fp4<1, 4, 256>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k,
+                               nullptr);
         else if (M <= 32)
-            hipLaunchKernelGGL((gemm_decode_fp4<1, 4, 512>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k);
+            hipLaunchKernelGGL((gemm_decode_fp4<1, 4, 512>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k,
+                               nullptr);
         else if (K <= 8192)
-            hipLaunchKernelGGL((gemm_decode_fp4<2, 2, 256>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k);
+            hipLaunchKernelGGL((gemm_decode_fp4<2, 2, 256>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k,
+                               nullptr);
         else
-            hipLaunchKernelGGL((gemm_decode_fp4<2, 2, 512>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k);
+            hipLaunchKernelGGL((gemm_decode_fp4<2, 2, 512>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k,
+                               nullptr);
     } else if (!FP8 && M <= 128 && K % 512 == 0) {
         const dim3 grid((unsigned)((N + 31) / 32));
         const uint8_t* sa8 = reinterpret_cast<const uint8_t*>(sa);
@@ -2280,6 +2302,36 @@ inline hipError_t launch_gemm(const void* qa, const void* sa, const void* qw, co
             hipLaunchKernelGGL((gemm_tile_kernel<FP8>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, st, a, sa,
                                w, sw, out, m, n, k, tiles_m, tiles_n);
     }
+    return hipGetLastError();
+}
+
+// Grouped A4W4 decode GEMM (MoE experts): grid (N / 32, G); every group at most max_rows <= 64 rows,
+// K % 2048 == 0, K <= 16384, all code and scale pointers 16-byte aligned (checked by the caller).
+inline hipError_t launch_gemm_a4w4_grouped(const void* qa, const void* sa, const void* qw, const void* sw, void* y,
+                                           const int32_t* offsets, int64_t G, int64_t max_rows, int64_t N, int64_t K,
+                                           hipStream_t st) {
+    const uint8_t* a = reinterpret_cast<const uint8_t*>(qa);
+    const uint8_t* w = reinterpret_cast<const uint8_t*>(qw);
+    const uint8_t* sa8 = reinterpret_cast<const uint8_t*>(sa);
+    const uint8_t* sw8 = reinterpret_cast<const uint8_t*>(sw);
+    uint16_t* out = reinterpret_cast<uint16_t*>(y);
+    const int n = (int)N, k = (int)K;
+    const dim3 grid((unsigned)((N + dec4::kNT - 1) / dec4::kNT), (unsigned)G);
+    if (max_rows <= 32 && K <= 2048)
+        hipLaunchKernelGGL((gemm_decode_fp4<1, 2, 64, true>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, 0, n, k,
+                           offsets);
+    else if (max_rows <= 32 && K <= 8192)
+        hipLaunchKernelGGL((gemm_decode_fp4<1, 4, 256, true>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, 0, n, k,
+                           offsets);
+    else if (max_rows <= 32)
+        hipLaunchKernelGGL((gemm_decode_fp4<1, 4, 512, true>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, 0, n, k,
+                           offsets);
+    else if (K <= 8192)
+        hipLaunchKernelGGL((gemm_decode_fp4<2, 2, 256, true>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, 0, n, k,
+                           offsets);
+    else
+        hipLaunchKernelGGL((gemm_decode_fp4<2, 2, 512, true>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, 0, n, k,
+                           offsets);
     return hipGetLastError();
 }
 

@@ -63,6 +63,8 @@ def lib() -> ctypes.CDLL:
         L.mx_gemm_a4w4_bf16.restype = i32
         L.gemm_a8w8_ptpc_bf16.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
         L.gemm_a8w8_ptpc_bf16.restype = i32
+        L.mx_gemm_a4w4_grouped_bf16.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp]
+        L.mx_gemm_a4w4_grouped_bf16.restype = i32
         _lib = L
     return _lib
 
@@ -90,6 +92,10 @@ def mx_gemm_a4w4_workspace_bytes(M, N, K) -> int:
 
 def mx_gemm_a4w4_bf16(qa, sa, qw, sw, y, M, N, K, workspace=None, workspace_bytes=0, stream=None) -> int:
     return lib().mx_gemm_a4w4_bf16(qa, sa, qw, sw, y, M, N, K, workspace, workspace_bytes, stream)
+
+
+def mx_gemm_a4w4_grouped_bf16(qa, sa, qw, sw, y, offsets, G, max_rows, N, K, stream=None) -> int:
+    return lib().mx_gemm_a4w4_grouped_bf16(qa, sa, qw, sw, y, offsets, G, max_rows, N, K, stream)
 
 
 def ptpc_quant_act_fp8(x, M, K, q, s, stream=None) -> int:
@@ -169,6 +175,27 @@ def gemm_a4w4(qa, sa, qw, sw, y=None):
     wbuf = torch.empty(ws, dtype=torch.uint8, device=qa.device) if ws else None
     _ok(mx_gemm_a4w4_bf16(qa.data_ptr(), sa.data_ptr(), qw.data_ptr(), sw.data_ptr(), y.data_ptr(), M, N, K,
                           wbuf.data_ptr() if ws else None, ws, _stream()), "mx_gemm_a4w4_bf16")
+    return y
+
+
+def gemm_a4w4_grouped(qa, sa, qw, sw, offsets, max_rows, y=None):
+    """Grouped A4W4 GEMM over experts: qa [T, K/2] / sa [T, K/32] packed activation rows, qw [G, N, K/2] /
+    sw [G, N, K/32] stacked expert weights, offsets int32 [G + 1] (device) -> BF16 Y [T, N], rows
+    offsets[e] .. offsets[e+1]-1 multiplied with expert e.  max_rows bounds every group's row count."""
+    torch = _torch()
+    for t, n in ((qa, "qa"), (sa, "sa")):
+        _need(t, torch.uint8, 2, n)
+    for t, n in ((qw, "qw"), (sw, "sw")):
+        _need(t, torch.uint8, 3, n)
+    _need(offsets, torch.int32, 1, "offsets")
+    T, K = qa.shape[0], qa.shape[1] * 2
+    G, N = qw.shape[0], qw.shape[1]
+    if (qw.shape[2] * 2 != K or sa.shape != (T, K // 32) or sw.shape != (G, N, K // 32)
+            or offsets.shape[0] != G + 1):
+        raise ValueError("inconsistent grouped A4W4 operand shapes")
+    y = torch.empty((T, N), dtype=torch.bfloat16, device=qa.device) if y is None else y
+    _ok(mx_gemm_a4w4_grouped_bf16(qa.data_ptr(), sa.data_ptr(), qw.data_ptr(), sw.data_ptr(), y.data_ptr(),
+                                  offsets.data_ptr(), G, max_rows, N, K, _stream()), "mx_gemm_a4w4_grouped_bf16")
     return y
 
 

@@ -134,7 +134,20 @@ CONFIGS = {
                                 x=("t3_outlier", 6, 7), w=("normal", 5, 0.02)),
     "ptpc_a8w8_m64": dict(kind="a8w8", M=64, N=OPROJ_N, K=OPROJ_K, x=("normal", 9), w=("normal", 8, 0.01)),
     "ptpc_a8w8_m8192": dict(kind="a8w8", M=8192, N=OPROJ_N, K=OPROJ_K, x=("normal", 10), w=("normal", 8, 0.01)),
+    # grouped MoE decode (synthetic: the pages give no expert shapes): 64 tokens x top-8 routed over
+    # 32 experts, each expert a [7168, 2048] MXFP4 projection (hidden 7168, intermediate 2048)
+    "moe_grouped_a4w4": dict(kind="a4w4_grouped", tokens=64, topk=8, G=32, N=OPROJ_N, K=2048,
+                             x=("normal", 11), w=("normal", 12, 0.02), route=13),
 }
+
+
+def route_counts(seed: int, tokens: int, topk: int, G: int) -> np.ndarray:
+    """Rows per expert when each token picks topk distinct experts uniformly (seeded): the first
+    topk entries of a Fisher-Yates shuffle of range(G), one shuffle per token."""
+    counts = np.zeros(G, np.int64)
+    for t in range(tokens):
+        counts[fisher_yates_prefix(seed * 1_000_003 + t, G, topk)] += 1
+    return counts
 
 
 def make_activations(cfg: dict, M: int | None = None) -> np.ndarray:

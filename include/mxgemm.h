@@ -111,6 +111,26 @@ mx_status mx_gemm_a4w4_bf16(const void *qa, const void *sa, const void *qw, cons
                             void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Grouped A4W4 GEMM over MoE experts, decode-sized groups: expert weights and
+ * activations both in OCP MXFP4 ("Kimi-K3-Quark-MXFP4-AttnFP8", section
+ * "Model Quantization").  Group e multiplies the activation rows
+ * offsets[e] .. offsets[e+1]-1 with expert weight e:
+ *   Y[r, :] = dequant(qa, sa)[r] . dequant(qw[e], sw[e])^T  for those rows r.
+ *   qa [T, K/2], sa [T, K/32]        packed activation codes / scales, T = offsets[G]
+ *   qw [G, N, K/2], sw [G, N, K/32]  stacked expert weights (e.g. mx_quant_weight_f32 on [G*N, K])
+ *   y_bf16 [T, N]                    out; rows outside every group are not written
+ *   offsets [G + 1] int32, DEVICE memory, non-decreasing, offsets[0] = 0: read by the
+ *            kernel, so routing computed on the GPU needs no host round trip (capturable)
+ *   max_rows  an upper bound on every group's row count, 0 <= max_rows <= 64; a group
+ *            with more rows has only its first max_rows rounded up to 32 or 64 rows written
+ * K % 2048 == 0 and K <= 16384; qa, sa, qw, sw 16-byte aligned; y_bf16 2-byte
+ * aligned; offsets 4-byte aligned; G <= 65535.  G, N or max_rows == 0: no-op.
+ */
+mx_status mx_gemm_a4w4_grouped_bf16(const void *qa, const void *sa, const void *qw, const void *sw,
+                                    void *y_bf16, const int32_t *offsets, int64_t G, int64_t max_rows,
+                                    int64_t N, int64_t K, void *stream);
+
+/*
  * Dynamic per-token FP8 quantization of BF16 activations ("dynamic per-token
  * FP8, computed online": "Kimi-K3-DSpark-FP8-PTPC", section "Phase 1 FP8 PTPC
  * Quantization").

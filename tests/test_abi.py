@@ -83,6 +83,23 @@ def test_gemm_argument_errors(mx):
     assert g8(None, None, None, None, None, 0, 0, 128) == mx.MX_SUCCESS
 
 
+def test_grouped_gemm_argument_errors(mx):
+    gg = mx.mx_gemm_a4w4_grouped_bf16
+    ok_args = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert gg(*ok_args, -1, 16, 512, 2048) == mx.MX_ERROR_INVALID_VALUE       # G
+    assert gg(*ok_args, 4, -1, 512, 2048) == mx.MX_ERROR_INVALID_VALUE        # max_rows
+    assert gg(*ok_args, 4, 16, -1, 2048) == mx.MX_ERROR_INVALID_VALUE         # N
+    assert gg(*ok_args, 4, 65, 512, 2048) == mx.MX_ERROR_UNSUPPORTED_SHAPE    # groups above 64 rows
+    assert gg(*ok_args, 4, 16, 512, 1024) == mx.MX_ERROR_UNSUPPORTED_SHAPE    # K % 2048
+    assert gg(*ok_args, 4, 16, 512, 18432) == mx.MX_ERROR_UNSUPPORTED_SHAPE   # K > 16384
+    assert gg(*ok_args, 65536, 16, 512, 2048) == mx.MX_ERROR_UNSUPPORTED_SHAPE
+    assert gg(FAKE, FAKE, FAKE, FAKE, FAKE, None, 4, 16, 512, 2048) == mx.MX_ERROR_INVALID_VALUE
+    assert gg(FAKE, FAKE + 4, FAKE, FAKE, FAKE, FAKE, 4, 16, 512, 2048) == mx.MX_ERROR_MISALIGNED
+    assert gg(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 2, 4, 16, 512, 2048) == mx.MX_ERROR_MISALIGNED
+    assert gg(None, None, None, None, None, None, 0, 16, 512, 2048) == mx.MX_SUCCESS   # no groups
+    assert gg(None, None, None, None, None, None, 4, 0, 512, 2048) == mx.MX_SUCCESS   # empty groups
+
+
 def test_valid_arguments_without_a_gpu_report_no_device(mx):
     import torch
     if torch.cuda.is_available():

@@ -75,3 +75,25 @@ def test_a8w8_layer_graph_replay(mx, M):
                                       M, N, K, s) == 0
 
     _replays_match(mx, torch, layer, [qa, sa, y])
+
+
+def test_a4w4_grouped_graph_replay(mx):
+    # the grouped MoE GEMM reads its group offsets on the device: capturable with routing on the GPU
+    import torch
+    sizes, N, K = [3, 0, 17, 40], 512, 2048
+    G, T = len(sizes), sum(sizes)
+    x = bf16_dev(synth.act_normal(65, T, K))
+    qw, sw = mx.quant_weight_mx(torch.from_numpy(synth.weight_normal(66, G * N, K, 0.02)).cuda())
+    qw, sw = qw.view(G, N, K // 2), sw.view(G, N, K // 32)
+    offsets = torch.tensor([0] + list(np.cumsum(sizes)), dtype=torch.int32, device="cuda")
+    qa = torch.empty((T, K // 2), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((T, K // 32), dtype=torch.uint8, device="cuda")
+    y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+
+    def layer():
+        s = torch.cuda.current_stream().cuda_stream
+        assert mx.mx_quant_act_bf16(x.data_ptr(), T, K, qa.data_ptr(), sa.data_ptr(), s) == 0
+        assert mx.mx_gemm_a4w4_grouped_bf16(qa.data_ptr(), sa.data_ptr(), qw.data_ptr(), sw.data_ptr(), y.data_ptr(),
+                                            offsets.data_ptr(), G, 64, N, K, s) == 0
+
+    _replays_match(mx, torch, layer, [qa, sa, y])

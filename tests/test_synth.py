@@ -39,3 +39,13 @@ def test_bf16_rounding_is_nearest_even():
     vals = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -1.0 - 2.0 ** -8, 1.0 + 2.0 ** -8 + 2.0 ** -20])
     got = synth.bf16_bits_to_f32(synth.f64_to_bf16_bits(vals))
     assert list(got) == [1.0, 1.0 + 2.0 ** -6, -1.0, 1.0 + 2.0 ** -7]
+
+
+def test_route_counts_are_topk_distinct_experts_per_token():
+    # every token contributes exactly topk rows, to topk distinct experts; seeded and reproducible
+    c = synth.route_counts(13, 64, 8, 32)
+    assert c.sum() == 64 * 8 and c.max() <= 64 and len(c) == 32
+    assert np.array_equal(c, synth.route_counts(13, 64, 8, 32))
+    for t in range(3):
+        picks = synth.fisher_yates_prefix(13 * 1_000_003 + t, 32, 8)
+        assert len(set(picks.tolist())) == 8
