@@ -1129,9 +1129,9 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_dma_fp4(const uint8_t* __res
 // request for part of a 128-byte line costs as much as the whole line, so
 // every global -> LDS copy here moves whole lines: a superstage is K = 256
 // (128 code bytes per row) of both TM-row operands, 8 rows per wave
-// instruction, into a ring of S slots (S = 2 for 256-row tiles; S = 4 for
-// 128-row tiles, whose small superstages would otherwise wait on copy
-// latency).  Scales are fetched in bulk, 32 bytes per row (K = 1024, four
+// instruction, into a ring of S slots (S = 2; S = 4 for 128-row tiles when
+// there is at most one tile per CU, whose small superstages would otherwise
+// wait on copy latency).  Scales are fetched in bulk, 32 bytes per row (K = 1024, four
 // superstages), into a ring of NB buffers, a quarter of a block with every
 // superstage's copies.
 // Output tile TM x TM (256, or 128 for shapes with too few 256-tiles to fill
