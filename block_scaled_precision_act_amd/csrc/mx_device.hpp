@@ -261,32 +261,36 @@ __device__ __forceinline__ void lds_wait_n_of(v4u (&a)[FW], v4u (&b)[FW]) {
     for (int i = 0; i < FW; ++i) asm volatile("" : "+v"(a[i]), "+v"(b[i]));
 }
 
-// MXFP4 quantization of eight consecutive BF16 values (one 16-byte load), the lane being one of four
-// consecutive lanes that hold a 32-value block (lanes 4k .. 4k+3, all active).  Returns the lane's
-// eight E2M1 codes (value 2i in the low nibble of byte i) and sets scale to the block's E8M0 byte:
-// max(E - 2, 0) for the largest exponent field E of the block, 0xFF with zero codes if the block holds
-// a NaN or an infinity.  The codes come from gfx950's scaled conversion, which divides by the
-// power-of-two scale and rounds to the nearest E2M1 value, ties to the even code, saturating at 6
-// and keeping the sign.
-__device__ __forceinline__ uint32_t mx_bf16x8_codes(uint4 x, uint32_t& scale) {
-    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+// MXFP4 quantization of one 32-value BF16 block (four 16-byte loads, values 8i .. 8i+7 in x[i]) by
+// one lane.  Returns the block's 16 code bytes (value 2j in the low nibble of byte j) and sets scale
+// to its E8M0 byte: max(E - 2, 0) for the largest exponent field E of the block, 0xFF with zero
+// codes if the block holds a NaN or an infinity.  The codes come from gfx950's scaled conversion,
+// which divides by the power-of-two scale and rounds to the nearest E2M1 value, ties to the even
+// code, saturating at 6 and keeping the sign.
+__device__ __forceinline__ uint4 mx_bf16x32_codes(const uint4 (&x)[4], uint32_t& scale) {
     uint32_t emax = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) emax = max(emax, max((w[i] >> 7) & 0xffu, (w[i] >> 23) & 0xffu));
-    emax = max(emax, (uint32_t)__shfl_xor((int)emax, 1));
-    emax = max(emax, (uint32_t)__shfl_xor((int)emax, 2));
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t w[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) emax = max(emax, max((w[j] >> 7) & 0xffu, (w[j] >> 23) & 0xffu));
+    }
     if (emax == 0xffu) {  // NaN or Inf in the block
         scale = 0xffu;
-        return 0u;
+        return make_uint4(0u, 0u, 0u, 0u);
     }
     scale = emax > 2u ? emax - 2u : 0u;
     const float sc = __uint_as_float(scale ? scale << 23 : 1u << 22);  // 2^(scale - 127)
     typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-    uint32_t codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(0u, __builtin_bit_cast(bf2, x.x), sc, 0);
-    codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes, __builtin_bit_cast(bf2, x.y), sc, 1);
-    codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes, __builtin_bit_cast(bf2, x.z), sc, 2);
-    codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes, __builtin_bit_cast(bf2, x.w), sc, 3);
-    return codes;
+    uint32_t c[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t v = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(0u, __builtin_bit_cast(bf2, x[i].x), sc, 0);
+        v = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(v, __builtin_bit_cast(bf2, x[i].y), sc, 1);
+        v = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(v, __builtin_bit_cast(bf2, x[i].z), sc, 2);
+        c[i] = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(v, __builtin_bit_cast(bf2, x[i].w), sc, 3);
+    }
+    return make_uint4(c[0], c[1], c[2], c[3]);
 }
 
 __device__ __forceinline__ uint4 ldg16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
