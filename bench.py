@@ -448,7 +448,7 @@ def profile_pass(ctx):
 # ----------------------------------------------------------------------------- PMC summary
 # Kernels whose HBM traffic the bench reports: key -> (name fragment, grid size in threads or None)
 PMC_KERNELS = {
-    "gemm_decode_fp4_m64": ("gemm_decode_fp4<2, 2, 256, false>", None),
+    "gemm_decode_fp4_m64": ("gemm_decode_fp4<2, 2, 256, false, 1>", None),
     "gemm_tile224_fp4_m8192": ("gemm_tile224_fp4<true>", 1024 * 256),
 }
 COPY_BYTES = 256 << 20  # the profile pass copies 256 MiB device -> device
@@ -538,7 +538,7 @@ def main():
 
     roof = roofline_gemm("a4w4", M, N, K, gemm_ms)
     roof["traffic"] = pmc_traffic("gemm_decode_fp4_m64")
-    roof["kernel"] = "gemm_decode_fp4<2, 2, 256, false>"
+    roof["kernel"] = "gemm_decode_fp4<2, 2, 256, false, 1>"
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak",

@@ -363,7 +363,7 @@ __global__ __launch_bounds__(256) void gemm_decode_lds_fp4(const uint8_t* __rest
 
 // ============================================================================
 // Decode path, per-wave LDS rings (FP4, M <= 64, K % 2048 == 0, K <= 16384,
-// 16-byte aligned scale rows).
+// 16-byte aligned scale rows; M <= 128 and K <= 8192 with two row halves).
 // One workgroup (4 waves) per 32 output columns.  A slab is K = 256 of the
 // 32*MF activation rows and the 32 weight rows: 128 code bytes per row, copied
 // global -> LDS (global_load_lds) 8 whole rows (whole cache lines) per wave
@@ -373,7 +373,9 @@ __global__ __launch_bounds__(256) void gemm_decode_lds_fp4(const uint8_t* __rest
 // 64 activation rows, then 32 weight rows, contiguous in memory) are copied
 // once, up front, as whole lines into one shared block; after that single
 // barrier no wave waits for another until the end, when the four partial
-// tiles are summed through LDS in a fixed order (deterministic).
+// tiles are summed through LDS in a fixed order (deterministic).  With two
+// row halves (RH = 2, M <= 128) waves 2h and 2h+1 share K half h, each with
+// its own 64 activation rows, and two partial tiles meet per output.
 // MFMA: 32 x 32 x 64, operand A = 32 weight rows (n), operand B = 32
 // activation rows (m); k-step t of a slab uses the row's chunks 4h + t in lane
 // group h (the K-permutation of the tile path; chunks are XOR-swizzled by
@@ -387,13 +389,19 @@ constexpr int kNT = 32;             // output columns per workgroup
 constexpr int kSlab = 128;          // code bytes per row per slab (K = 256)
 constexpr int kMaxMine = 16;        // slabs per wave supported (K <= 16384)
 // KSMAX: scale bytes per row the shared block holds (256: K <= 8192, 512: K <= 16384)
-template <int MF, int S, int KSMAX>
+// RH: row halves.  RH = 1: wave w owns K quarter w of all 32 MF activation rows.  RH = 2: wave w
+// owns K half w / 2 of activation rows 32 MF (w % 2) .. 32 MF (w % 2) + 32 MF - 1, so a slab still
+// holds 32 MF activation rows and the workgroup covers 64 MF rows (both waves of a K half copy
+// the same weight rows; the second copy is mostly an L2 hit).
+template <int MF, int S, int KSMAX, int RH = 1>
 struct Cfg {
-    static constexpr int kArows = 32 * MF;
+    static constexpr int kArows = 32 * MF;                   // activation rows per slab
     static constexpr int kRows = kArows + kNT;              // activation rows, then weight rows
     static constexpr int kSlabBytes = kRows * kSlab;         // 12 KB (MF = 2) or 8 KB
     static constexpr int kCopies = kSlabBytes / 1024;        // copies per wave per slab
-    static constexpr int kScBytes = kRows * KSMAX;           // shared scale block
+    static constexpr int kScArows = RH * kArows;             // activation rows of the workgroup
+    static constexpr int kScRows = kScArows + kNT;           // rows of the shared scale block
+    static constexpr int kScBytes = kScRows * KSMAX;         // shared scale block
     static constexpr int kScCopies = kScBytes / 1024 / 4;    // scale copies per wave
     static constexpr int kRing = 4 * S * kSlabBytes;
     static constexpr int kLds = kRing + kScBytes;
@@ -401,6 +409,7 @@ struct Cfg {
     static_assert(kScCopies + S * kCopies <= 63, "vmcnt");
     static_assert(kLds <= 160 * 1024, "LDS");
     static_assert(4 * MF * 16 * 64 * 4 <= kLds, "reduction staging");
+    static_assert(RH == 1 || RH == 2, "row halves");
 };
 }  // namespace dec4
 
@@ -410,17 +419,17 @@ struct Cfg {
 // group's workgroups return before their first barrier.
 // KSMAX = 64 (K <= 2048, 68 KB of LDS at MF = 1, S = 2) lets two workgroups share a CU: with so
 // few slabs per wave, concurrency rather than ring depth hides the memory latency.
-template <int MF, int S, int KSMAX, bool GROUPED = false>
+template <int MF, int S, int KSMAX, bool GROUPED = false, int RH = 1>
 __global__ __launch_bounds__(256, KSMAX == 64 ? 2 : 1) void gemm_decode_fp4(const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa,
                                                           const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw,
                                                           uint16_t* __restrict__ y, int M, int N, int K,
                                                           const int32_t* __restrict__ goff) {
-    using C = dec4::Cfg<MF, S, KSMAX>;
+    using C = dec4::Cfg<MF, S, KSMAX, RH>;
     using namespace dec4;
     if constexpr (GROUPED) {
         const int e = blockIdx.y;
         const int r0 = goff[e];
-        M = min(goff[e + 1] - r0, 32 * MF);
+        M = min(goff[e + 1] - r0, C::kScArows);
         if (M <= 0) return;  // the whole workgroup (M is uniform), before any barrier
         qa += (int64_t)r0 * (K / 2);
         sa += (int64_t)r0 * (K / 32);
@@ -435,8 +444,10 @@ __global__ __launch_bounds__(256, KSMAX == 64 ? 2 : 1) void gemm_decode_fp4(cons
     const int l32 = lane & 31, h = lane >> 5;
     const int64_t KB = (int64_t)K / 2;
     const int KS = K / 32;                  // scale bytes per row
-    const int nmine = K / 1024;             // slabs per wave (even)
-    const int s0 = wave * nmine;            // first slab of this wave
+    const int kq = wave / RH, rh = wave % RH;  // K part and row half of this wave
+    const int nmine = K * RH / 1024;        // slabs per wave (even)
+    const int s0 = kq * nmine;              // first slab of this wave
+    const int ra = rh * C::kArows;          // first activation row of this wave
     uint8_t* const ring = lds + wave * S * C::kSlabBytes;
     uint8_t* const scb = lds + C::kRing;
 
@@ -450,10 +461,10 @@ __global__ __launch_bounds__(256, KSMAX == 64 ? 2 : 1) void gemm_decode_fp4(cons
         const int q = 64 * c + lane;
         const int r = q / P, p = q - r * P;
         const uint8_t* src = sa;
-        if (r < C::kRows) {
+        if (r < C::kScRows) {
             const int64_t off = 16 * ((p + r) % P);
-            src = r < C::kArows ? sa + (int64_t)min(r, M - 1) * KS + off
-                                : sw + (int64_t)min(n0 + r - C::kArows, N - 1) * KS + off;
+            src = r < C::kScArows ? sa + (int64_t)min(r, M - 1) * KS + off
+                                  : sw + (int64_t)min(n0 + r - C::kScArows, N - 1) * KS + off;
         }
         g2lds16(src, scb + 1024 * c);
     }
@@ -472,7 +483,7 @@ __global__ __launch_bounds__(256, KSMAX == 64 ? 2 : 1) void gemm_decode_fp4(cons
         const int r = 8 * i + (lane >> 3);
         const int chunk = (lane & 7) ^ ((r & 7) ^ ((r >> 3) & 1));
         if (r < C::kArows)
-            rowp[i] = 8 * i < M ? qa + (int64_t)min(r, M - 1) * KB + 16 * chunk : qa;
+            rowp[i] = ra + 8 * i < M ? qa + (int64_t)min(ra + r, M - 1) * KB + 16 * chunk : qa;
         else
             rowp[i] = qw + (int64_t)min(n0 + r - C::kArows, N - 1) * KB + 16 * chunk;
     }
@@ -500,9 +511,9 @@ __global__ __launch_bounds__(256, KSMAX == 64 ? 2 : 1) void gemm_decode_fp4(cons
         const int r = 32 * g + l32;
         xoff[g] = r * kSlab;
         xsw[g] = (r & 7) ^ ((r >> 3) & 1);
-        xsr[g] = r;
+        xsr[g] = ra + r;  // row of the scale block
     }
-    const int wr = C::kArows + l32;
+    const int wr = C::kArows + l32, wsr = C::kScArows + l32;
     const int woff = wr * kSlab, wsw = (wr & 7) ^ ((wr >> 3) & 1);
     auto scale_at = [&](int r, int j) -> uint32_t {  // dword of row r for local slab j, lane group h
         const int s = s0 + j;                            // slab index in K: bytes 8 s .. 8 s + 7 of the row
@@ -524,7 +535,7 @@ __global__ __launch_bounds__(256, KSMAX == 64 ? 2 : 1) void gemm_decode_fp4(cons
         wait_vmcnt<(S - 1) * C::kCopies>();
         __builtin_amdgcn_sched_barrier(0);
         const uint32_t sb = rbase + (j % S) * C::kSlabBytes;
-        uint32_t ws = scale_at(wr, j);
+        uint32_t ws = scale_at(wsr, j);
         uint32_t xs[MF];
 #pragma unroll
         for (int g = 0; g < MF; ++g) xs[g] = scale_at(xsr[g], j);
@@ -548,7 +559,7 @@ __global__ __launch_bounds__(256, KSMAX == 64 ? 2 : 1) void gemm_decode_fp4(cons
         }
     }
 
-    // 3. fixed-order reduction of the four partial tiles through LDS
+    // 3. fixed-order reduction of the partial tiles (four per output, or two with RH = 2) through LDS
     wait_vmcnt<0>();  // the trailing refills
     __syncthreads();  // every wave is done with its ring and scale block
     float* red = reinterpret_cast<float*>(lds);  // [wave][g][reg][lane]
@@ -557,21 +568,22 @@ __global__ __launch_bounds__(256, KSMAX == 64 ? 2 : 1) void gemm_decode_fp4(cons
 #pragma unroll
         for (int r = 0; r < 16; ++r) red[((wave * MF + g) * 16 + r) * 64 + lane] = acc[g][r];
     __syncthreads();
-    // wave w finalizes register quad w of every fragment: D rows (n) 8w + 4h + e, column (m) l32
+    // wave w finalizes register quad w of every fragment of every row half: D rows (n) 8w + 4h + e,
+    // column (m) l32; the partials of K parts 0, 1, ... are added in that order
     const bool vec_ok = (N & 3) == 0 && (reinterpret_cast<uintptr_t>(y) & 7) == 0;
 #pragma unroll
-    for (int g = 0; g < MF; ++g) {
+    for (int fg = 0; fg < RH * MF; ++fg) {
+        const int half = fg / MF, g = fg % MF;
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = 4 * wave + e;
-            float t = red[((0 * MF + g) * 16 + r) * 64 + lane];
-            t += red[((1 * MF + g) * 16 + r) * 64 + lane];
-            t += red[((2 * MF + g) * 16 + r) * 64 + lane];
-            t += red[((3 * MF + g) * 16 + r) * 64 + lane];
+            float t = red[((half * MF + g) * 16 + r) * 64 + lane];
+#pragma unroll
+            for (int q = 1; q < 4 / RH; ++q) t += red[(((q * RH + half) * MF + g) * 16 + r) * 64 + lane];
             v[e] = t;
         }
-        const int m = 32 * g + l32;
+        const int m = half * C::kArows + 32 * g + l32;
         const int n = n0 + 8 * wave + 4 * h;
         if (m >= M) continue;
         uint16_t* dst = y + (int64_t)m * N + n;
@@ -2199,6 +2211,12 @@ inline hipError_t launch_gemm(const void* qa, const void* sa, const void* qw, co
         else
             hipLaunchKernelGGL((gemm_decode_fp4<2, 2, 512>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k,
                                nullptr);
+    } else if (!FP8 && M <= 128 && K % 2048 == 0 && K <= 8192 && scales16) {
+        // two row halves of 64 rows: the per-wave slabs of the M = 64 kernel, and every CU reads the
+        // activations once (128 scale rows + 32: a 40 KB scale block beside the 96 KB ring)
+        hipLaunchKernelGGL((gemm_decode_fp4<2, 2, 256, false, 2>), dim3((unsigned)((N + dec4::kNT - 1) / dec4::kNT)),
+                           dim3(256), 0, st, a, reinterpret_cast<const uint8_t*>(sa), w,
+                           reinterpret_cast<const uint8_t*>(sw), out, m, n, k, nullptr);
     } else if (!FP8 && M <= 128 && K % 512 == 0) {
         const dim3 grid((unsigned)((N + 31) / 32));
         const uint8_t* sa8 = reinterpret_cast<const uint8_t*>(sa);

@@ -55,7 +55,8 @@ def _random_mx(orc, seed, M, N, K, w_std=0.02):
     return qa, sa, qw, sw
 
 
-# Decode paths: M <= 64 with K % 2048 == 0 (scale rows up to 256 or up to 512 bytes) and not; M <= 128.
+# Decode paths: M <= 64 with K % 2048 == 0 (scale rows up to 256 or up to 512 bytes) and not; M <= 128 in two
+# 64-row halves (K % 2048 == 0, K <= 8192) and not.
 # Tile paths (M > 128): K % 512, % 256 or neither; 128-row tiles when there would be at most 160 tiles of
 # 256 rows, else 256 x 224 tiles when they take fewer rounds (1300 x 7000, 2600 x 4001, the prefill and
 # M = 2048 configurations), else 256 x 256.  Ragged M and N, several tiles.
@@ -65,7 +66,7 @@ SHAPES = [(1, 256, 128), (3, 100, 384), (16, 7168, 1024), (17, 33, 256), (37, 10
           (600, 1100, 2176), (257, 257, 128), (259, 1030, 256), (1000, 800, 4096), (777, 520, 768),
           (1, 256, 2048), (33, 520, 4096), (64, 100, 2048), (7, 300, 16384), (48, 77, 6144),
           (2200, 3896, 512), (2200, 3900, 1024), (40, 129, 16384), (64, 96, 10240),
-          (1300, 7000, 512), (2600, 4001, 512)]
+          (1300, 7000, 512), (2600, 4001, 512), (65, 520, 4096), (127, 1000, 8192), (96, 77, 2048)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
@@ -157,7 +158,7 @@ def test_a4w4_nan_scale_propagates(mx, orc):
 
 def test_a4w4_deterministic_and_guarded(mx, orc):
     import torch
-    for M, N, K in [(37, 1000, 1024), (300, 700, 1024)]:
+    for M, N, K in [(37, 1000, 1024), (100, 1000, 2048), (300, 700, 1024)]:
         qa, sa, qw, sw = _random_mx(orc, 77 + M, M, N, K)
         pad = 4096
         buf = torch.full((M * N + 2 * pad,), -12345.0, dtype=torch.bfloat16, device="cuda")
