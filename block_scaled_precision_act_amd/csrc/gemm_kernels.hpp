@@ -601,7 +601,8 @@ __global__ __launch_bounds__(256, KSMAX == 64 ? 2 : 1) void gemm_decode_fp4(cons
 }
 
 // ============================================================================
-// Decode path, FP8 (E4M3 codes, FP32 per-row scales; M <= 64, K % 512 == 0).
+// Decode path, FP8 (E4M3 codes, FP32 per-row scales; M <= 64, K % 512 == 0;
+// M <= 128 with two row halves, as in the FP4 decode kernel).
 // The FP4 decode design above on byte codes: one workgroup (4 waves) per 32
 // output columns, wave w owns a quarter of K and streams its K = 128 slabs
 // (128 code bytes per row: the 32*MF activation rows, then the 32 weight rows)
@@ -616,7 +617,9 @@ __global__ __launch_bounds__(256, KSMAX == 64 ? 2 : 1) void gemm_decode_fp4(cons
 namespace dec8 {
 constexpr int kNT = 32;             // output columns per workgroup
 constexpr int kSlab = 128;          // code bytes per row per slab (K = 128)
-template <int MF, int S>
+// RH: row halves, as in the FP4 decode kernel (RH = 2: waves 2h and 2h+1 share K half h, each with
+// its own 32 MF activation rows)
+template <int MF, int S, int RH = 1>
 struct Cfg {
     static constexpr int kArows = 32 * MF;
     static constexpr int kRows = kArows + kNT;              // activation rows, then weight rows
@@ -626,22 +629,25 @@ struct Cfg {
     static_assert(S * kCopies <= 63, "vmcnt");
     static_assert(kLds <= 160 * 1024, "LDS");
     static_assert(4 * MF * 16 * 64 * 4 <= kLds, "reduction staging");
+    static_assert(RH == 1 || RH == 2, "row halves");
 };
 }  // namespace dec8
 
-template <int MF, int S>
+template <int MF, int S, int RH = 1>
 __global__ __launch_bounds__(256, 1) void gemm_decode_fp8(const uint8_t* __restrict__ qa, const float* __restrict__ sa,
                                                           const uint8_t* __restrict__ qw, const float* __restrict__ sw,
                                                           uint16_t* __restrict__ y, int M, int N, int K) {
-    using C = dec8::Cfg<MF, S>;
+    using C = dec8::Cfg<MF, S, RH>;
     using namespace dec8;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[C::kLds];
     const int n0 = blockIdx.x * kNT;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l32 = lane & 31, h = lane >> 5;
-    const int nmine = K / 512;              // slabs per wave
-    const int s0 = wave * nmine;            // first slab of this wave
+    const int kq = wave / RH, rh = wave % RH;  // K part and row half of this wave
+    const int nmine = K * RH / 512;         // slabs per wave
+    const int s0 = kq * nmine;              // first slab of this wave
+    const int ra = rh * C::kArows;          // first activation row of this wave
     uint8_t* const ring = lds + wave * S * C::kSlabBytes;
 
     // code copies: copy i moves rows 8i .. 8i+7 (lane / 8) of the slab, the lane filling chunk
@@ -656,7 +662,7 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_fp8(const uint8_t* __restr
         const int r = 8 * i + (lane >> 3);
         const int chunk = (lane & 7) ^ ((r & 7) ^ ((r >> 3) & 1));
         if (r < C::kArows)
-            rowp[i] = 8 * i < M ? qa + (int64_t)min(r, M - 1) * K + 16 * chunk : qa;
+            rowp[i] = ra + 8 * i < M ? qa + (int64_t)min(ra + r, M - 1) * K + 16 * chunk : qa;
         else
             rowp[i] = qw + (int64_t)min(n0 + r - C::kArows, N - 1) * K + 16 * chunk;
     }
@@ -729,25 +735,26 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_fp8(const uint8_t* __restr
 #pragma unroll
         for (int r = 0; r < 16; ++r) red[((wave * MF + g) * 16 + r) * 64 + lane] = acc[g][r];
     __syncthreads();
-    // wave w finalizes register quad w of every fragment: D rows (n) 8w + 4h + e, column (m) l32
+    // wave w finalizes register quad w of every fragment of every row half: D rows (n) 8w + 4h + e,
+    // column (m) l32; the partials of K parts 0, 1, ... are added in that order
     const bool vec_ok = (N & 3) == 0 && (reinterpret_cast<uintptr_t>(y) & 7) == 0;
     const int n = n0 + 8 * wave + 4 * h;
     float swn[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) swn[e] = sw[min(n + e, N - 1)];
 #pragma unroll
-    for (int g = 0; g < MF; ++g) {
-        const int m = 32 * g + l32;
+    for (int fg = 0; fg < RH * MF; ++fg) {
+        const int half = fg / MF, g = fg % MF;
+        const int m = half * C::kArows + 32 * g + l32;
         if (m >= M) continue;
         const float sam = sa[m];
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = 4 * wave + e;
-            float t = red[((0 * MF + g) * 16 + r) * 64 + lane];
-            t += red[((1 * MF + g) * 16 + r) * 64 + lane];
-            t += red[((2 * MF + g) * 16 + r) * 64 + lane];
-            t += red[((3 * MF + g) * 16 + r) * 64 + lane];
+            float t = red[((half * MF + g) * 16 + r) * 64 + lane];
+#pragma unroll
+            for (int q = 1; q < 4 / RH; ++q) t += red[(((q * RH + half) * MF + g) * 16 + r) * 64 + lane];
             v[e] = t * sam * swn[e];
         }
         uint16_t* dst = y + (int64_t)m * N + n;
@@ -2237,6 +2244,11 @@ inline hipError_t launch_gemm(const void* qa, const void* sa, const void* qw, co
             hipLaunchKernelGGL((gemm_decode_fp8<1, 5>), grid, dim3(256), 0, st, a, sa32, w, sw32, out, m, n, k);
         else
             hipLaunchKernelGGL((gemm_decode_fp8<2, 3>), grid, dim3(256), 0, st, a, sa32, w, sw32, out, m, n, k);
+    } else if (FP8 && M <= 128 && K % 512 == 0) {
+        // two row halves of 64 rows (the per-wave slabs of the M = 64 kernel)
+        hipLaunchKernelGGL((gemm_decode_fp8<2, 3, 2>), dim3((unsigned)((N + dec8::kNT - 1) / dec8::kNT)), dim3(256),
+                           0, st, a, reinterpret_cast<const float*>(sa), w, reinterpret_cast<const float*>(sw), out, m,
+                           n, k);
     } else if (M <= 128) {
         const dim3 grid((unsigned)((N + 31) / 32));
         if (M <= 16)
