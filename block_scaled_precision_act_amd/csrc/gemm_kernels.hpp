@@ -474,9 +474,8 @@ __global__ __launch_bounds__(256, KSMAX == 64 ? 2 : 1) void gemm_decode_fp4(cons
     //    ds_read_b128 (32 four-byte banks) hit distinct banks, and so do 16 lanes over 64 banks.
     //    An activation copy whose 8 rows all lie at or past M reads one address in every lane (one
     //    cache line): those rows only
-    //    feed output columns that are never stored.  A batch for a slab past the wave's last one
-    //    also reads a single address (one line, data unused), so every wave issues the same
-    //    number of copies and the wait counts below are fixed.
+    //    feed output columns that are never stored.  Every wave issues the same copies (its nmine
+    //    slabs, each in one batch), so the wait counts below are fixed.
     const uint8_t* rowp[C::kCopies];
 #pragma unroll
     for (int i = 0; i < C::kCopies; ++i) {
@@ -528,11 +527,15 @@ __global__ __launch_bounds__(256, KSMAX == 64 ? 2 : 1) void gemm_decode_fp4(cons
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[g][r] = 0.f;
 
-    for (int j = 0; j < nmine; ++j) {
-        // slab j (and, for j = 0, the scale block) has landed once only the later S - 1 batches
-        // may still be in flight
+    // slab j; WAIT: the copies that may still be in flight (the later batches), REFILL: copy slab
+    // j + S into the slot once it is read.  The last S slabs refill nothing, so no wave waits for
+    // copies past its end before the reduction.  nmine >= S for every launch: K % 2048 == 0 gives
+    // nmine >= 2, and S = 4 runs only for K > 8192.
+    auto slab = [&](int j, auto WAIT, auto REFILL) {
+        // slab j (and, for j = 0, the scale block) has landed once only the later batches may
+        // still be in flight
         __builtin_amdgcn_sched_barrier(0);
-        wait_vmcnt<(S - 1) * C::kCopies>();
+        wait_vmcnt<decltype(WAIT)::value>();
         __builtin_amdgcn_sched_barrier(0);
         const uint32_t sb = rbase + (j % S) * C::kSlabBytes;
         uint32_t ws = scale_at(wsr, j);
@@ -548,7 +551,7 @@ __global__ __launch_bounds__(256, KSMAX == 64 ? 2 : 1) void gemm_decode_fp4(cons
         }
         lds_wait_dec<MF>(wv, xv, ws, xs);
         __builtin_amdgcn_sched_barrier(0);
-        issue(j + S);  // the slot is read: refill it
+        if constexpr (decltype(REFILL)::value) issue(j + S);  // the slot is read: refill it
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int g = 0; g < MF; ++g) {
@@ -557,7 +560,13 @@ __global__ __launch_bounds__(256, KSMAX == 64 ? 2 : 1) void gemm_decode_fp4(cons
             acc[g] = mfma32<kFmtFP4, 2>(fp4_operand(wv[2]), fp4_operand(xv[2][g]), acc[g], (int)ws, (int)xs[g]);
             acc[g] = mfma32<kFmtFP4, 3>(fp4_operand(wv[3]), fp4_operand(xv[3][g]), acc[g], (int)ws, (int)xs[g]);
         }
-    }
+    };
+    for (int j = 0; j < nmine - S; ++j)
+        slab(j, std::integral_constant<int, (S - 1) * C::kCopies>{}, std::true_type{});
+    static_for<S>([&](auto t) {
+        slab(nmine - S + decltype(t)::value, std::integral_constant<int, (S - 1 - decltype(t)::value) * C::kCopies>{},
+             std::false_type{});
+    });
 
     // 3. fixed-order reduction of the partial tiles (four per output, or two with RH = 2) through LDS
     wait_vmcnt<0>();  // the trailing refills
