@@ -706,10 +706,15 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_fp8(const uint8_t* __restr
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[g][r] = 0.f;
 
-    for (int j = 0; j < nmine; ++j) {
-        // slab j has landed once only the later S - 1 batches may still be in flight
+    // slab j; WAIT: the copies that may still be in flight, REFILL: copy slab j + S into the slot
+    // once it is read.  The last S slabs refill nothing, so the waits before the reduction find no
+    // copies past the end in flight, except when a wave has fewer slabs than slots (small K): the
+    // prologue's batches past the end then stay, the tail skips the missing slabs, and the waits
+    // it keeps count at most those batches too many (they only wait longer).
+    auto slab = [&](int j, auto WAIT, auto REFILL) {
+        // slab j has landed once only the later batches may still be in flight
         __builtin_amdgcn_sched_barrier(0);
-        wait_vmcnt<(S - 1) * C::kCopies>();
+        wait_vmcnt<decltype(WAIT)::value>();
         __builtin_amdgcn_sched_barrier(0);
         const uint32_t sb = rbase + (j % S) * C::kSlabBytes;
         v4u wv[4], xv[4][MF];
@@ -721,7 +726,7 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_fp8(const uint8_t* __restr
         }
         lds_wait_codes<MF>(wv, xv);
         __builtin_amdgcn_sched_barrier(0);
-        issue(j + S);  // the slot is read: refill it
+        if constexpr (decltype(REFILL)::value) issue(j + S);  // the slot is read: refill it
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -733,7 +738,14 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_fp8(const uint8_t* __restr
                 acc[g] = mfma32_f16(w1, e4m3x8_to_f16x8(xv[t][g][2], xv[t][g][3]), acc[g]);
             }
         }
-    }
+    };
+    for (int j = 0; j < nmine - S; ++j)
+        slab(j, std::integral_constant<int, (S - 1) * C::kCopies>{}, std::true_type{});
+    static_for<S>([&](auto t) {
+        const int j = nmine - S + decltype(t)::value;
+        if (j >= 0)
+            slab(j, std::integral_constant<int, (S - 1 - decltype(t)::value) * C::kCopies>{}, std::false_type{});
+    });
 
     // fixed-order reduction of the four partial tiles through LDS, then the row and column scales
     wait_vmcnt<0>();  // the trailing refills
