@@ -531,7 +531,7 @@ __global__ __launch_bounds__(256, KSMAX == 64 ? 2 : 1) void gemm_decode_fp4(cons
     // j + S into the slot once it is read.  The last S slabs refill nothing, so no wave waits for
     // copies past its end before the reduction.  nmine >= S for every launch: K % 2048 == 0 gives
     // nmine >= 2, and S = 4 runs only for K > 8192.
-    auto slab = [&](int j, auto WAIT, auto REFILL) {
+    auto slab = [&](int j, auto WAIT, auto REFILL) __attribute__((always_inline)) {
         // slab j (and, for j = 0, the scale block) has landed once only the later batches may
         // still be in flight
         __builtin_amdgcn_sched_barrier(0);
@@ -711,7 +711,7 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_fp8(const uint8_t* __restr
     // copies past the end in flight, except when a wave has fewer slabs than slots (small K): the
     // prologue's batches past the end then stay, the tail skips the missing slabs, and the waits
     // it keeps count at most those batches too many (they only wait longer).
-    auto slab = [&](int j, auto WAIT, auto REFILL) {
+    auto slab = [&](int j, auto WAIT, auto REFILL) __attribute__((always_inline)) {
         // slab j has landed once only the later batches may still be in flight
         __builtin_amdgcn_sched_barrier(0);
         wait_vmcnt<decltype(WAIT)::value>();
@@ -1363,7 +1363,13 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_fp4(const uint8_t* __restric
         __builtin_amdgcn_sched_barrier(0);                                                                         \
     }
 
-    for (int u = 0; u < nsup; ++u) {
+    // superstage u; WAIT: the copies that may still be in flight once those of u + 1 have landed,
+    // REFILL: issue the copies of u + S.  The last S superstages refill nothing, so neither their
+    // barriers nor the epilogue wait for copies past the end (128-row tiles).  With fewer
+    // superstages than slots (K = 512 at S = 4) the prologue's extra batches stay in flight, the
+    // missing steps are skipped, and the waits kept count at most those batches too many (they
+    // only wait longer).
+    auto step = [&](int u, auto WAIT, auto REFILL) __attribute__((always_inline)) {
         // in flight: scales + k-steps 0, 1 of u (LDS reads); the copies of u + 1
         lds_wait_first_n<FW>(r0w, r0x, wsc, xsc);  // scales and k-step 0
         __builtin_amdgcn_sched_barrier(0);
@@ -1375,7 +1381,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_fp4(const uint8_t* __restric
         lds_wait_n_of<0, FW>(r3w, r3x);
         // this wave's copies of u + 1 (and of the scale part) have landed; those of u + 2 .. u + S - 1
         // may still be in flight
-        wait_vmcnt<(C::kS - 2) * (C::kCodeCopies + C::kScPerWave)>();
+        wait_vmcnt<decltype(WAIT)::value>();
         __builtin_amdgcn_s_barrier();  // every wave: done reading u, copies of u + 1 complete
         __builtin_amdgcn_sched_barrier(0);
         uint32_t wsk[FW], xsk[FW];  // the scales of u, still needed for k-steps 2 and 3
@@ -1384,8 +1390,8 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_fp4(const uint8_t* __restric
             wsk[f] = wsc[f];
             xsk[f] = xsc[f];
         }
-        rd_scales(wsc, xsc, u + 1);  // past the end these read the repeated last superstage: unused
-        issue_scale(u + C::kS);
+        rd_scales(wsc, xsc, u + 1);  // past the end these read stale data: unused
+        if constexpr (decltype(REFILL)::value) issue_scale(u + C::kS);
         // k-steps 2 and 3 of u (2 FW^2 MFMAs), in this order, with the kCodeCopies copies of u + S and
         // the 4 FW operand reads of k-steps 0 and 1 of u + 1 spread between them (a wave keeps at most
         // 15 LDS reads in flight, so a burst of them would stall it)
@@ -1405,7 +1411,8 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_fp4(const uint8_t* __restric
                     else
                         acc[f][g] = mfma32<kFmtFP4, 3>(fp4_operand(r3w[f]), fp4_operand(r3x[g]), acc[f][g], (int)wsk[f],
                                                        (int)xsk[g]);
-                    if ((i % kEvery) == kEvery - 1 && i / kEvery < C::kCodeCopies) issue_code(u + C::kS, i / kEvery);
+                    if constexpr (decltype(REFILL)::value)
+                        if ((i % kEvery) == kEvery - 1 && i / kEvery < C::kCodeCopies) issue_code(u + C::kS, i / kEvery);
                     if ((i % kRdEvery) == kRdEvery - 1) {
                         const int ri = i / kRdEvery;
                         if (ri < 2 * FW) rd_one(r0w, r0x, u + 1, 0, ri);
@@ -1413,6 +1420,21 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_fp4(const uint8_t* __restric
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
+    };
+    constexpr int kBatch = C::kCodeCopies + C::kScPerWave;
+    if constexpr (TM == 256) {
+        // one call site: the peeled copies of the 256-row body no longer fit the registers (spills),
+        // so every superstage refills (past the end: copies of the last superstage, never read)
+        for (int u = 0; u < nsup; ++u) step(u, std::integral_constant<int, (C::kS - 2) * kBatch>{}, std::true_type{});
+    } else {
+        for (int u = 0; u < nsup - C::kS; ++u)
+            step(u, std::integral_constant<int, (C::kS - 2) * kBatch>{}, std::true_type{});
+        static_for<C::kS>([&](auto t) {
+            constexpr int T = decltype(t)::value;
+            const int u = nsup - C::kS + T;
+            if (u >= 0)
+                step(u, std::integral_constant<int, (C::kS - 2 - T > 0 ? C::kS - 2 - T : 0) * kBatch>{}, std::false_type{});
+        });
     }
 #undef MX_STEP_RD
     wait_vmcnt<0>();
@@ -1617,7 +1639,9 @@ __global__ __launch_bounds__(256, 1) void gemm_tile224_fp4(const uint8_t* __rest
     static_for<kRd>([&](auto ic) { rd_scale(wsc, xsc, sc_of(0) + wsrow0, sc_of(0) + xsrow0, ic); });
     static_for<kRd>([&](auto ic) { rd_one(r0w, r0x, slot_of(0) + wrow0 + ck0, slot_of(0) + xrow0 + ck0, ic); });
 
-    for (int u = 0; u < nsup; ++u) {
+    // superstage u; REFILL: issue the copies of u + 2 (the last two superstages have none to issue,
+    // so neither their barriers nor the epilogue wait for copies past the end)
+    auto step = [&](int u, auto REFILL) __attribute__((always_inline)) {
         // in flight: the scales and k-step 0 of u (LDS reads); the copies of u + 1
         lds_wait<0>();
         lds_tie(r0w);
@@ -1654,12 +1678,11 @@ __global__ __launch_bounds__(256, 1) void gemm_tile224_fp4(const uint8_t* __rest
         for (int j = 0; j < kFA; ++j) xsk[j] = xsc[j];
         lds_tie(wsk);  // the copies (VALU) are done here ...
         lds_tie(xsk);
-        issue_scale(u + 2);
+        if constexpr (decltype(REFILL)::value) issue_scale(u + 2);
         wait_states8<1>();  // ... and some wait states before an MFMA reads them
         __builtin_amdgcn_sched_barrier(0);
         // k-step 1, with the kCodeCopies copies of u + 2 and the 2 kRd reads (scales, then k-step 0)
-        // of u + 1 spread between the MFMAs; past the end these read the repeated last superstage,
-        // never used
+        // of u + 1 spread between the MFMAs; past the end these read stale slot data, never used
         // k-step 1 (activation-fragment-major), with the copies of u + 2 and the reads of u + 1 between
         // the MFMAs: the 15 scales first, the weight fragments (fresh registers), then activation
         // fragment j once column j has read r1x[j] (two MFMAs later), j = 7 early
@@ -1670,7 +1693,8 @@ __global__ __launch_bounds__(256, 1) void gemm_tile224_fp4(const uint8_t* __rest
                 constexpr int i = decltype(ic)::value, j = i / kFW, f = i % kFW;
                 mfma16_fp4_agpr<1>(acc[f][j], r1w[f], r1x[j], wsk[f], xsk[j]);
                 static_for<kCodeCopies>([&](auto cc) {
-                    if constexpr ((decltype(cc)::value * kMf) / kCodeCopies == i) issue_code(u + 2, decltype(cc)::value);
+                    if constexpr (decltype(REFILL)::value && (decltype(cc)::value * kMf) / kCodeCopies == i)
+                        issue_code(u + 2, decltype(cc)::value);
                 });
                 static_for<kRd>([&](auto rc) {
                     if constexpr (decltype(rc)::value == i) rd_scale(wsc, xsc, wsb, xsb, rc);
@@ -1683,7 +1707,10 @@ __global__ __launch_bounds__(256, 1) void gemm_tile224_fp4(const uint8_t* __rest
                 __builtin_amdgcn_sched_barrier(0);
             });
         }
-    }
+    };
+    for (int u = 0; u < nsup - 2; ++u) step(u, std::true_type{});
+    if (nsup >= 2) step(nsup - 2, std::false_type{});
+    step(nsup - 1, std::false_type{});
     wait_vmcnt<0>();
     lds_wait<0>();
     lds_tie(r0w);
@@ -2106,7 +2133,9 @@ __global__ __launch_bounds__(256, 1) void gemm_tile224_fp8(const uint8_t* __rest
     static_assert(kFW % 2 == 1 && kFA == kFW + 1, "the operand schedule assumes 7 x 8 fragments");
     auto none = [](auto) {};
 
-    for (int u = 0; u < nsup; ++u) {
+    // superstage u; REFILL: issue the copies of u + 2 (the last two superstages have none to issue,
+    // so neither their barriers nor the epilogue wait for copies past the end)
+    auto step = [&](int u, auto REFILL) __attribute__((always_inline)) {
         // read step 0 (chunk 2g): k-step (0, 0) from xa, widening (0, 1) into xb_; k-step (0, 1) from
         // xb_, widening (1, 0) into xa once the reads of read step 1 are in.  The reads of read step 1
         // go out during k-step (0, 0).
@@ -2133,7 +2162,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tile224_fp8(const uint8_t* __rest
         __builtin_amdgcn_sched_barrier(0);
         // read step 1 (chunk 2g + 1): k-step (1, 0) from xa, widening (1, 1) into xb_, with the copies
         // of u + 2 and the reads of read step 0 of u + 1; k-step (1, 1) from xb_, widening (0, 0) of
-        // u + 1 into xa (past the end these read the repeated last superstage, never used)
+        // u + 1 into xa (past the end these read stale slot data, never used)
         {
             const uint32_t wb = slot_of(u + 1) + wrow0 + ck0, xb = slot_of(u + 1) + xrow0 + ck0;
             kstep(xa, xb_, r1w, r1w, r1x, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{},
@@ -2141,7 +2170,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tile224_fp8(const uint8_t* __rest
                   [&](auto ic) {
                       constexpr int i = decltype(ic)::value;
                       static_for<kCodeCopies>([&](auto cc) {
-                          if constexpr ((decltype(cc)::value * kMf) / kCodeCopies == i)
+                          if constexpr (decltype(REFILL)::value && (decltype(cc)::value * kMf) / kCodeCopies == i)
                               issue_code(u + 2, decltype(cc)::value);
                       });
                       static_for<kRd>([&](auto rc) {
@@ -2155,7 +2184,10 @@ __global__ __launch_bounds__(256, 1) void gemm_tile224_fp8(const uint8_t* __rest
         __builtin_amdgcn_sched_barrier(0);
         kstep(xb_, xa, r1w, r0w, r0x, std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{},
               std::integral_constant<int, 1>{}, none);
-    }
+    };
+    for (int u = 0; u < nsup - 2; ++u) step(u, std::true_type{});
+    if (nsup >= 2) step(nsup - 2, std::false_type{});  // K = 128: one superstage
+    step(nsup - 1, std::false_type{});
     wait_vmcnt<0>();
     wait_states8<3>();  // last MFMA -> reads of the accumulators (tied here, so none moves above)
 #pragma unroll
