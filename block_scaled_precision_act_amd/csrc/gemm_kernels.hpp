@@ -8,7 +8,7 @@
 //   FP8 (A8W8): A, W are E4M3 codes with one FP32 scale per row
 //     ("Kimi-K3-DSpark-FP8-PTPC", section "Phase 1 FP8 PTPC Quantization").
 //     The codes are widened exactly to FP16 in registers and multiplied with
-//     FP16 MFMAs; the epilogue multiplies by sA[m] * sW[n].  (gfx950's FP8
+//     FP16 MFMAs; the epilogue multiplies by sA[m] * sW[n] in FP64.  (gfx950's FP8
 //     MFMA sums each group of 8 products with a short internal adder - a
 //     small product next to a large one in the same group is dropped - which
 //     misses the 1e-6 * sum|a*w| accuracy this layer is held to; its FP16 and
@@ -180,7 +180,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(const uint8_t* __r
         const int m = 16 * i + 4 * (l >> 4) + r, n = n0 + 16 * j + (l & 15);
         if (m < M && n < N) {
             if constexpr (FP8)
-                sum = sum * reinterpret_cast<const float*>(sa_)[m] * reinterpret_cast<const float*>(sw_)[n];
+                sum = ptpc_scaled(sum, reinterpret_cast<const float*>(sa_)[m], reinterpret_cast<const float*>(sw_)[n]);
             y[(int64_t)m * N + n] = (uint16_t)bf16_rne(sum);
         }
     }
@@ -621,7 +621,7 @@ __global__ __launch_bounds__(256, KSMAX == 64 ? 2 : 1) void gemm_decode_fp4(cons
 // operands (every E4M3 value is an FP16 normal) for v_mfma_f32_32x32x16_f16:
 // lane group h takes chunks 4h .. 4h+3, chunk 4h+t half u feeding k-step
 // (t, u) of both operands.  The four partial tiles are summed through LDS in a
-// fixed order; the epilogue applies (sum * sA[m]) * sW[n] and rounds to BF16.
+// fixed order; the epilogue applies sum * sA[m] * sW[n] (in FP64) and rounds to BF16.
 // ============================================================================
 namespace dec8 {
 constexpr int kNT = 32;             // output columns per workgroup
@@ -776,7 +776,7 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_fp8(const uint8_t* __restr
             float t = red[((half * MF + g) * 16 + r) * 64 + lane];
 #pragma unroll
             for (int q = 1; q < 4 / RH; ++q) t += red[(((q * RH + half) * MF + g) * 16 + r) * 64 + lane];
-            v[e] = t * sam * swn[e];
+            v[e] = ptpc_scaled(t, sam, swn[e]);
         }
         uint16_t* dst = y + (int64_t)m * N + n;
         if (vec_ok && n + 3 < N) {
@@ -979,7 +979,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(const uint8_t* __rest
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     v[e] = acc[f][g][4 * j + e];
-                    if constexpr (FP8) v[e] = v[e] * sxm * reinterpret_cast<const float*>(sw_)[min(n + e, N - 1)];
+                    if constexpr (FP8) v[e] = ptpc_scaled(v[e], sxm, reinterpret_cast<const float*>(sw_)[min(n + e, N - 1)]);
                 }
                 if (vec_ok && n + 3 < N) {
                     uint2 pk;
@@ -1942,7 +1942,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_fp8(const uint8_t* __restric
                 const int nl = 128 * wn + 32 * f + 8 * j + 4 * h;
                 float v[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = acc[f][g][4 * j + e] * sxm * swv[f][j][e];
+                for (int e = 0; e < 4; ++e) v[e] = ptpc_scaled(acc[f][g][4 * j + e], sxm, swv[f][j][e]);
                 uint2 pk;
                 pk.x = bf16x2_rne(v[0], v[1]);
                 pk.y = bf16x2_rne(v[2], v[3]);
@@ -2197,7 +2197,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tile224_fp8(const uint8_t* __rest
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
 
-    // Epilogue through LDS: (acc * sA[m]) * sW[n] rounded to BF16, each lane 4 consecutive n of one
+    // Epilogue through LDS: acc * sA[m] * sW[n] (in FP64) rounded to BF16, each lane 4 consecutive n of one
     // m per fragment pair; then whole 448-byte tile rows.
     float sxm[kFA];
 #pragma unroll
@@ -2213,7 +2213,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tile224_fp8(const uint8_t* __rest
             const int ml = (kTM / 2) * wm + 16 * j + l16;
             float v[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = acc[f][j][e] * sxm[j] * swn[e];
+            for (int e = 0; e < 4; ++e) v[e] = ptpc_scaled(acc[f][j][e], sxm[j], swn[e]);
             uint2 pk;
             pk.x = bf16x2_rne(v[0], v[1]);
             pk.y = bf16x2_rne(v[2], v[3]);

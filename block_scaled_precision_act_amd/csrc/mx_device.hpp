@@ -93,6 +93,14 @@ __device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2));
 }
 
+// PTPC epilogue value acc * sa * sw: the FP32 sum and the two FP32 scales are multiplied in FP64,
+// where the scale product is exact and nothing over- or underflows, then rounded to FP32 once (the
+// caller rounds that to BF16).  In FP32 the product of the three could overflow or underflow part
+// way although the result is an ordinary number (a 2^118 row scale against a 2^-60 column scale).
+__device__ __forceinline__ float ptpc_scaled(float acc, float sa, float sw) {
+    return (float)((double)acc * ((double)sa * (double)sw));
+}
+
 // 16 bytes per lane from global memory straight into LDS: lane i of the wave writes
 // lds_base + 16 * i (lds_base must be the same for the whole wave).
 __device__ __forceinline__ void g2lds16(const void* g, void* lds_base) {

@@ -134,6 +134,24 @@ def _need(t, dtype, ndim, name):
         raise ValueError("%s must be contiguous" % name)
 
 
+def _out(t, dtype, shape, like, name):
+    """A caller-supplied output: checked like an input, plus its exact shape and device, since the
+    kernels write shape-many elements through its pointer.  None allocates a fresh one."""
+    torch = _torch()
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=like.device)
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    _need(t, dtype, len(shape), name)
+    if t.device != like.device:
+        raise ValueError("%s must be on %s, got %s" % (name, like.device, t.device))
+    return t
+
+
 def _ok(status, where):
     if status != MX_SUCCESS:
         raise MxError(status, where)
@@ -144,8 +162,8 @@ def quant_act_mx(x, q=None, s=None):
     torch = _torch()
     _need(x, torch.bfloat16, 2, "x")
     M, K = x.shape
-    q = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device) if q is None else q
-    s = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device) if s is None else s
+    q = _out(q, torch.uint8, (M, K // 2), x, "q")
+    s = _out(s, torch.uint8, (M, K // 32), x, "s")
     _ok(mx_quant_act_bf16(x.data_ptr(), M, K, q.data_ptr(), s.data_ptr(), _stream()), "mx_quant_act_bf16")
     return q, s
 
@@ -170,7 +188,7 @@ def gemm_a4w4(qa, sa, qw, sw, y=None):
     N = qw.shape[0]
     if qw.shape[1] * 2 != K or sa.shape != (M, K // 32) or sw.shape != (N, K // 32):
         raise ValueError("inconsistent A4W4 operand shapes")
-    y = torch.empty((M, N), dtype=torch.bfloat16, device=qa.device) if y is None else y
+    y = _out(y, torch.bfloat16, (M, N), qa, "y")
     ws = mx_gemm_a4w4_workspace_bytes(M, N, K)
     wbuf = torch.empty(ws, dtype=torch.uint8, device=qa.device) if ws else None
     _ok(mx_gemm_a4w4_bf16(qa.data_ptr(), sa.data_ptr(), qw.data_ptr(), sw.data_ptr(), y.data_ptr(), M, N, K,
@@ -193,7 +211,7 @@ def gemm_a4w4_grouped(qa, sa, qw, sw, offsets, max_rows, y=None):
     if (qw.shape[2] * 2 != K or sa.shape != (T, K // 32) or sw.shape != (G, N, K // 32)
             or offsets.shape[0] != G + 1):
         raise ValueError("inconsistent grouped A4W4 operand shapes")
-    y = torch.empty((T, N), dtype=torch.bfloat16, device=qa.device) if y is None else y
+    y = _out(y, torch.bfloat16, (T, N), qa, "y")
     _ok(mx_gemm_a4w4_grouped_bf16(qa.data_ptr(), sa.data_ptr(), qw.data_ptr(), sw.data_ptr(), y.data_ptr(),
                                   offsets.data_ptr(), G, max_rows, N, K, _stream()), "mx_gemm_a4w4_grouped_bf16")
     return y
@@ -238,7 +256,7 @@ def gemm_a8w8(qa, sa, qw, sw, y=None):
     N = qw.shape[0]
     if qw.shape[1] != K or sa.shape[0] != M or sw.shape[0] != N:
         raise ValueError("inconsistent A8W8 operand shapes")
-    y = torch.empty((M, N), dtype=torch.bfloat16, device=qa.device) if y is None else y
+    y = _out(y, torch.bfloat16, (M, N), qa, "y")
     _ok(gemm_a8w8_ptpc_bf16(qa.data_ptr(), sa.data_ptr(), qw.data_ptr(), sw.data_ptr(), y.data_ptr(), M, N, K,
                             _stream()), "gemm_a8w8_ptpc_bf16")
     return y

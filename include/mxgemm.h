@@ -35,7 +35,10 @@
  *       PTPC row: a = max|x|, s = fl32(a / 448) (s = 1 when a == 0),
  *       code = E4M3fn round-to-nearest-even of fl32(x / s), saturating at 448;
  *       a row with NaN/Inf gets s = NaN and every code 0x7F.
- *       GEMMs accumulate in FP32 and round the result to BF16 (nearest even).
+ *       GEMMs accumulate in FP32 and round the result to BF16 (nearest even):
+ *       a result beyond BF16's finite range becomes +-inf, one in or below its
+ *       subnormal range rounds gradually (to +-0 below 2^-134).  The A8W8
+ *       epilogue multiplies the FP32 sum by both FP32 scales in FP64.
  *   - Errors: argument errors are detected on the host before anything is
  *     enqueued and returned as an mx_status; a launch failure returns
  *     MX_ERROR_LAUNCH.  Faults during asynchronous execution surface on the

@@ -113,3 +113,19 @@ def test_tensor_helpers_reject_bad_inputs_before_the_library(mx):
         mx.quant_act_mx(torch.zeros(2, 64, dtype=torch.float32))
     with pytest.raises(ValueError):
         mx.quant_act_mx(torch.zeros(2, 64, dtype=torch.bfloat16))  # not a device tensor
+
+
+def test_tensor_helpers_reject_bad_outputs(mx):
+    """A caller-supplied output of the wrong dtype, shape, device or layout is refused before its
+    pointer reaches a kernel (the kernels write shape-many elements through it)."""
+    import torch
+    like = torch.zeros(2, 64, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        mx._out(torch.zeros(2, 32, dtype=torch.float32), torch.uint8, (2, 32), like, "q")
+    with pytest.raises(ValueError, match="shape"):
+        mx._out(torch.zeros(2, 31, dtype=torch.uint8), torch.uint8, (2, 32), like, "q")
+    with pytest.raises(ValueError, match="shape"):
+        mx._out(torch.zeros(64, 2, dtype=torch.bfloat16), torch.bfloat16, (2, 64), like, "y")
+    with pytest.raises(ValueError, match="device"):
+        mx._out(torch.zeros(2, 32, dtype=torch.uint8), torch.uint8, (2, 32), like, "q")   # host memory
+    assert mx._out(None, torch.uint8, (2, 32), like, "q").shape == (2, 32)

@@ -66,7 +66,10 @@ SHAPES = [(1, 256, 128), (3, 100, 384), (16, 7168, 1024), (17, 33, 256), (37, 10
           (600, 1100, 2176), (257, 257, 128), (259, 1030, 256), (1000, 800, 4096), (777, 520, 768),
           (1, 256, 2048), (33, 520, 4096), (64, 100, 2048), (7, 300, 16384), (48, 77, 6144),
           (2200, 3896, 512), (2200, 3900, 1024), (40, 129, 16384), (64, 96, 10240),
-          (1300, 7000, 512), (2600, 4001, 512), (65, 520, 4096), (127, 1000, 8192), (96, 77, 2048)]
+          (1300, 7000, 512), (2600, 4001, 512), (65, 520, 4096), (127, 1000, 8192), (96, 77, 2048),
+          # the 512-K LDS-staged decode kernel at 17..32 and 65..128 rows (K % 2048 != 0, or K > 8192), and
+          # the register-staged decode kernel at 33..64 and 65..128 rows (K % 512 != 0), e.g. a 7168-wide input
+          (24, 300, 7168), (100, 300, 7168), (100, 77, 10240), (48, 100, 384), (100, 100, 640)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
