@@ -168,7 +168,8 @@ class A4W4Layer:
         self.sa = [torch.empty((M, K // 32), dtype=torch.uint8, device=ctx.dev) for _ in range(rotate)]
         self.y = [torch.empty((M, N), dtype=torch.bfloat16, device=ctx.dev) for _ in range(rotate)]
         self.ws = mx.mx_gemm_a4w4_workspace_bytes(M, N, K)  # shared by the steps (they run in stream order)
-        self.wbuf = torch.empty(max(self.ws, 16), dtype=torch.uint8, device=ctx.dev)
+        # zero-filled once; every call leaves its counters at zero again
+        self.wbuf = torch.zeros(max(self.ws, 16), dtype=torch.uint8, device=ctx.dev)
 
     def quant(self, r):
         mx, ctx = self.ctx.mx, self.ctx
@@ -184,6 +185,16 @@ class A4W4Layer:
     def step(self, r):
         q, g = self.quant(r), self.gemm(r)
         return lambda: (q(), g())
+
+    def fused(self, r):
+        """The same layer through the one-call entry (BF16 X in, BF16 Y out)."""
+        mx, ctx = self.ctx.mx, self.ctx
+        if not hasattr(self, "lws"):
+            self.lws = mx.mx_linear_a4w4_workspace_bytes(self.M, self.N, self.K)
+            self.lbuf = ctx.torch.zeros(max(self.lws, 256), dtype=ctx.torch.uint8, device=ctx.dev)
+        return lambda: ok(mx.mx_linear_a4w4_bf16(self.x[r].data_ptr(), self.qw[r].data_ptr(), self.sw[r].data_ptr(),
+                                                 self.y[r].data_ptr(), self.M, self.N, self.K, self.lbuf.data_ptr(),
+                                                 self.lws, ctx.stream()), "mx_linear_a4w4_bf16")
 
 
 class A8W8Layer:
@@ -327,6 +338,27 @@ def layer_entry(ctx, layer, kind, args, label):
         e["gemm"]["note"] = ("E4M3 operands widened exactly to FP16 and run on FP16 MFMA (peak %.0f TFLOP/s); "
                              "frac is against the FP8 peak" % PEAK_FP16_TFLOPS)
     return e
+
+
+def one_call_layer_entry(ctx, args):
+    """The one-call A4W4 layer (mx_linear_a4w4_bf16: one kernel at these sizes, quantizing X inside the
+    GEMM's workgroups) beside the two-launch layer (quantizer + GEMM), o_proj weight, M = 1, 16, 64."""
+    out = {}
+    for Ms in (1, 16, 64):
+        lay = make_a4w4(ctx, "oproj_decode_a4w4", M=Ms)
+        one_ms = kernel_ms(ctx, lay, "fused", args.kernel_reps)
+        two_ms = kernel_ms(ctx, lay, "step", args.kernel_reps)
+        # algorithmic bytes of the layer: BF16 X in, the MXFP4 weight and its scales in, BF16 Y out
+        byt = 2 * Ms * lay.K + lay.N * lay.K // 2 + lay.N * lay.K // 32 + 2 * Ms * lay.N
+        gbs = byt / (one_ms * 1e-3) / 1e9
+        out["M=%d" % Ms] = {"one_call_us": round(one_ms * 1e3, 3), "two_launch_us": round(two_ms * 1e3, 3),
+                            "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "frac": round(gbs / PEAK_HBM_GBS, 4), "alg_bytes_per_launch": byt}
+        del lay
+        ctx.torch.cuda.empty_cache()
+    return {"workload": "A4W4 o_proj layer BF16 X [M, 8192] -> BF16 Y [M, 7168], W [7168, 8192] MXFP4; "
+                        "one call (quantization inside the split-K GEMM) vs quantizer + GEMM, graph-replayed, "
+                        "rotated copies", "by_M": out}
 
 
 def weight_conversion_entry(ctx, args):
@@ -579,6 +611,8 @@ def main():
             also[name] = layer_entry(ctx, lay, "a8w8", args, name)
             del lay
             torch.cuda.empty_cache()
+        log("one-call layer")
+        also["a4w4_one_call_layer"] = one_call_layer_entry(ctx, args)
         log("offline weight conversion")
         also["weight_conversion"] = weight_conversion_entry(ctx, args)
         log("grouped MoE A4W4")

@@ -107,6 +107,27 @@ MX_API mx_status mx_gemm_a4w4_bf16(const void* qa, const void* sa, const void* q
     return launched(mx::launch_gemm_a4w4(qa, sa, qw, sw, y_bf16, M, N, K, workspace, reinterpret_cast<hipStream_t>(stream)));
 }
 
+MX_API size_t mx_linear_a4w4_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (check_gemm(M, N, K) != MX_SUCCESS || M == 0 || N == 0) return 0;
+    return mx::linear_a4w4_workspace_bytes(M, N, K);
+}
+
+MX_API mx_status mx_linear_a4w4_bf16(const void* x_bf16, const void* qw, const void* sw, void* y_bf16, int64_t M,
+                                     int64_t N, int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
+    mx_status st = check_gemm(M, N, K);
+    if (st != MX_SUCCESS) return st;
+    if (M == 0 || N == 0) return MX_SUCCESS;
+    if (!x_bf16 || !qw || !sw || !y_bf16) return MX_ERROR_INVALID_VALUE;
+    const size_t need = mx_linear_a4w4_workspace_bytes(M, N, K);
+    if (workspace_bytes < need || (need && !workspace)) return MX_ERROR_WORKSPACE;
+    if (!aligned(x_bf16, 16) || !aligned(qw, 16) || !aligned(sw, 4) || !aligned(y_bf16, 2) ||
+        (need && !aligned(workspace, 256)))
+        return MX_ERROR_MISALIGNED;
+    if ((st = check_device()) != MX_SUCCESS) return st;
+    return launched(mx::launch_linear_a4w4(x_bf16, qw, sw, y_bf16, M, N, K, workspace,
+                                           reinterpret_cast<hipStream_t>(stream)));
+}
+
 MX_API mx_status mx_gemm_a4w4_grouped_bf16(const void* qa, const void* sa, const void* qw, const void* sw,
                                            void* y_bf16, const int32_t* offsets, int64_t G, int64_t max_rows,
                                            int64_t N, int64_t K, void* stream) {

@@ -18,6 +18,10 @@ hipError_t launch_quant_ptpc_f32(const void* x, int64_t rows, int64_t K, void* q
 hipError_t launch_gemm_a4w4(const void* qa, const void* sa, const void* qw, const void* sw, void* y,
                             int64_t M, int64_t N, int64_t K, void* workspace, hipStream_t st);
 size_t gemm_a4w4_workspace_bytes(int64_t M, int64_t N, int64_t K);
+// One-launch A4W4 layer: BF16 X -> MXFP4 (inside the GEMM's workgroups) -> BF16 Y.
+hipError_t launch_linear_a4w4(const void* x, const void* qw, const void* sw, void* y, int64_t M, int64_t N, int64_t K,
+                              void* workspace, hipStream_t st);
+size_t linear_a4w4_workspace_bytes(int64_t M, int64_t N, int64_t K);
 // Grouped A4W4 GEMM over MoE experts (decode-sized groups, see mx_gemm_a4w4_grouped_bf16).
 hipError_t launch_a4w4_grouped(const void* qa, const void* sa, const void* qw, const void* sw, void* y,
                                const int32_t* offsets, int64_t G, int64_t max_rows, int64_t N, int64_t K,

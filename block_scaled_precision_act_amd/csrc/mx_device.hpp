@@ -275,30 +275,39 @@ __device__ __forceinline__ void lds_wait_n_of(v4u (&a)[FW], v4u (&b)[FW]) {
 // codes if the block holds a NaN or an infinity.  The codes come from gfx950's scaled conversion,
 // which divides by the power-of-two scale and rounds to the nearest E2M1 value, ties to the even
 // code, saturating at 6 and keeping the sign.
+// Largest biased exponent field of eight BF16 values (one 16-byte piece of a block).
+__device__ __forceinline__ uint32_t bf16x8_emax(uint4 x) {
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    uint32_t emax = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) emax = max(emax, max((w[j] >> 7) & 0xffu, (w[j] >> 23) & 0xffu));
+    return emax;
+}
+// E8M0 scale byte of a block from its largest exponent field: max(E - 2, 0), 0xFF for NaN/Inf.
+__device__ __forceinline__ uint32_t mx_scale_of_emax(uint32_t emax) {
+    return emax == 0xffu ? 0xffu : (emax > 2u ? emax - 2u : 0u);
+}
+// Eight BF16 values -> eight E2M1 codes (value 2j in the low nibble of byte j) at scale byte `scale`
+// (not 0xFF): gfx950's scaled conversion divides by 2^(scale - 127), an FP32 bit pattern that is
+// subnormal for scale bytes 0 and 1, and rounds to the nearest E2M1 value (ties to the even code,
+// saturating at 6, sign kept).
+__device__ __forceinline__ uint32_t bf16x8_codes(uint4 x, uint32_t scale) {
+    const float sc = __uint_as_float(scale ? scale << 23 : 1u << 22);  // 2^(scale - 127)
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    uint32_t v = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(0u, __builtin_bit_cast(bf2, x.x), sc, 0);
+    v = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(v, __builtin_bit_cast(bf2, x.y), sc, 1);
+    v = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(v, __builtin_bit_cast(bf2, x.z), sc, 2);
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(v, __builtin_bit_cast(bf2, x.w), sc, 3);
+}
+
 __device__ __forceinline__ uint4 mx_bf16x32_codes(const uint4 (&x)[4], uint32_t& scale) {
     uint32_t emax = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t w[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) emax = max(emax, max((w[j] >> 7) & 0xffu, (w[j] >> 23) & 0xffu));
-    }
-    if (emax == 0xffu) {  // NaN or Inf in the block
-        scale = 0xffu;
-        return make_uint4(0u, 0u, 0u, 0u);
-    }
-    scale = emax > 2u ? emax - 2u : 0u;
-    const float sc = __uint_as_float(scale ? scale << 23 : 1u << 22);  // 2^(scale - 127)
-    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-    uint32_t c[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        uint32_t v = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(0u, __builtin_bit_cast(bf2, x[i].x), sc, 0);
-        v = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(v, __builtin_bit_cast(bf2, x[i].y), sc, 1);
-        v = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(v, __builtin_bit_cast(bf2, x[i].z), sc, 2);
-        c[i] = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(v, __builtin_bit_cast(bf2, x[i].w), sc, 3);
-    }
-    return make_uint4(c[0], c[1], c[2], c[3]);
+    for (int i = 0; i < 4; ++i) emax = max(emax, bf16x8_emax(x[i]));
+    scale = mx_scale_of_emax(emax);
+    if (scale == 0xffu) return make_uint4(0u, 0u, 0u, 0u);  // NaN or Inf in the block
+    return make_uint4(bf16x8_codes(x[0], scale), bf16x8_codes(x[1], scale), bf16x8_codes(x[2], scale),
+                      bf16x8_codes(x[3], scale));
 }
 
 __device__ __forceinline__ uint4 ldg16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }

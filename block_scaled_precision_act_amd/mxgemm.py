@@ -64,6 +64,10 @@ def lib() -> ctypes.CDLL:
         L.gemm_a8w8_ptpc_bf16.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
         L.gemm_a8w8_ptpc_bf16.restype = i32
         L.mx_gemm_a4w4_grouped_bf16.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp]
+        L.mx_linear_a4w4_workspace_bytes.argtypes = [i64, i64, i64]
+        L.mx_linear_a4w4_workspace_bytes.restype = ctypes.c_size_t
+        L.mx_linear_a4w4_bf16.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, ctypes.c_size_t, vp]
+        L.mx_linear_a4w4_bf16.restype = i32
         L.mx_gemm_a4w4_grouped_bf16.restype = i32
         _lib = L
     return _lib
@@ -92,6 +96,14 @@ def mx_gemm_a4w4_workspace_bytes(M, N, K) -> int:
 
 def mx_gemm_a4w4_bf16(qa, sa, qw, sw, y, M, N, K, workspace=None, workspace_bytes=0, stream=None) -> int:
     return lib().mx_gemm_a4w4_bf16(qa, sa, qw, sw, y, M, N, K, workspace, workspace_bytes, stream)
+
+
+def mx_linear_a4w4_workspace_bytes(M, N, K) -> int:
+    return lib().mx_linear_a4w4_workspace_bytes(M, N, K)
+
+
+def mx_linear_a4w4_bf16(x, qw, sw, y, M, N, K, workspace=None, workspace_bytes=0, stream=None) -> int:
+    return lib().mx_linear_a4w4_bf16(x, qw, sw, y, M, N, K, workspace, workspace_bytes, stream)
 
 
 def mx_gemm_a4w4_grouped_bf16(qa, sa, qw, sw, y, offsets, G, max_rows, N, K, stream=None) -> int:
@@ -152,6 +164,21 @@ def _out(t, dtype, shape, like, name):
     return t
 
 
+_workspaces = {}
+
+
+def _workspace(device, nbytes):
+    """A zero-filled GEMM workspace of at least nbytes, kept per (device, stream): the library
+    leaves it zero-filled after every call, and calls on one stream never overlap."""
+    torch = _torch()
+    key = (device, _stream())
+    buf = _workspaces.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _workspaces[key] = buf
+    return buf
+
+
 def _ok(status, where):
     if status != MX_SUCCESS:
         raise MxError(status, where)
@@ -190,7 +217,7 @@ def gemm_a4w4(qa, sa, qw, sw, y=None):
         raise ValueError("inconsistent A4W4 operand shapes")
     y = _out(y, torch.bfloat16, (M, N), qa, "y")
     ws = mx_gemm_a4w4_workspace_bytes(M, N, K)
-    wbuf = torch.empty(ws, dtype=torch.uint8, device=qa.device) if ws else None
+    wbuf = _workspace(qa.device, ws) if ws else None
     _ok(mx_gemm_a4w4_bf16(qa.data_ptr(), sa.data_ptr(), qw.data_ptr(), sw.data_ptr(), y.data_ptr(), M, N, K,
                           wbuf.data_ptr() if ws else None, ws, _stream()), "mx_gemm_a4w4_bf16")
     return y
@@ -218,9 +245,27 @@ def gemm_a4w4_grouped(qa, sa, qw, sw, offsets, max_rows, y=None):
 
 
 def linear_a4w4(x, qw, sw):
-    """The A4W4 layer: dynamic MXFP4 quantization of BF16 x, then the block-scaled GEMM."""
+    """The A4W4 layer in two launches: dynamic MXFP4 quantization of BF16 x, then the block-scaled GEMM."""
     qa, sa = quant_act_mx(x)
     return gemm_a4w4(qa, sa, qw, sw)
+
+
+def linear_a4w4_fused(x, qw, sw, y=None):
+    """The A4W4 layer through mx_linear_a4w4_bf16: BF16 x [M, K] -> BF16 Y [M, N], one launch at decode sizes."""
+    torch = _torch()
+    _need(x, torch.bfloat16, 2, "x")
+    _need(qw, torch.uint8, 2, "qw")
+    _need(sw, torch.uint8, 2, "sw")
+    M, K = x.shape
+    N = qw.shape[0]
+    if qw.shape[1] * 2 != K or sw.shape != (N, K // 32):
+        raise ValueError("inconsistent A4W4 layer shapes")
+    y = _out(y, torch.bfloat16, (M, N), x, "y")
+    ws = mx_linear_a4w4_workspace_bytes(M, N, K)
+    wbuf = _workspace(x.device, ws) if ws else None
+    _ok(mx_linear_a4w4_bf16(x.data_ptr(), qw.data_ptr(), sw.data_ptr(), y.data_ptr(), M, N, K,
+                            wbuf.data_ptr() if ws else None, ws, _stream()), "mx_linear_a4w4_bf16")
+    return y
 
 
 def quant_act_ptpc(x):

@@ -93,9 +93,17 @@ mx_status mx_quant_weight_f32(const float *w, int64_t N, int64_t K,
                               void *q, void *s, void *stream);
 
 /*
- * Bytes of workspace mx_gemm_a4w4_bf16 needs for this shape (currently 0 for
- * every shape; callers that pass the queried size stay correct if a later
- * version needs one).
+ * Bytes of workspace mx_gemm_a4w4_bf16 needs for this shape: nonzero for the
+ * decode sizes that split K across workgroups - M <= 64, 32-column tiles that
+ * would fill at most half the GPU (N <= 4096), K split into 4 or 8 parts of
+ * 2048 K-values giving at least 128 workgroups of 128 columns; e.g. 4,198,400
+ * bytes for (64, 4096, 8192) - and 0 otherwise (the (64, 7168, 8192) decode
+ * layer runs the workspace-free decode kernel, measured faster there).
+ * The workspace holds a 4 KB area of 32-bit counters (one per 32-column
+ * group) and FP32 partial tiles after it.  It must be zero-filled (e.g.
+ * hipMemset) before its first use; every call leaves it ready for the next
+ * one (counters back at zero), for any shape.  Calls that share a workspace
+ * must not run concurrently: issue them on one stream.
  */
 size_t mx_gemm_a4w4_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
@@ -107,11 +115,47 @@ size_t mx_gemm_a4w4_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *   qw [N, K/2], sw [N, K/32]   weight codes / scales (e.g. from mx_quant_weight_f32)
  *   y_bf16 [M, N]               out
  * K > 0 and K % 128 == 0.  qa, qw 16-byte aligned; sa, sw 4-byte aligned;
- * y_bf16 2-byte aligned.  workspace may be NULL when workspace_bytes is 0.
+ * y_bf16 2-byte aligned.  workspace: at least mx_gemm_a4w4_workspace_bytes(M,
+ * N, K) bytes, 16-byte aligned, zero-filled before first use (see there);
+ * may be NULL when that size is 0, else MX_ERROR_WORKSPACE.  The split-K
+ * decode kernel sums the K parts of each output in a fixed order, so results
+ * do not depend on timing.  It relies on workgroups being dealt round-robin
+ * to the XCDs (the parts of a tile meet in one XCD's L2).
  */
 mx_status mx_gemm_a4w4_bf16(const void *qa, const void *sa, const void *qw, const void *sw,
                             void *y_bf16, int64_t M, int64_t N, int64_t K,
                             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Bytes of workspace mx_linear_a4w4_bf16 needs for this shape (same rules as
+ * mx_gemm_a4w4_workspace_bytes: zero-filled before first use, left ready by
+ * every call, not shared by concurrent calls; one zero-filled buffer of the
+ * larger size may serve both entry points on one stream).
+ */
+size_t mx_linear_a4w4_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * The A4W4 layer in one call: BF16 activations in, BF16 out, the activations
+ * quantized dynamically to MXFP4 on the way ("dynamic MXFP4 activations with
+ * A4W4 dispatch": "Kimi-K3 DSpark O-Proj-only MXFP4", section "Exact
+ * quantization coverage").  Y = dequant(mx_quant_act_bf16(X)) . dequant(qw,
+ * sw)^T, the same value the two calls give.
+ *   x_bf16 [M, K]  in  BF16, 16-byte aligned
+ *   qw [N, K/2], sw [N, K/32]  weight codes / scales (qw 16-byte, sw 4-byte aligned)
+ *   y_bf16 [M, N]  out, 2-byte aligned
+ *   workspace  at least mx_linear_a4w4_workspace_bytes(M, N, K) bytes, 256-byte
+ *              aligned, zero-filled before first use.
+ * K > 0 and K % 128 == 0.  At decode sizes (M <= 64, K a multiple of 1024 that
+ * splits into 2, 4 or 8 parts, enough 128-column tiles for half the GPU, sw
+ * 16-byte aligned) this is ONE kernel launch: every workgroup quantizes its K
+ * part of X into LDS, bit for bit as mx_quant_act_bf16, and runs the split-K
+ * GEMM on it, so no activation codes are written to memory.  Other shapes run
+ * mx_quant_act_bf16 (codes and scales in the workspace) and mx_gemm_a4w4_bf16
+ * in two launches on the same stream.
+ */
+mx_status mx_linear_a4w4_bf16(const void *x_bf16, const void *qw, const void *sw, void *y_bf16,
+                              int64_t M, int64_t N, int64_t K,
+                              void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Grouped A4W4 GEMM over MoE experts, decode-sized groups: expert weights and

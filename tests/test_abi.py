@@ -76,7 +76,30 @@ def test_gemm_argument_errors(mx):
     assert g4(FAKE, FAKE, FAKE, FAKE, FAKE + 1, 8, 8, 128) == mx.MX_ERROR_MISALIGNED
     assert g4(None, None, None, None, None, 0, 8, 128) == mx.MX_SUCCESS
     assert g4(None, None, None, None, None, 8, 0, 128) == mx.MX_SUCCESS
-    assert mx.mx_gemm_a4w4_workspace_bytes(64, 7168, 8192) == 0
+    # the split-K decode GEMM (only where the decode rings would fill at most half the CUs): a 4 KB counter
+    # area + tiles x K parts x 4 waves x fragments x 4 KB of partials
+    assert mx.mx_gemm_a4w4_workspace_bytes(64, 4096, 8192) == 4096 + 32 * 4 * 4 * 2 * 4096
+    assert mx.mx_gemm_a4w4_workspace_bytes(32, 2048, 16384) == 4096 + 16 * 8 * 4 * 1 * 4096
+    assert mx.mx_gemm_a4w4_workspace_bytes(64, 7168, 8192) == 0     # the decode rings
+    # the one-launch layer: split-K wherever a plan keeps half the CUs busy, else codes + GEMM
+    assert mx.mx_linear_a4w4_workspace_bytes(64, 7168, 8192) == 4096 + 56 * 4 * 4 * 2 * 4096
+    assert mx.mx_linear_a4w4_workspace_bytes(1, 7168, 8192) == 4096 + 56 * 4 * 4 * 1 * 4096
+    assert mx.mx_linear_a4w4_workspace_bytes(100, 7168, 8192) == 4096 + 100 * 4096 + 25600  # codes + scales
+    assert mx.mx_gemm_a4w4_workspace_bytes(64, 128 * 256 + 1, 8192) == 0  # more than 256 tiles
+    assert mx.mx_gemm_a4w4_workspace_bytes(65, 7168, 8192) == 0     # two row halves, no workspace
+    assert mx.mx_gemm_a4w4_workspace_bytes(64, 512, 8192) == 0      # too few tiles to split
+    assert mx.mx_gemm_a4w4_workspace_bytes(64, 7168, 8192 + 128) == 0
+    assert g4(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 4096, 8192, None, 0) == mx.MX_ERROR_WORKSPACE
+    assert g4(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 4096, 8192, FAKE, 1024) == mx.MX_ERROR_WORKSPACE
+    lin = mx.mx_linear_a4w4_bf16
+    wsl = mx.mx_linear_a4w4_workspace_bytes(64, 7168, 8192)
+    assert lin(FAKE, FAKE, FAKE, FAKE, 64, 7168, 8192, None, 0) == mx.MX_ERROR_WORKSPACE
+    assert lin(FAKE, FAKE, FAKE, FAKE, 64, 7168, 8192, FAKE, wsl - 1) == mx.MX_ERROR_WORKSPACE
+    assert lin(FAKE, FAKE, FAKE, FAKE, 64, 7168, 8096, FAKE, wsl) == mx.MX_ERROR_UNSUPPORTED_SHAPE  # K % 128
+    assert lin(FAKE + 8, FAKE, FAKE, FAKE, 64, 7168, 8192, FAKE, wsl) == mx.MX_ERROR_MISALIGNED
+    assert lin(FAKE, FAKE, FAKE, FAKE, 64, 7168, 8192, FAKE + 16, wsl) == mx.MX_ERROR_MISALIGNED    # 256-byte ws
+    assert lin(None, FAKE, FAKE, FAKE, 64, 7168, 8192, FAKE, wsl) == mx.MX_ERROR_INVALID_VALUE
+    assert lin(None, None, None, None, 0, 7168, 8192, None, 0) == mx.MX_SUCCESS
     g8 = mx.gemm_a8w8_ptpc_bf16
     assert g8(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 8, 64) == mx.MX_ERROR_UNSUPPORTED_SHAPE
     assert g8(FAKE, FAKE + 2, FAKE, FAKE, FAKE, 8, 8, 128) == mx.MX_ERROR_MISALIGNED

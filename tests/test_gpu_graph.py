@@ -46,7 +46,7 @@ def test_a4w4_layer_graph_replay(mx, M, N, K):
     sa = torch.empty((M, K // 32), dtype=torch.uint8, device="cuda")
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     wsb = mx.mx_gemm_a4w4_workspace_bytes(M, N, K)
-    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device="cuda")  # zero-filled before first use
 
     def layer():
         s = torch.cuda.current_stream().cuda_stream

@@ -1,0 +1,123 @@
+"""GPU parity of the one-call A4W4 layer mx_linear_a4w4_bf16 (BF16 X in, BF16 Y out; dynamic MXFP4
+activations with A4W4 dispatch: "Kimi-K3 DSpark O-Proj-only MXFP4", section "Exact quantization
+coverage"), through the C ABI.
+
+At decode sizes it is one kernel that quantizes each K part of X inside the split-K GEMM's workgroups.
+  * Against the oracle: the oracle quantizes X and forms the exact GEMM; the GPU layer must be within
+    |gpu - exact| <= 2^-8 |exact| + 1e-6 sum|a w| on every output.
+  * Against the two calls (mx_quant_act_bf16, then mx_gemm_a4w4_bf16) on shapes where that GEMM takes
+    the same split-K kernel: identical bits, which also shows the in-kernel quantization matches the
+    quantizer bit for bit - including rows of zeros, subnormals, huge values, ties and NaN/Inf.
+Shapes with no one-launch plan (M > 64, K % 1024 != 0) take the two-launch path and are checked too.
+"""
+import numpy as np
+import pytest
+
+from block_scaled_precision_act_amd import synth
+from parity import bf16_dev, bf16_host, gemm_within_tolerance, to_dev
+
+pytestmark = pytest.mark.gpu
+NT = 16
+
+
+def _layer(mx, torch, x, qw, sw, ws=None):
+    M, K = x.shape
+    N = qw.shape[0]
+    wsb = mx.mx_linear_a4w4_workspace_bytes(M, N, K)
+    if ws is None:
+        ws = torch.zeros(max(wsb, 256), dtype=torch.uint8, device="cuda")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    st = mx.mx_linear_a4w4_bf16(x.data_ptr(), qw.data_ptr(), sw.data_ptr(), y.data_ptr(), M, N, K, ws.data_ptr(),
+                                ws.numel(), s)
+    assert st == 0, mx.status_string(st)
+    return y
+
+
+def _weight(orc, seed, N, K):
+    return orc.mx_quant_f32(synth.weight_normal(seed, N, K, 0.02), nthreads=NT)
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (64, 7168, 8192),   # the o_proj decode layer: 64 rows, 8 slabs per part, 4 parts
+    (16, 7168, 8192),   # 32-row fragments
+    (1, 7168, 8192),
+    (5, 4000, 4096),    # 32 rows, 4 slabs, 4 parts, ragged last tile
+    (33, 8100, 4096),   # 64 rows, 8 slabs, 2 parts
+    (64, 2900, 8192),   # 64 rows, 4 slabs, 8 parts, idle workgroups
+    (100, 3000, 2048),  # no one-launch plan (M > 64): quantizer + GEMM
+    (24, 5000, 640),    # no plan (K % 1024 != 0)
+])
+def test_linear_matches_oracle(mx, orc, M, N, K):
+    import torch
+    x = synth.act_normal(M + N + K, M, K)
+    qw, sw = _weight(orc, M + 3, N, K)
+    y = _layer(mx, torch, bf16_dev(x), to_dev(qw), to_dev(sw))
+    qa, sa = orc.mx_quant_bf16(x, nthreads=NT)
+    ye, ad, _ = orc.gemm_a4w4_at(qa, sa, qw, sw, nthreads=NT)
+    ok, ratio, nbad = gemm_within_tolerance(bf16_host(y), ye, ad)
+    print("layer %dx%dx%d: max err/bound %.4f" % (M, N, K, ratio))
+    assert ok, "%d elements outside tolerance (max err/bound %.3g)" % (nbad, ratio)
+
+
+def _special_rows(M, K, seed):
+    """N(0, 1) rows, then rows that exercise the quantizer's special cases."""
+    x = synth.act_normal(seed, M, K).copy()
+    rng = np.random.default_rng(seed)
+    x[1] = 0                                                       # all-zero blocks: scale 0x00
+    x[2] = rng.integers(1, 0x80, K, dtype=np.uint16) | (rng.integers(0, 2, K, dtype=np.uint16) << 15)  # subnormals
+    x[3] = synth.f64_to_bf16_bits(rng.standard_normal(K) * 2.0 ** 120)                                 # huge
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.0], np.float64)                         # grid midpoints
+    x[4] = synth.f64_to_bf16_bits(np.resize(ties, K) * np.where(np.arange(K) % 3, 1.0, -1.0))
+    x[5, 100] = 0x7FC0                                             # NaN: its block gets scale 0xFF
+    x[6, 4000 % K] = 0xFF80                                        # -inf
+    return x
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 4096, 8192), (32, 2048, 16384), (20, 2048, 16384)])
+def test_linear_bit_identical_to_two_calls(mx, orc, M, N, K):
+    import torch
+    assert mx.mx_gemm_a4w4_workspace_bytes(M, N, K) > 0, "the two-call GEMM should take the split-K kernel"
+    x = bf16_dev(_special_rows(M, K, 7 + M))
+    qw, sw = (to_dev(a) for a in _weight(orc, 11, N, K))
+    y1 = _layer(mx, torch, x, qw, sw)
+    qa, sa = mx.quant_act_mx(x)
+    y2 = mx.gemm_a4w4(qa, sa, qw, sw)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    # and the NaN / inf blocks came out NaN where the exact result is NaN
+    ye, ad, _ = orc.gemm_a4w4_at(qa.cpu().numpy(), sa.cpu().numpy(), qw.cpu().numpy(), sw.cpu().numpy(), nthreads=NT)
+    ok, ratio, nbad = gemm_within_tolerance(bf16_host(y1), ye, ad)
+    assert ok, "%d elements outside tolerance (max err/bound %.3g)" % (nbad, ratio)
+
+
+def test_linear_repeatable_and_shares_workspace(mx, orc):
+    """Repeated one-call layers give identical bits; one zero-filled workspace serves layer and GEMM calls
+    of different shapes in turn (each leaves the counters at zero)."""
+    import torch
+    shapes = [(64, 7168, 8192), (5, 4000, 4096), (100, 3000, 2048)]
+    size = max(max(mx.mx_linear_a4w4_workspace_bytes(*s), mx.mx_gemm_a4w4_workspace_bytes(*s)) for s in shapes)
+    size = max(size, mx.mx_gemm_a4w4_workspace_bytes(64, 4096, 8192))
+    ws = torch.zeros(size, dtype=torch.uint8, device="cuda")
+    ops = []
+    for i, (M, N, K) in enumerate(shapes):
+        qw, sw = (to_dev(a) for a in _weight(orc, 40 + i, N, K))
+        ops.append((bf16_dev(synth.act_normal(50 + i, M, K)), qw, sw))
+    g = tuple(to_dev(a) for a in _weight(orc, 60, 4096, 8192))
+    gx = bf16_dev(synth.act_normal(61, 64, 8192))
+    gqa, gsa = mx.quant_act_mx(gx)
+
+    def gemm():
+        y = torch.empty((64, 4096), dtype=torch.bfloat16, device="cuda")
+        s = torch.cuda.current_stream().cuda_stream
+        assert mx.mx_gemm_a4w4_bf16(gqa.data_ptr(), gsa.data_ptr(), g[0].data_ptr(), g[1].data_ptr(), y.data_ptr(),
+                                    64, 4096, 8192, ws.data_ptr(), size, s) == 0
+        return y
+
+    first = [_layer(mx, torch, *o, ws=ws) for o in ops] + [gemm()]
+    for rep in range(2):
+        again = [_layer(mx, torch, *o, ws=ws) for o in ops] + [gemm()]
+        torch.cuda.synchronize()
+        for a, b in zip(first, again):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "repeat %d differs" % rep
+    assert int(ws[:4096].count_nonzero()) == 0

@@ -1,0 +1,115 @@
+"""GPU parity of the split-K decode A4W4 GEMM (K split across workgroups, partial tiles summed
+through the caller's workspace in K-part order), through the C ABI, against the oracle's exact
+GEMM: |gpu - exact| <= 2^-8 |exact| + 1e-6 sum|a w| per element, all outputs.
+
+Layer: the attention output projection of "Kimi-K3 DSpark O-Proj-only MXFP4", section "Exact
+quantization coverage" (weight (7168, 8192) MXFP4, (7168, 256) E8M0 scales, dynamic MXFP4
+activations).  The GEMM takes this kernel where its 32-column decode tiles would fill at most half of
+the CUs (N <= 4096) and K splits into 4 or 8 parts of 2048: one shape per instantiation (32 or 64
+activation rows, 4 or 8 parts), ragged N (a partial last tile) and tile counts that are not a multiple
+of 8 (idle workgroups in the grid).  The one-call layer (tests/test_gpu_linear.py) runs the other
+instantiations.
+"""
+import numpy as np
+import pytest
+
+from block_scaled_precision_act_amd import synth
+from parity import bf16_host, gemm_within_tolerance, to_dev
+
+pytestmark = pytest.mark.gpu
+NT = 16
+
+# (M, N, K): rows per fragment set, slabs per part, parts
+SPLIT_SHAPES = [
+    (7, 4096, 8192),     # 32 rows, 4 parts
+    (16, 4000, 8192),    # 32 rows, 4 parts, ragged last tile
+    (20, 2000, 16384),   # 32 rows, 8 parts
+    (64, 4096, 8192),    # 64 rows, 4 parts
+    (33, 3990, 8192),    # 64 rows, 4 parts, ragged last tile
+    (50, 2000, 16384),   # 64 rows, 8 parts
+    (64, 2900, 16384),   # 64 rows, 8 parts (23 tiles: one idle workgroup per part and XCD)
+]
+
+
+def _operands(orc, seed, M, N, K):
+    x = synth.act_normal(seed, M, K)
+    w = synth.weight_normal(seed + 1, N, K, 0.02)
+    qa, sa = orc.mx_quant_bf16(x, nthreads=NT)
+    qw, sw = orc.mx_quant_f32(w, nthreads=NT)
+    return qa, sa, qw, sw
+
+
+def _gemm(mx, torch, qa, sa, qw, sw, ws):
+    M, N, K = qa.shape[0], qw.shape[0], qa.shape[1] * 2
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    st = mx.mx_gemm_a4w4_bf16(qa.data_ptr(), sa.data_ptr(), qw.data_ptr(), sw.data_ptr(), y.data_ptr(), M, N, K,
+                              ws.data_ptr(), ws.numel(), s)
+    assert st == 0, mx.status_string(st)
+    return y
+
+
+@pytest.mark.parametrize("M,N,K", SPLIT_SHAPES)
+def test_splitk_matches_oracle(mx, orc, M, N, K):
+    import torch
+    wsb = mx.mx_gemm_a4w4_workspace_bytes(M, N, K)
+    assert wsb > 0, "shape should take the split-K path"
+    qa, sa, qw, sw = _operands(orc, M * 31 + N + K, M, N, K)
+    y, ad, _ = orc.gemm_a4w4_at(qa, sa, qw, sw, nthreads=NT)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    yg = _gemm(mx, torch, to_dev(qa), to_dev(sa), to_dev(qw), to_dev(sw), ws)
+    torch.cuda.synchronize()
+    ok, ratio, nbad = gemm_within_tolerance(bf16_host(yg), y, ad)
+    print("split-K %dx%dx%d: max err/bound %.4f" % (M, N, K, ratio))
+    assert ok, "%d elements outside tolerance (max err/bound %.3g)" % (nbad, ratio)
+    # every call leaves the counter area (the first 4 KB) at zero
+    assert int(ws[:4096].count_nonzero()) == 0
+
+
+def test_splitk_deterministic_and_workspace_reuse(mx, orc):
+    """Repeated calls give identical bits (the K parts are summed in a fixed order, whatever order
+    the workgroups finish in); one workspace serves calls of different shapes in turn; and no
+    write lands outside Y."""
+    import torch
+    shapes = [(64, 4096, 8192), (20, 2000, 16384), (64, 2900, 16384)]
+    ops = [tuple(to_dev(a) for a in _operands(orc, 500 + i, *s)) for i, s in enumerate(shapes)]
+    wsb = max(mx.mx_gemm_a4w4_workspace_bytes(*s) for s in shapes)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    first = [_gemm(mx, torch, *o, ws) for o in ops]
+    for rep in range(3):
+        for o, f in zip(ops, first):
+            y = _gemm(mx, torch, *o, ws)
+            torch.cuda.synchronize()
+            assert torch.equal(y.view(torch.int16), f.view(torch.int16)), "repeat %d differs" % rep
+    # guard bands around Y
+    qa, sa, qw, sw = ops[0]
+    M, N, K = shapes[0]
+    pad = 4096
+    buf = torch.full((M * N + 2 * pad,), -12345.0, dtype=torch.bfloat16, device="cuda")
+    y = buf[pad:pad + M * N].view(M, N)
+    s = torch.cuda.current_stream().cuda_stream
+    assert mx.mx_gemm_a4w4_bf16(qa.data_ptr(), sa.data_ptr(), qw.data_ptr(), sw.data_ptr(), y.data_ptr(), M, N, K,
+                                ws.data_ptr(), wsb, s) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), first[0].view(torch.int16))
+    sentinel = torch.tensor(-12345.0).to(torch.bfloat16).float().item()
+    assert bool((torch.cat([buf[:pad], buf[pad + M * N:]]).float() == sentinel).all()), "a write landed outside Y"
+
+
+def test_splitk_unaligned_scales_fall_back(mx, orc):
+    """Scale rows that are only 4-byte aligned take the workspace-free decode kernels (same result
+    within tolerance); the workspace is still accepted."""
+    import torch
+    M, N, K = 64, 4096, 8192
+    qa, sa, qw, sw = _operands(orc, 77, M, N, K)
+    y, ad, _ = orc.gemm_a4w4_at(qa, sa, qw, sw, nthreads=NT)
+
+    def shifted(a):
+        buf = torch.zeros(a.size + 4, dtype=torch.uint8, device="cuda")
+        view = buf[4:].view(a.shape)
+        view.copy_(torch.from_numpy(a))
+        return view
+
+    out = mx.gemm_a4w4(to_dev(qa), shifted(sa), to_dev(qw), shifted(sw))
+    ok, ratio, nbad = gemm_within_tolerance(bf16_host(out), y, ad)
+    assert ok, "%d elements outside tolerance (max err/bound %.3g)" % (nbad, ratio)
