@@ -107,6 +107,19 @@ MX_API mx_status mx_gemm_a4w4_bf16(const void* qa, const void* sa, const void* q
     return launched(mx::launch_gemm_a4w4(qa, sa, qw, sw, y_bf16, M, N, K, workspace, reinterpret_cast<hipStream_t>(stream)));
 }
 
+MX_API mx_status mx_gemm_a4w4_bf16_noalloc(const void* qa, const void* sa, const void* qw, const void* sw,
+                                           void* y_bf16, int64_t M, int64_t N, int64_t K, void* stream) {
+    mx_status st = check_gemm(M, N, K);
+    if (st != MX_SUCCESS) return st;
+    if (M == 0 || N == 0) return MX_SUCCESS;
+    if (!qa || !sa || !qw || !sw || !y_bf16) return MX_ERROR_INVALID_VALUE;
+    if (mx_gemm_a4w4_workspace_bytes(M, N, K) > mx::kGemmScratchBytes) return MX_ERROR_WORKSPACE;
+    if (!aligned(qa, 16) || !aligned(qw, 16) || !aligned(sa, 4) || !aligned(sw, 4) || !aligned(y_bf16, 2))
+        return MX_ERROR_MISALIGNED;
+    if ((st = check_device()) != MX_SUCCESS) return st;
+    return launched(mx::launch_gemm_a4w4_noalloc(qa, sa, qw, sw, y_bf16, M, N, K, reinterpret_cast<hipStream_t>(stream)));
+}
+
 MX_API size_t mx_linear_a4w4_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     if (check_gemm(M, N, K) != MX_SUCCESS || M == 0 || N == 0) return 0;
     return mx::linear_a4w4_workspace_bytes(M, N, K);

@@ -16,6 +16,8 @@
 // Layer.  mx_linear_a4w4_bf16 runs the split-K kernel with its activation block
 // quantized from BF16 X inside each workgroup (one launch) whenever a split-K
 // plan exists (M <= 64), else the quantizer and the GEMM in two launches.
+#include <mutex>
+
 #include "gemm_kernels.hpp"
 #include "gemm_splitk.hpp"
 #include "launch.hpp"
@@ -126,6 +128,43 @@ hipError_t launch_linear_a4w4(const void* x, const void* qw, const void* sw, voi
     hipError_t e = launch_quant_mx_bf16(x, M, K, qa, sa, st);
     if (e != hipSuccess) return e;
     return launch_gemm_a4w4(qa, sa, qw, sw, y, M, N, K, nullptr, st);
+}
+
+// ---------------------------------------------------------------------------------------------------------
+// Allocation-free GEMM: the split-K workspace lives in a static device array (zero-filled when the code
+// object is loaded; every call leaves its counters at zero again), one copy per GPU.  In host code the
+// array's name is only a stand-in: its device address is looked up once per device, with that device
+// current, and only that address is ever passed to a kernel.
+namespace {
+__device__ __align__(256) uint8_t scratch[kGemmScratchBytes];
+constexpr int kMaxScratchDevices = 64;
+void* g_scratch_ptr[kMaxScratchDevices];
+std::once_flag g_scratch_once[kMaxScratchDevices];
+hipError_t g_scratch_err[kMaxScratchDevices];
+}  // namespace
+
+hipError_t gemm_scratch_ptr(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+    });
+    *out = g_scratch_ptr[dev];
+    return g_scratch_err[dev];
+}
+
+hipError_t launch_gemm_a4w4_noalloc(const void* qa, const void* sa, const void* qw, const void* sw, void* y,
+                                    int64_t M, int64_t N, int64_t K, hipStream_t st) {
+    void* ws = nullptr;
+    if (gemm_a4w4_workspace_bytes(M, N, K) > 0) {
+        hipError_t e = gemm_scratch_ptr(&ws);
+        if (e != hipSuccess) return e;
+    }
+    return launch_gemm_a4w4(qa, sa, qw, sw, y, M, N, K, ws, st);
 }
 
 hipError_t launch_a4w4_grouped(const void* qa, const void* sa, const void* qw, const void* sw, void* y,

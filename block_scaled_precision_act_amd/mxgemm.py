@@ -64,6 +64,8 @@ def lib() -> ctypes.CDLL:
         L.gemm_a8w8_ptpc_bf16.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
         L.gemm_a8w8_ptpc_bf16.restype = i32
         L.mx_gemm_a4w4_grouped_bf16.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp]
+        L.mx_gemm_a4w4_bf16_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
+        L.mx_gemm_a4w4_bf16_noalloc.restype = i32
         L.mx_linear_a4w4_workspace_bytes.argtypes = [i64, i64, i64]
         L.mx_linear_a4w4_workspace_bytes.restype = ctypes.c_size_t
         L.mx_linear_a4w4_bf16.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, ctypes.c_size_t, vp]
@@ -96,6 +98,10 @@ def mx_gemm_a4w4_workspace_bytes(M, N, K) -> int:
 
 def mx_gemm_a4w4_bf16(qa, sa, qw, sw, y, M, N, K, workspace=None, workspace_bytes=0, stream=None) -> int:
     return lib().mx_gemm_a4w4_bf16(qa, sa, qw, sw, y, M, N, K, workspace, workspace_bytes, stream)
+
+
+def mx_gemm_a4w4_bf16_noalloc(qa, sa, qw, sw, y, M, N, K, stream=None) -> int:
+    return lib().mx_gemm_a4w4_bf16_noalloc(qa, sa, qw, sw, y, M, N, K, stream)
 
 
 def mx_linear_a4w4_workspace_bytes(M, N, K) -> int:

@@ -127,6 +127,22 @@ mx_status mx_gemm_a4w4_bf16(const void *qa, const void *sa, const void *qw, cons
                             void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * mx_gemm_a4w4_bf16 for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same arguments without a workspace.  The split-K kernel's workspace is a
+ * static device array of 4 MiB + 4 KiB per GPU, held from the library's load
+ * until the process ends; it is zero when loaded and every call leaves it
+ * ready for the next.  Shapes whose workspace would be larger (see
+ * mx_gemm_a4w4_workspace_bytes) return MX_ERROR_WORKSPACE before anything is
+ * enqueued.  The call itself allocates nothing.  All calls on one GPU share
+ * the array, so calls that overlap on one GPU (other streams, other threads)
+ * race: issue them on one stream.  Results equal mx_gemm_a4w4_bf16's bit for
+ * bit.
+ */
+mx_status mx_gemm_a4w4_bf16_noalloc(const void *qa, const void *sa, const void *qw, const void *sw,
+                                    void *y_bf16, int64_t M, int64_t N, int64_t K, void *stream);
+
+/*
  * Bytes of workspace mx_linear_a4w4_bf16 needs for this shape (same rules as
  * mx_gemm_a4w4_workspace_bytes: zero-filled before first use, left ready by
  * every call, not shared by concurrent calls; one zero-filled buffer of the

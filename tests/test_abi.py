@@ -91,6 +91,12 @@ def test_gemm_argument_errors(mx):
     assert mx.mx_gemm_a4w4_workspace_bytes(64, 7168, 8192 + 128) == 0
     assert g4(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 4096, 8192, None, 0) == mx.MX_ERROR_WORKSPACE
     assert g4(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 4096, 8192, FAKE, 1024) == mx.MX_ERROR_WORKSPACE
+    na = mx.mx_gemm_a4w4_bf16_noalloc
+    assert na(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 4096, 16384) == mx.MX_ERROR_WORKSPACE   # needs 8 MiB of scratch
+    assert na(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 8, 96) == mx.MX_ERROR_UNSUPPORTED_SHAPE
+    assert na(FAKE, None, FAKE, FAKE, FAKE, 64, 4096, 8192) == mx.MX_ERROR_INVALID_VALUE
+    assert na(FAKE, FAKE, FAKE, FAKE, FAKE + 1, 64, 4096, 8192) == mx.MX_ERROR_MISALIGNED
+    assert na(None, None, None, None, None, 0, 4096, 8192) == mx.MX_SUCCESS
     lin = mx.mx_linear_a4w4_bf16
     wsl = mx.mx_linear_a4w4_workspace_bytes(64, 7168, 8192)
     assert lin(FAKE, FAKE, FAKE, FAKE, 64, 7168, 8192, None, 0) == mx.MX_ERROR_WORKSPACE

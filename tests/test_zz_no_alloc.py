@@ -1,0 +1,44 @@
+"""The allocation-free GEMM entry point mx_gemm_a4w4_bf16_noalloc (workspace in a static per-GPU array),
+through the C ABI, against mx_gemm_a4w4_bf16 with a caller workspace: identical bits, on calls in a
+row - a split-K shape, then a smaller one, then a shape that needs no scratch, then the first again -
+and within tolerance of the oracle's exact GEMM."""
+import numpy as np
+import pytest
+
+from block_scaled_precision_act_amd import synth
+from parity import bf16_host, gemm_within_tolerance, to_dev
+
+pytestmark = pytest.mark.gpu
+NT = 16
+
+
+def _ops(orc, seed, M, N, K):
+    qa, sa = orc.mx_quant_bf16(synth.act_normal(seed, M, K), nthreads=NT)
+    qw, sw = orc.mx_quant_f32(synth.weight_normal(seed + 1, N, K, 0.02), nthreads=NT)
+    return qa, sa, qw, sw
+
+
+def test_noalloc_matches_workspace_entry(mx, orc):
+    import torch
+    shapes = [(64, 4096, 8192), (20, 2000, 16384), (64, 7168, 8192), (64, 4096, 8192)]
+    assert mx.mx_gemm_a4w4_workspace_bytes(*shapes[0]) > mx.mx_gemm_a4w4_workspace_bytes(*shapes[1]) > 0
+    s = torch.cuda.current_stream().cuda_stream
+    cache = {}
+    for i, (M, N, K) in enumerate(shapes):
+        if (M, N, K) not in cache:
+            host = _ops(orc, 900 + i, M, N, K)
+            cache[(M, N, K)] = (host, tuple(to_dev(a) for a in host))
+        host, (qa, sa, qw, sw) = cache[(M, N, K)]
+        y0 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        y1 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        assert mx.mx_gemm_a4w4_bf16_noalloc(qa.data_ptr(), sa.data_ptr(), qw.data_ptr(), sw.data_ptr(),
+                                            y1.data_ptr(), M, N, K, s) == 0
+        wsb = mx.mx_gemm_a4w4_workspace_bytes(M, N, K)
+        ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device="cuda")
+        assert mx.mx_gemm_a4w4_bf16(qa.data_ptr(), sa.data_ptr(), qw.data_ptr(), sw.data_ptr(), y0.data_ptr(),
+                                    M, N, K, ws.data_ptr(), wsb, s) == 0
+        torch.cuda.synchronize()
+        assert torch.equal(y0.view(torch.int16), y1.view(torch.int16)), "call %d (%d x %d x %d) differs" % (i, M, N, K)
+        ye, ad, _ = orc.gemm_a4w4_at(*host, nthreads=NT)
+        ok, ratio, nbad = gemm_within_tolerance(bf16_host(y1), ye, ad)
+        assert ok, "call %d: %d elements outside tolerance (max err/bound %.3g)" % (i, nbad, ratio)
