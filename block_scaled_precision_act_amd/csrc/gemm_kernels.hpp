@@ -413,31 +413,14 @@ struct Cfg {
 };
 }  // namespace dec4
 
-// GROUPED: grid.y indexes groups (MoE experts).  Group e multiplies rows goff[e] .. goff[e+1]-1
-// of the packed activations with weight e of the stacked weights ([G, N, K/2] codes, [G, N, K/32]
-// scales) into the same rows of y; it takes at most 32 MF rows (the caller's bound), and an empty
-// group's workgroups return before their first barrier.
-// KSMAX = 64 (K <= 2048, 68 KB of LDS at MF = 1, S = 2) lets two workgroups share a CU: with so
-// few slabs per wave, concurrency rather than ring depth hides the memory latency.
-template <int MF, int S, int KSMAX, bool GROUPED = false, int RH = 1>
-__global__ __launch_bounds__(256, KSMAX == 64 ? 2 : 1) void gemm_decode_fp4(const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa,
-                                                          const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw,
-                                                          uint16_t* __restrict__ y, int M, int N, int K,
-                                                          const int32_t* __restrict__ goff) {
+// The decode ring's work on one set of at most 32 MF RH activation rows (M of them) and the workgroup's
+// 32 columns, in the workgroup's LDS block (the kernel below).
+template <int MF, int S, int KSMAX, int RH>
+__device__ __forceinline__ void decode_fp4_rows(const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa,
+                                                const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw,
+                                                uint16_t* __restrict__ y, int M, int N, int K, uint8_t* lds) {
     using C = dec4::Cfg<MF, S, KSMAX, RH>;
     using namespace dec4;
-    if constexpr (GROUPED) {
-        const int e = blockIdx.y;
-        const int r0 = goff[e];
-        M = min(goff[e + 1] - r0, C::kScArows);
-        if (M <= 0) return;  // the whole workgroup (M is uniform), before any barrier
-        qa += (int64_t)r0 * (K / 2);
-        sa += (int64_t)r0 * (K / 32);
-        y += (int64_t)r0 * N;
-        qw += (int64_t)e * N * (K / 2);
-        sw += (int64_t)e * N * (K / 32);
-    }
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[C::kLds];
     const int n0 = blockIdx.x * kNT;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -606,6 +589,38 @@ __global__ __launch_bounds__(256, KSMAX == 64 ? 2 : 1) void gemm_decode_fp4(cons
             for (int e = 0; e < 4; ++e)
                 if (n + e < N) dst[e] = (uint16_t)(bf16x2_rne(v[e], 0.f) & 0xffffu);
         }
+    }
+}
+
+// GROUPED: grid.y indexes groups (MoE experts).  Group e multiplies rows goff[e] .. goff[e+1]-1
+// of the packed activations with weight e of the stacked weights ([G, N, K/2] codes, [G, N, K/32]
+// scales) into the same rows of y.  The workgroup takes the group's rows in chunks of 32 MF (a
+// barrier between chunks, which reuse the LDS block), so every row of every group is written whatever
+// bound the caller passed; an empty group's workgroups return before their first barrier.
+// KSMAX = 64 (K <= 2048, 68 KB of LDS at MF = 1, S = 2) lets two workgroups share a CU: with so
+// few slabs per wave, concurrency rather than ring depth hides the memory latency.
+template <int MF, int S, int KSMAX, bool GROUPED = false, int RH = 1>
+__global__ __launch_bounds__(256, KSMAX == 64 ? 2 : 1) void gemm_decode_fp4(const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa,
+                                                          const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw,
+                                                          uint16_t* __restrict__ y, int M, int N, int K,
+                                                          const int32_t* __restrict__ goff) {
+    using C = dec4::Cfg<MF, S, KSMAX, RH>;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[C::kLds];
+    if constexpr (GROUPED) {
+        const int e = blockIdx.y;
+        const int r0 = __builtin_amdgcn_readfirstlane(goff[e]);
+        const int rows = __builtin_amdgcn_readfirstlane(goff[e + 1]) - r0;  // uniform over the workgroup
+        if (rows <= 0) return;  // the whole workgroup, before any barrier
+        qw += (int64_t)e * N * (K / 2);
+        sw += (int64_t)e * N * (K / 32);
+        for (int c = 0; c < rows; c += C::kScArows) {
+            if (c > 0) __syncthreads();  // every wave has read the previous chunk's reduction staging
+            const int64_t r = (int64_t)r0 + c;
+            decode_fp4_rows<MF, S, KSMAX, RH>(qa + r * (K / 2), sa + r * (K / 32), qw, sw, y + r * N,
+                                              min(rows - c, C::kScArows), N, K, lds);
+        }
+    } else {
+        decode_fp4_rows<MF, S, KSMAX, RH>(qa, sa, qw, sw, y, M, N, K, lds);
     }
 }
 
@@ -2390,8 +2405,9 @@ inline hipError_t launch_gemm(const void* qa, const void* sa, const void* qw, co
     return hipGetLastError();
 }
 
-// Grouped A4W4 decode GEMM (MoE experts): grid (N / 32, G); every group at most max_rows <= 64 rows,
-// K % 2048 == 0, K <= 16384, all code and scale pointers 16-byte aligned (checked by the caller).
+// Grouped A4W4 decode GEMM (MoE experts): grid (N / 32, G); max_rows (the largest group, or a bound on it)
+// picks 32- or 64-row chunks - every row of every group is written either way; K % 2048 == 0, K <= 16384,
+// all code and scale pointers 16-byte aligned (checked by the caller).
 inline hipError_t launch_gemm_a4w4_grouped(const void* qa, const void* sa, const void* qw, const void* sw, void* y,
                                            const int32_t* offsets, int64_t G, int64_t max_rows, int64_t N, int64_t K,
                                            hipStream_t st) {

@@ -232,7 +232,8 @@ def gemm_a4w4(qa, sa, qw, sw, y=None):
 def gemm_a4w4_grouped(qa, sa, qw, sw, offsets, max_rows, y=None):
     """Grouped A4W4 GEMM over experts: qa [T, K/2] / sa [T, K/32] packed activation rows, qw [G, N, K/2] /
     sw [G, N, K/32] stacked expert weights, offsets int32 [G + 1] (device) -> BF16 Y [T, N], rows
-    offsets[e] .. offsets[e+1]-1 multiplied with expert e.  max_rows bounds every group's row count."""
+    offsets[e] .. offsets[e+1]-1 multiplied with expert e.  max_rows (the largest group) picks 32- or 64-row
+    chunks; every row of every group is written whatever its value."""
     torch = _torch()
     for t, n in ((qa, "qa"), (sa, "sa")):
         _need(t, torch.uint8, 2, n)

@@ -174,7 +174,7 @@ mx_status mx_linear_a4w4_bf16(const void *x_bf16, const void *qw, const void *sw
                               void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Grouped A4W4 GEMM over MoE experts, decode-sized groups: expert weights and
+ * Grouped A4W4 GEMM over MoE experts: expert weights and
  * activations both in OCP MXFP4 ("Kimi-K3-Quark-MXFP4-AttnFP8", section
  * "Model Quantization").  Group e multiplies the activation rows
  * offsets[e] .. offsets[e+1]-1 with expert weight e:
@@ -184,8 +184,13 @@ mx_status mx_linear_a4w4_bf16(const void *x_bf16, const void *qw, const void *sw
  *   y_bf16 [T, N]                    out; rows outside every group are not written
  *   offsets [G + 1] int32, DEVICE memory, non-decreasing, offsets[0] = 0: read by the
  *            kernel, so routing computed on the GPU needs no host round trip (capturable)
- *   max_rows  an upper bound on every group's row count, 0 <= max_rows <= 64; a group
- *            with more rows has only its first max_rows rounded up to 32 or 64 rows written
+ *   max_rows  the largest group's row count (or any bound on it), >= 0: it only
+ *            picks the kernel - each workgroup takes its group in chunks of 32
+ *            rows (max_rows <= 32) or 64 rows (larger), and every row of every
+ *            group is written whatever the value; 0 declares every group empty.
+ *            Groups are streamed as decode work (the expert weight columns of a
+ *            workgroup are re-read from L2 per 64-row chunk): sized for routed
+ *            decode tokens, correct for groups of any size.
  * K % 2048 == 0 and K <= 16384; qa, sa, qw, sw 16-byte aligned; y_bf16 2-byte
  * aligned; offsets 4-byte aligned; G <= 65535.  G, N or max_rows == 0: no-op.
  */

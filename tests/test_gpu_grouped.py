@@ -51,6 +51,30 @@ def test_grouped_a4w4_matches_oracle(mx, orc, sizes, N, K, max_rows):
         assert ok, "group %d: %d elements outside tolerance (max err/bound %.3g)" % (e, nbad, ratio)
 
 
+@pytest.mark.parametrize("sizes,N,K,max_rows", [
+    ([100, 0, 65, 7], 512, 2048, 32),        # groups above the bound: 32-row chunks, every row written
+    ([300, 1000, 3], 256, 4096, 64),         # prefill-sized groups in 64-row chunks
+    ([64, 65, 128, 129], 300, 2048, 1),      # chunk edges; a bound far below the real sizes
+])
+def test_grouped_every_row_of_large_groups(mx, orc, sizes, N, K, max_rows):
+    """max_rows only picks 32- or 64-row chunks: groups of 65 .. 1000 rows, and groups larger than the
+    bound the caller passed, are computed in full (checked against the oracle group by group)."""
+    import torch
+    qa, sa, qw, sw, offsets = _grouped_case(orc, 3 * N + K + sum(sizes), sizes, N, K)
+    T = int(offsets[-1])
+    y = torch.full((T, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    mx.gemm_a4w4_grouped(to_dev(qa), to_dev(sa), to_dev(qw), to_dev(sw), to_dev(offsets), max_rows, y=y)
+    yh = bf16_host(y)
+    for e in range(len(sizes)):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r0 == r1:
+            continue
+        ye, ad, _ = orc.gemm_a4w4_at(qa[r0:r1], sa[r0:r1], qw[e], sw[e], nthreads=NT)
+        ok, ratio, nbad = gemm_within_tolerance(yh[r0:r1], ye, ad)
+        print("group %d (%d rows, max_rows %d): max err/bound %.4f" % (e, r1 - r0, max_rows, ratio))
+        assert ok, "group %d: %d elements outside tolerance (max err/bound %.3g)" % (e, nbad, ratio)
+
+
 @pytest.mark.parametrize("K", [2048, 4096])
 def test_grouped_equals_per_group_gemm_bit_for_bit(mx, orc, K):
     # the ungrouped decode GEMM runs the same kernel design (K = 2048: with a 2-slot ring; the order
