@@ -431,28 +431,89 @@ def grouped_entry(ctx, args):
 
 
 # ----------------------------------------------------------------------------- CPU baseline
-def cpu_baseline():
-    import numpy as np
+def host_threads():
+    """(threads the oracle uses, CPUs this process may run on): all of them unless OMP_NUM_THREADS
+    sets a smaller share of the host."""
     import oracle
-    from block_scaled_precision_act_amd import synth
-    cfg = synth.CONFIGS["oproj_decode_a4w4"]
-    threads = min(16, oracle.default_threads())
-    x_bits = synth.make_activations(cfg)
-    qw, sw = oracle.mx_quant_f32(synth.make_weight(cfg), nthreads=threads)  # offline, not timed
-    M, N, K = cfg["M"], cfg["N"], cfg["K"]
+    cpus = oracle.default_threads()
+    try:
+        share = int(os.environ.get("OMP_NUM_THREADS", "0"))
+    except ValueError:
+        share = 0
+    return (min(cpus, share) if share > 0 else cpus), cpus
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _timed(fn, budget_s, max_reps=200):
     t0 = time.perf_counter()
     reps = 0
     while True:
+        fn()
+        reps += 1
+        if time.perf_counter() - t0 > budget_s or reps >= max_reps:
+            break
+    return (time.perf_counter() - t0) / reps, reps
+
+
+def cpu_baseline():
+    """The oracle (plain C, exact arithmetic, row-parallel) on the host: the headline decode layer in
+    full for about 10 s, then every configuration of the layer for about 2 s each, large ones on a
+    sample of rows (MXFP4 / PTPC quantization of those rows + their exact GEMM against all of W),
+    with the full-layer time extrapolated from the rows per second."""
+    import oracle
+    from block_scaled_precision_act_amd import synth
+    threads, cpus = host_threads()
+    cfg = synth.CONFIGS["oproj_decode_a4w4"]
+    x_bits = synth.make_activations(cfg)
+    qw, sw = oracle.mx_quant_f32(synth.make_weight(cfg), nthreads=threads)  # offline, not timed
+    M, N, K = cfg["M"], cfg["N"], cfg["K"]
+
+    def layer():
         qa, sa = oracle.mx_quant_bf16(x_bits, nthreads=threads)
         oracle.gemm_a4w4_at(qa, sa, qw, sw, nthreads=threads)
-        reps += 1
-        if time.perf_counter() - t0 > 10.0 or reps >= 200:
-            break
-    total = time.perf_counter() - t0
-    sec = total / reps
-    return {"value": round(2.0 * M * N * K / sec / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": "full o_proj decode layer (MXFP4 quantization of X [64, 8192] + exact A4W4 GEMM against "
-                      "W [7168, 8192]), %d repetition(s), %.2f s each, %.1f s in total" % (reps, sec, total)}
+
+    sec, reps = _timed(layer, 10.0)
+    out = {"value": round(2.0 * M * N * K / sec / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+           "host_cpus": cpus, "cpu_model": cpu_model(), "kind": "oracle",
+           "sample": "full o_proj decode layer (MXFP4 quantization of X [64, 8192] + exact A4W4 GEMM against "
+                     "W [7168, 8192]), %d repetition(s), %.2f s each" % (reps, sec)}
+    per = {}
+    weights = {}
+    for name, rows in (("tiny_a4w4", None), ("oproj_decode_a4w4", None), ("oproj_prefill_a4w4", 64),
+                       ("msweep_outlier_a4w4", 64), ("ptpc_a8w8_m64", None), ("ptpc_a8w8_m8192", 64)):
+        c = synth.CONFIGS[name]
+        Mc, Nc, Kc = c["M"], c["N"], c["K"]
+        Ms = Mc if rows is None else rows
+        x = synth.make_activations(c, Ms)
+        key = (c["w"], c["kind"], Nc, Kc)
+        if key not in weights:
+            w = synth.make_weight(c)
+            weights[key] = (oracle.mx_quant_f32 if c["kind"] == "a4w4" else oracle.ptpc_quant_f32)(w, nthreads=threads)
+        wq, ws_ = weights[key]
+        if c["kind"] == "a4w4":
+            def run():
+                qa, sa = oracle.mx_quant_bf16(x, nthreads=threads)
+                oracle.gemm_a4w4_at(qa, sa, wq, ws_, nthreads=threads)
+        else:
+            def run():
+                qa, sa = oracle.ptpc_quant_bf16(x, nthreads=threads)
+                oracle.gemm_a8w8_at(qa, sa, wq, ws_, nthreads=threads)
+        s_, r_ = _timed(run, 2.0)
+        full_s = s_ * Mc / Ms
+        per[name] = {"M": Mc, "N": Nc, "K": Kc, "rows_timed": Ms, "reps": r_, "sample_s": round(s_, 4),
+                     "full_layer_s": round(full_s, 3), "tflops": round(2.0 * Mc * Nc * Kc / full_s / 1e12, 6)}
+    out["per_config"] = per
+    return out
 
 
 # ----------------------------------------------------------------------------- profile pass
