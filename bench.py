@@ -530,6 +530,8 @@ def profile_pass(ctx):
     for r in range(min(4, dec.R)):
         dec.quant(r)()
         dec.gemm(r)()
+    for r in range(min(4, dec.R)):
+        dec.fused(r)()
     torch.cuda.synchronize()
     pre = make_a4w4(ctx, "oproj_prefill_a4w4", rotate=2)
     for r in range(2):
@@ -544,6 +546,7 @@ def profile_pass(ctx):
 PMC_KERNELS = {
     "gemm_decode_fp4_m64": ("gemm_decode_fp4<2, 2, 256, false, 1>", None),
     "gemm_tile224_fp4_m8192": ("gemm_tile224_fp4<true>", 1024 * 256),
+    "linear_splitk_fused_m64": ("gemm_splitk_fp4<2, 4, 8, 4, true>", None),
 }
 COPY_BYTES = 256 << 20  # the profile pass copies 256 MiB device -> device
 
