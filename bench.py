@@ -341,10 +341,11 @@ def layer_entry(ctx, layer, kind, args, label):
 
 
 def one_call_layer_entry(ctx, args):
-    """The one-call A4W4 layer (mx_linear_a4w4_bf16: one kernel at these sizes, quantizing X inside the
-    GEMM's workgroups) beside the two-launch layer (quantizer + GEMM), o_proj weight, M = 1, 16, 64."""
+    """The one-call A4W4 layer (mx_linear_a4w4_bf16: one kernel for M <= 8, quantizing X inside the split-K
+    GEMM's workgroups; the quantizer and the GEMM above that) beside the two-launch layer (quantizer + GEMM
+    entries), o_proj weight, M = 1, 8, 16, 64."""
     out = {}
-    for Ms in (1, 16, 64):
+    for Ms in (1, 8, 16, 64):
         lay = make_a4w4(ctx, "oproj_decode_a4w4", M=Ms)
         one_ms = kernel_ms(ctx, lay, "fused", args.kernel_reps)
         two_ms = kernel_ms(ctx, lay, "step", args.kernel_reps)
@@ -352,13 +353,14 @@ def one_call_layer_entry(ctx, args):
         byt = 2 * Ms * lay.K + lay.N * lay.K // 2 + lay.N * lay.K // 32 + 2 * Ms * lay.N
         gbs = byt / (one_ms * 1e-3) / 1e9
         out["M=%d" % Ms] = {"one_call_us": round(one_ms * 1e3, 3), "two_launch_us": round(two_ms * 1e3, 3),
+                            "one_call_path": "one launch" if Ms <= 8 else "quantizer + GEMM",
                             "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                             "frac": round(gbs / PEAK_HBM_GBS, 4), "alg_bytes_per_launch": byt}
         del lay
         ctx.torch.cuda.empty_cache()
     return {"workload": "A4W4 o_proj layer BF16 X [M, 8192] -> BF16 Y [M, 7168], W [7168, 8192] MXFP4; "
-                        "one call (quantization inside the split-K GEMM) vs quantizer + GEMM, graph-replayed, "
-                        "rotated copies", "by_M": out}
+                        "one call (one launch with the quantization inside the split-K GEMM for M <= 8) vs "
+                        "quantizer + GEMM entries, graph-replayed, rotated copies", "by_M": out}
 
 
 def weight_conversion_entry(ctx, args):
@@ -530,8 +532,10 @@ def profile_pass(ctx):
     for r in range(min(4, dec.R)):
         dec.quant(r)()
         dec.gemm(r)()
-    for r in range(min(4, dec.R)):
-        dec.fused(r)()
+    torch.cuda.synchronize()
+    one = make_a4w4(ctx, "oproj_decode_a4w4", M=1)
+    for r in range(min(4, one.R)):
+        one.fused(r)()
     torch.cuda.synchronize()
     pre = make_a4w4(ctx, "oproj_prefill_a4w4", rotate=2)
     for r in range(2):
@@ -544,9 +548,9 @@ def profile_pass(ctx):
 # ----------------------------------------------------------------------------- PMC summary
 # Kernels whose HBM traffic the bench reports: key -> (name fragment, grid size in threads or None)
 PMC_KERNELS = {
-    "gemm_decode_fp4_m64": ("gemm_decode_fp4<2, 2, 256, false, 1>", None),
+    "gemm_splitk_fp4_m64": ("gemm_splitk_fp4<2, 4, 8, 4, false>", None),
     "gemm_tile224_fp4_m8192": ("gemm_tile224_fp4<true>", 1024 * 256),
-    "linear_splitk_fused_m64": ("gemm_splitk_fp4<2, 4, 8, 4, true>", None),
+    "linear_splitk_fused_m1": ("gemm_splitk_fp4<1, 5, 8, 4, true>", None),
 }
 COPY_BYTES = 256 << 20  # the profile pass copies 256 MiB device -> device
 
@@ -634,8 +638,8 @@ def main():
     log("step %.3f us -> %.2f TFLOP/s" % (ms_per_step * 1e3, value))
 
     roof = roofline_gemm("a4w4", M, N, K, gemm_ms)
-    roof["traffic"] = pmc_traffic("gemm_decode_fp4_m64")
-    roof["kernel"] = "gemm_decode_fp4<2, 2, 256, false, 1>"
+    roof["traffic"] = pmc_traffic("gemm_splitk_fp4_m64")
+    roof["kernel"] = "gemm_splitk_fp4<2, 4, 8, 4, false>"
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak",

@@ -1,21 +1,25 @@
-// gemm_a4w4.hip - MXFP4 A4W4 GEMM and one-launch layer entries ("A4W4 dispatch"
+// gemm_a4w4.hip - MXFP4 A4W4 GEMM and one-call layer entries ("A4W4 dispatch"
 // with dynamic MXFP4 activations: "Kimi-K3 DSpark O-Proj-only MXFP4", section
 // "Exact quantization coverage").
 //
-// GEMM.  Decode sizes (M <= 64) whose 32-column tiles would occupy at most half
-// of the 256 CUs, with K long enough for parts of 2048 K-values, take the
-// split-K kernel (gemm_splitk.hpp), which needs the caller's workspace.  Other
+// GEMM.  Decode sizes (M <= 64) with K a multiple of 8192 take the split-K
+// kernel (gemm_splitk.hpp: 128-column tiles, K parts of 2048, the partials
+// summed across the tile's workgroups), which needs the caller's workspace,
+// when its grid is at least half the CUs and fits the device at once (else,
+// e.g. on a device with fewer CUs, the ring kernels run and the workspace is
+// not touched).  Other
 // shapes take the kernels of gemm_kernels.hpp: the decode rings for M <= 128
 // (K split over the waves of a workgroup) and the LDS-tiled kernels above.
-// Measured (N, K, M = 64 unless noted; graph-replayed): split-K is faster at
-// (4096, 8192) 9.7 vs 10.3 us and (2048, 16384, M = 32) 9.5 vs 12.5 us, slower
-// at (7168, 8192) 11.7 vs 11.3 us, (2048, 8192) and (7168, 4096): there its
-// cross-workgroup reduction (partial stores, count, partial loads: about 3 us
-// of round trips) costs more than the activation re-reads it saves.
+// Measured (graph-replayed, rotated weights, us): split-K vs ring at K = 8192:
+// N = 7168 M = 64 10.4 vs 12.4, M = 1 7.8 vs 8.4; N = 2048 M = 64 6.6 vs 9.9;
+// at K = 16384, N = 4096, M = 64 11.1 vs 17.7; at K = 4096 the ring kernels
+// are as fast or faster (N = 7168, M = 64: 7.4 vs 7.2), so they keep it.
 //
-// Layer.  mx_linear_a4w4_bf16 runs the split-K kernel with its activation block
-// quantized from BF16 X inside each workgroup (one launch) whenever a split-K
-// plan exists (M <= 64), else the quantizer and the GEMM in two launches.
+// Layer.  mx_linear_a4w4_bf16 quantizes inside the split-K workgroups (one
+// launch) for M <= 8, where that beat the quantizer + GEMM pair (N = 7168,
+// K = 8192, M = 1: 8.6 vs 9.9 us); above that every workgroup quantizing its
+// K part of all M rows costs more than the second launch (M = 16: 11.4 vs
+// 10.4 us), so the layer runs the quantizer and the GEMM.
 #include <mutex>
 
 #include "gemm_kernels.hpp"
@@ -26,26 +30,41 @@ namespace mx {
 
 namespace {
 
-// The split-K plan of a shape: slabs (K = 256) per part, parts, tiles, fragments; nsl == 0 if none.
-// layer: the one-launch layer's plan (any split that keeps half the CUs busy); else the GEMM's (only
-// where the split was measured faster than the decode rings).
+// Compute units of the current device (cached per device); 0 if the query fails.
+constexpr int kMaxDevices = 64;
+int device_cus() {
+    static int cus[kMaxDevices];
+    static std::once_flag once[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    std::call_once(once[dev], [dev] {
+        int n = 0;
+        cus[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess ? n : 0;
+    });
+    return cus[dev];
+}
+
+// The split-K plan of a shape: slabs (K = 256) per part, parts, tiles, fragments; nsl == 0 if none.  Every
+// plan keeps at least half of the 256 CUs busy with at most 256 workgroups (it depends on the shape only, so
+// the workspace queries do too).  layer: the one-launch layer's plan (parts of 1024 or 2048 K-values); else
+// the GEMM's (parts of 2048, at least 4: measured faster than the decode rings there).
 struct SplitPlan {
     int nsl = 0, kp = 0, tiles = 0, mf = 0;
     int grid() const { return 8 * kp * ((tiles + 7) / 8); }
+    // The kernel's tail needs every workgroup resident at once (one per CU: its LDS block rules out two).
+    bool fits_device() const { return nsl != 0 && grid() <= device_cus(); }
 };
 
 SplitPlan split_plan(int64_t M, int64_t N, int64_t K, bool layer) {
     SplitPlan p;
-    if (M < 1 || M > 64 || K % 1024 != 0 || N < 1 || N > (int64_t)sk::kTN * sk::kMaxTiles) return p;
+    if (M < 1 || M > 64 || K % 1024 != 0 || N < 1 || N > (int64_t)sk::kTN * sk::kMaxGrid) return p;
     const int tiles = (int)((N + sk::kTN - 1) / sk::kTN);
-    if (!layer && (N + 31) / 32 > 128) return p;  // the decode rings fill more than half the CUs
     for (int nsl : {8, 4}) {
         if (K % (256 * nsl) != 0) continue;
         const int64_t kp = K / (256 * nsl);
         if (kp != 2 && kp != 4 && kp != 8) continue;
         if (!layer && (nsl != 8 || kp < 4)) continue;
-        // at least half the 256 CUs busy, at most two rounds of workgroups
-        if ((int64_t)tiles * kp < 128 || 8 * kp * ((tiles + 7) / 8) > 512) continue;
+        if ((int64_t)tiles * kp < 128 || 8 * kp * ((tiles + 7) / 8) > sk::kMaxGrid) continue;
         p.nsl = nsl;
         p.kp = (int)kp;
         p.tiles = tiles;
@@ -55,16 +74,22 @@ SplitPlan split_plan(int64_t M, int64_t N, int64_t K, bool layer) {
     return p;
 }
 
+template <int MF, int S, int NSL, int KP, bool FUSED>
+hipError_t launch_split_kp(const SplitPlan& p, const uint8_t* a, const uint8_t* sa, const uint8_t* w,
+                           const uint8_t* sw, uint16_t* y, int m, int n, int k, uint8_t* ws, hipStream_t st) {
+    hipLaunchKernelGGL((gemm_splitk_fp4<MF, S, NSL, KP, FUSED>), dim3((unsigned)p.grid()), dim3(256), 0, st, a, sa, w,
+                       sw, y, m, n, k, p.tiles, ws);
+    return hipGetLastError();
+}
+
 template <int MF, int S, int NSL, bool FUSED>
 hipError_t launch_split_nsl(const SplitPlan& p, const uint8_t* a, const uint8_t* sa, const uint8_t* w,
                             const uint8_t* sw, uint16_t* y, int m, int n, int k, uint8_t* ws, hipStream_t st) {
-    const dim3 grid((unsigned)p.grid()), block(256);
     switch (p.kp) {
-        case 2: hipLaunchKernelGGL((gemm_splitk_fp4<MF, S, NSL, 2, FUSED>), grid, block, 0, st, a, sa, w, sw, y, m, n, k, p.tiles, ws); break;
-        case 4: hipLaunchKernelGGL((gemm_splitk_fp4<MF, S, NSL, 4, FUSED>), grid, block, 0, st, a, sa, w, sw, y, m, n, k, p.tiles, ws); break;
-        default: hipLaunchKernelGGL((gemm_splitk_fp4<MF, S, NSL, 8, FUSED>), grid, block, 0, st, a, sa, w, sw, y, m, n, k, p.tiles, ws); break;
+        case 2: return launch_split_kp<MF, S, NSL, 2, FUSED>(p, a, sa, w, sw, y, m, n, k, ws, st);
+        case 4: return launch_split_kp<MF, S, NSL, 4, FUSED>(p, a, sa, w, sw, y, m, n, k, ws, st);
+        default: return launch_split_kp<MF, S, NSL, 8, FUSED>(p, a, sa, w, sw, y, m, n, k, ws, st);
     }
-    return hipGetLastError();
 }
 
 // FUSED: qa is BF16 X [M, K] and sa is unused.
@@ -78,12 +103,18 @@ hipError_t launch_split(const SplitPlan& p, const void* qa, const void* sa, cons
     uint16_t* out = reinterpret_cast<uint16_t*>(y);
     uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
     const int m = (int)M, n = (int)N, k = (int)K;
-    // ring depth: 4 slots with 64 activation rows (140 KB of LDS), 5 with 32 (122 KB); 4 at 4 slabs per part
-    if (p.mf == 1)
-        return p.nsl == 8 ? launch_split_nsl<1, 5, 8, FUSED>(p, a, sa8, w, sw8, out, m, n, k, ws, st)
-                          : launch_split_nsl<1, 4, 4, FUSED>(p, a, sa8, w, sw8, out, m, n, k, ws, st);
-    return p.nsl == 8 ? launch_split_nsl<2, 4, 8, FUSED>(p, a, sa8, w, sw8, out, m, n, k, ws, st)
-                      : launch_split_nsl<2, 4, 4, FUSED>(p, a, sa8, w, sw8, out, m, n, k, ws, st);
+    // ring depth: 4 slots with 64 activation rows (140 KB of LDS), 5 with 32 (122 KB); 4 at 4 slabs per part.
+    // The one-launch layer (FUSED) runs only for M <= 8: one fragment.
+    if constexpr (FUSED) {
+        return p.nsl == 8 ? launch_split_nsl<1, 5, 8, true>(p, a, sa8, w, sw8, out, m, n, k, ws, st)
+                          : launch_split_nsl<1, 4, 4, true>(p, a, sa8, w, sw8, out, m, n, k, ws, st);
+    } else {
+        if (p.mf == 1)
+            return p.nsl == 8 ? launch_split_nsl<1, 5, 8, false>(p, a, sa8, w, sw8, out, m, n, k, ws, st)
+                              : launch_split_nsl<1, 4, 4, false>(p, a, sa8, w, sw8, out, m, n, k, ws, st);
+        return p.nsl == 8 ? launch_split_nsl<2, 4, 8, false>(p, a, sa8, w, sw8, out, m, n, k, ws, st)
+                          : launch_split_nsl<2, 4, 4, false>(p, a, sa8, w, sw8, out, m, n, k, ws, st);
+    }
 }
 
 bool aligned16(const void* a, const void* b) {
@@ -102,32 +133,35 @@ size_t gemm_a4w4_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 hipError_t launch_gemm_a4w4(const void* qa, const void* sa, const void* qw, const void* sw, void* y, int64_t M,
                             int64_t N, int64_t K, void* workspace, hipStream_t st) {
     const SplitPlan p = split_plan(M, N, K, false);
-    if (p.nsl && workspace && aligned16(sa, sw))
+    if (workspace && aligned16(sa, sw) && p.fits_device())
         return launch_split<false>(p, qa, sa, qw, sw, y, M, N, K, workspace, st);
     return launch_gemm<false>(qa, sa, qw, sw, y, M, N, K, st);
 }
 
-// Either path fits: the one-launch split-K layer (counter area, then partials), or - when no plan applies or
-// the weight scales are not 16-byte aligned - the activation codes and scales, placed after the counter area
-// so that they never disturb the counters a later one-launch call relies on.  (The GEMM of the two-launch
-// path never needs a workspace: a GEMM split-K plan implies a layer plan, and the only other reason to take
-// two launches, unaligned weight scales, also rules the GEMM's split out.)
+// The layer's workspace holds either path: the one-launch split-K layer's partial slots, or the quantizer's
+// codes and scales placed past the largest partial area of any split-K launch (the split-K kernels read a 0
+// word there as "not written yet", so nothing else may leave data in that area of a shared workspace),
+// followed through by the GEMM, whose own split-K plan then uses the partial area.
+constexpr int kLinearOneLaunchMaxM = 8;
+constexpr size_t kLinearCodesOffset = sk::kMaxWorkspaceBytes;
+
 size_t linear_a4w4_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     const SplitPlan p = split_plan(M, N, K, true);
-    const size_t fused = p.nsl ? sk::workspace_bytes(p.tiles, p.kp, p.mf) : 0;
-    const size_t two = sk::kCounterBytes + align256((size_t)M * K / 2) + align256((size_t)M * K / 32);
-    return fused > two ? fused : two;
+    const size_t one = p.nsl ? sk::workspace_bytes(p.tiles, p.kp, p.mf) : 0;
+    const size_t two = kLinearCodesOffset + align256((size_t)M * K / 2) + align256((size_t)M * K / 32);
+    return one > two ? one : two;
 }
 
 hipError_t launch_linear_a4w4(const void* x, const void* qw, const void* sw, void* y, int64_t M, int64_t N, int64_t K,
                               void* workspace, hipStream_t st) {
     const SplitPlan p = split_plan(M, N, K, true);
-    if (p.nsl && aligned16(qw, sw)) return launch_split<true>(p, x, nullptr, qw, sw, y, M, N, K, workspace, st);
-    uint8_t* qa = reinterpret_cast<uint8_t*>(workspace) + sk::kCounterBytes;
+    if (M <= kLinearOneLaunchMaxM && aligned16(qw, sw) && p.fits_device())
+        return launch_split<true>(p, x, nullptr, qw, sw, y, M, N, K, workspace, st);
+    uint8_t* qa = reinterpret_cast<uint8_t*>(workspace) + kLinearCodesOffset;
     uint8_t* sa = qa + align256((size_t)M * K / 2);
     hipError_t e = launch_quant_mx_bf16(x, M, K, qa, sa, st);
     if (e != hipSuccess) return e;
-    return launch_gemm_a4w4(qa, sa, qw, sw, y, M, N, K, nullptr, st);
+    return launch_gemm_a4w4(qa, sa, qw, sw, y, M, N, K, workspace, st);
 }
 
 // ---------------------------------------------------------------------------------------------------------
@@ -136,6 +170,7 @@ hipError_t launch_linear_a4w4(const void* x, const void* qw, const void* sw, voi
 // array's name is only a stand-in: its device address is looked up once per device, with that device
 // current, and only that address is ever passed to a kernel.
 namespace {
+static_assert(kGemmScratchBytes >= sk::kMaxWorkspaceBytes, "the static workspace holds every split-K plan");
 __device__ __align__(256) uint8_t scratch[kGemmScratchBytes];
 constexpr int kMaxScratchDevices = 64;
 void* g_scratch_ptr[kMaxScratchDevices];

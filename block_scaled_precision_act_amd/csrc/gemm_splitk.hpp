@@ -16,23 +16,25 @@
 //     lines per copy), waiting only for their own copies: no barrier in the
 //     main loop.  The order of a workgroup's slabs is rotated by its tile, so
 //     the workgroups streaming at one moment spread over the HBM channels;
-//   * the KP partial tiles of a column group are summed across workgroups: each
-//     wave stores its FP32 partial (64 x 32) to the workspace, waits until the
-//     stores are complete, and increments the group's counter.  The wave that
-//     sees the count reach KP - 1 reads the other KP - 1 partials, adds all KP
-//     in K-part order (0, 1, ..., KP - 1: deterministic, whatever the arrival
-//     order), writes BF16 and resets the counter to 0.  No wave ever waits for
-//     another workgroup, so the design needs no co-residency.
+//   * the KP partial tiles of a column group (tile, wave: 32 MF x 32 FP32) are
+//     summed across workgroups slice by slice: part p < min(KP, 4 MF) owns one
+//     slice, every wave stores the slices it does not own into their owners'
+//     workspace slots without waiting, and each owner polls its slots until
+//     every word has arrived, adds the KP slices in K-part order (0, 1, ...,
+//     KP - 1: deterministic, whatever the arrival order), writes BF16 and
+//     clears the slots.  So the tail costs one L2 round trip after the last
+//     partial lands, not a store-acknowledge, a counter and a read in turn.
 //
-// The KP workgroups of a tile are blockIdx t % 8 + 8 (KP (t / 8) + q): equal
-// modulo 8, which places them on one XCD (workgroups are dealt round-robin to
-// the XCDs), so partials and counters meet in that XCD's L2 without cache
-// maintenance.  The workspace holds one counter per column group in a fixed
-// 4 KB area at its start (at most 256 tiles x 4 groups), then the partials.
-// It must be zero-filled before its first use; every launch leaves the
-// counters at zero, and no launch's partials reach into the counter area, so
-// one workspace serves launches of any shapes in turn.  Launches that share a
-// workspace must not overlap.
+// An owner waits for other workgroups, so every workgroup of the grid must be
+// resident at once: the host launches this kernel only when the grid (at most
+// 256 workgroups, one per CU, as the LDS block rules out two) fits the
+// device's CUs.  The KP workgroups of a tile are blockIdx t % 8 + 8 (KP (t / 8)
+// + q): equal modulo 8, which places them on one XCD (workgroups are dealt
+// round-robin to the XCDs), so the partials meet in that XCD's L2 without
+// cache maintenance; polls read with device-scope coherence (never from the
+// CU's L1).  The workspace must be zero-filled before its first use; every
+// launch leaves it all zero, so one workspace serves launches of any shapes in
+// turn.  Launches that share a workspace must not overlap.
 #pragma once
 
 #include "mx_device.hpp"
@@ -65,55 +67,179 @@ struct Cfg {
     static_assert(kLds <= 160 * 1024, "LDS");
 };
 
-// Workspace: the counter area (4 per tile, at most kMaxTiles tiles), then KP partials of
-// 4 waves x MF fragments x 4 KB per tile.
-constexpr int kMaxTiles = 256;
-constexpr size_t kCounterBytes = kMaxTiles * 4 * sizeof(uint32_t);
-inline size_t workspace_bytes(int tiles, int KP, int MF) {
-    return kCounterBytes + (size_t)tiles * KP * 4 * MF * 4096;
+// Workspace: the partial slots of every column group (tile, wave), KP x MF x 4 KB per group.  A launch has
+// at most kMaxGrid workgroups (all resident at once, one per CU), so at most 8 MiB.
+constexpr int kMaxGrid = 256;
+__host__ __device__ inline size_t workspace_bytes(int tiles, int KP, int MF) {
+    return (size_t)tiles * KP * 4 * MF * 4096;
 }
+constexpr size_t kMaxWorkspaceBytes = (size_t)kMaxGrid * 4 * 2 * 4096;
 }  // namespace sk
 
 // FUSED prologue: quantize rows 0 .. M-1 of BF16 X, K-values 256 s0 .. 256 (s0 + NSL) - 1, into the LDS
 // activation block and scale rows of the split-K kernel, bit for bit as mx_quant_act_bf16 does.  A row's
 // part is NSL / 2 pieces of 1 KB; one wave instruction loads a whole piece (whole cache lines), so a 32-value
-// block (64 bytes) spans four lanes: lane l holds values 8 (l % 4) .. +7 of block 16 k + l / 4 of piece k.
-// The block's exponent maximum is reduced over its four lanes; each lane converts its eight values and
-// writes them (4 bytes) to the block's 16-byte chunk, and the block's first lane writes the scale byte.
-// Rows at or past M are not written (they only feed output columns that are never stored).
-template <int MF, int S, int NSL>
-__device__ __forceinline__ void quantize_part_impl(const uint8_t* __restrict__ x, int M, int K, int s0, int wave,
-                                                   int lane, uint8_t* actb, uint8_t* scb) {
+// block (64 bytes) spans the four lanes of a quad: lane l holds values 8 (l % 4) .. +7 of block 16 k + l / 4
+// of piece k.  The block's exponent maximum is reduced over the quad (DPP lane swaps), each lane converts
+// its eight values and writes their 4 code bytes to the block's 16-byte chunk, and the quad writes the
+// scale byte.  Wave w takes pieces w, w + 4, ... in chunks of kB, two chunks in flight (the next chunk's
+// loads are issued before the current one is converted); a chunk's loads are unconditional (pieces past
+// the wave's count reload its last piece, not converted), so the compiler's waits count exactly one chunk.
+// Rows at or past M are not written (they only feed output rows that are never stored).
+template <int MF, int S, int NSL, int kB>
+__device__ __forceinline__ void quantize_chunks(const uint8_t* __restrict__ x, int K, int s0, int wave, int lane,
+                                                int count, uint8_t* actb, uint8_t* scb) {
     using C = sk::Cfg<MF, S, NSL>;
     constexpr int kPieces = NSL / 2;  // 1 KB pieces per row
-    constexpr int kB = 8;             // pieces in flight per lane
-    const int items = M * kPieces;
     const int pc = lane & 3;
-    for (int i0 = wave; i0 < items; i0 += 4 * kB) {
-        uint4 v[kB];
+    auto load = [&](uint4 (&v)[kB], int n0) {
 #pragma unroll
         for (int u = 0; u < kB; ++u) {
-            const int i = min(i0 + 4 * u, items - 1);  // past the end: reload the last piece (not written)
+            const int i = wave + 4 * min(n0 + u, count - 1);
             const int r = i / kPieces, k = i % kPieces;
             v[u] = ldg16(x + ((int64_t)r * K + (int64_t)s0 * 256 + 512 * k) * 2 + 16 * lane);
         }
+    };
+    auto convert = [&](const uint4 (&v)[kB], int n0) {
 #pragma unroll
         for (int u = 0; u < kB; ++u) {
-            const int i = i0 + 4 * u;
-            if (i >= items) break;  // wave-uniform
+            if (n0 + u >= count) break;  // wave-uniform
+            const int i = wave + 4 * (n0 + u);
             const int r = i / kPieces, k = i % kPieces;
-            uint32_t emax = bf16x8_emax(v[u]);
-            emax = max(emax, (uint32_t)__shfl_xor((int)emax, 1));
-            emax = max(emax, (uint32_t)__shfl_xor((int)emax, 2));
-            const uint32_t scale = mx_scale_of_emax(emax);
-            const uint32_t codes = scale == 0xffu ? 0u : bf16x8_codes(v[u], scale);
+            const uint32_t scale = mx_scale_of_emax(quad_max(bf16x8_emax(v[u])));
+            const uint32_t codes = bf16x8_codes(v[u], scale);
             const int b = 16 * k + (lane >> 2);  // block within the part
             const int j = b >> 3, c = b & 7;     // slab and chunk within the slab's 128-byte line
-            *reinterpret_cast<uint32_t*>(actb + (r * NSL + j) * sk::kSlab + 16 * (c ^ sk::key(r)) + 4 * pc) = codes;
-            if (pc == 0) scb[r * 8 * NSL + 16 * ((b / 16 + r) % C::kP) + (b & 15)] = (uint8_t)scale;
+            *reinterpret_cast<uint32_t*>(actb + (r * NSL + j) * sk::kSlab + 16 * (c ^ sk::key(r)) + 4 * pc) =
+                scale == 0xffu ? 0u : codes;
+            scb[r * 8 * NSL + 16 * ((b / 16 + r) % C::kP) + (b & 15)] = (uint8_t)scale;
+        }
+    };
+    uint4 va[kB], vb[kB];
+    load(va, 0);
+    for (int n0 = 0; n0 < count; n0 += 2 * kB) {
+        if (n0 + kB < count) {
+            load(vb, n0 + kB);
+            convert(va, n0);
+            if (n0 + 2 * kB < count) {
+                load(va, n0 + 2 * kB);
+                convert(vb, n0 + kB);
+            } else {
+                convert(vb, n0 + kB);
+            }
+        } else {
+            convert(va, n0);
         }
     }
 }
+
+template <int MF, int S, int NSL>
+__device__ __forceinline__ void quantize_part(const uint8_t* __restrict__ x, int M, int K, int s0, int wave, int lane,
+                                              uint8_t* actb, uint8_t* scb) {
+    const int count = (M * (NSL / 2) - wave + 3) / 4;  // pieces of this wave
+    if (count <= 0) return;
+    if (count <= 4) quantize_chunks<MF, S, NSL, 2>(x, K, s0, wave, lane, count, actb, scb);
+    else if (count <= 16) quantize_chunks<MF, S, NSL, 8>(x, K, s0, wave, lane, count, actb, scb);
+    else quantize_chunks<MF, S, NSL, 16>(x, K, s0, wave, lane, count, actb, scb);
+}
+
+namespace sk {
+// Partial sums cross workgroups as 32-bit words, complemented, with every NaN made the quiet NaN
+// 0x7FC00000 first: a stored word is never 0, so a 0 word reads as "not written yet".  Both tails leave
+// every word they wrote at 0 again before the launch ends, so the partial area is all 0 between launches.
+__device__ __forceinline__ uint32_t partial_word(float v) { return ~(v != v ? 0x7FC00000u : __float_as_uint(v)); }
+__device__ __forceinline__ float partial_value(uint32_t w) { return __uint_as_float(~w); }
+__device__ __forceinline__ v4u partial_words(const v4f& v) {
+    return v4u{partial_word(v[0]), partial_word(v[1]), partial_word(v[2]), partial_word(v[3])};
+}
+__device__ __forceinline__ v4f partial_values(const v4u& w) {
+    return v4f{partial_value(w[0]), partial_value(w[1]), partial_value(w[2]), partial_value(w[3])};
+}
+constexpr int kBufferWord3 = 0x00020000;  // raw (unformatted) buffer descriptor
+constexpr int kSpinLimit = 1 << 18;       // polls before a tail gives up (about 0.3 s)
+
+// Tail: the KP workgroups of a tile are all resident at once (the host checks that the grid fits the
+// device), and the first R = min(KP, 4 MF) parts each sum one slice of the column group's partial tile:
+// part p < R owns the float4s u = U p .. U p + U - 1 (U = 4 MF / R) of every lane's 4 MF (float4 u is
+// fragment u / 4, registers 4 (u % 4) .. +3).  Each wave stores the slices it does not own to their
+// owners' slots, without waiting; an owner then polls its slot of every other part (coherent loads that
+// skip the CU's L1) until no word reads 0, adds the KP slices in K-part order, stores BF16 and clears the
+// slots it read.  Every store it waits for was issued by a resident wave, so the poll ends; a bounded
+// count of polls keeps the kernel finite even if the co-residency the host checked were broken (the sums
+// are then wrong).
+template <int MF, int KP, typename Store>
+__device__ __forceinline__ void tail_sum(const v4f (&mine)[MF][4], uint8_t* ws, int ws_range, int t, int q, int wave,
+                                          int lane, Store&& store_one) {
+    constexpr int R = KP < 4 * MF ? KP : 4 * MF;  // parts that own a slice
+    constexpr int U = 4 * MF / R;                 // float4s per lane in a slice
+    static_assert(U * R == 4 * MF, "slices of whole float4s");
+    // slot (p, qq) of column group (t, wave): slice p of part qq, written by qq, read by p; float4 uu of lane
+    // l at + 1024 uu + 16 l.  R KP slots of 1024 U bytes per group: the group's share of the workspace.
+    auto slot = [&](int p, int qq) -> uint32_t {
+        return (uint32_t)(((((size_t)t * 4 + wave) * R + p) * KP + qq) * (1024 * U) + 16 * lane);
+    };
+    static_for<R>([&](auto pc) {
+        constexpr int p = decltype(pc)::value;
+        if (p == q) return;
+        v4u* const dst = reinterpret_cast<v4u*>(ws + slot(p, q));
+        static_for<U>([&](auto uc) {
+            constexpr int uu = decltype(uc)::value, u = U * p + uu;
+            dst[64 * uu] = partial_words(mine[u / 4][u % 4]);
+        });
+    });
+    if (q >= R) return;  // a part without a slice only contributes
+    v4f own[U] = {};
+    static_for<R>([&](auto pc) {
+        constexpr int p = decltype(pc)::value;
+        if (p != q) return;
+        static_for<U>([&](auto uc) {
+            constexpr int uu = decltype(uc)::value, u = U * p + uu;
+            own[uu] = partial_values(partial_words(mine[u / 4][u % 4]));  // NaNs made canonical, as the others'
+        });
+    });
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(ws, (short)0, ws_range, kBufferWord3);
+    v4u pv[KP - 1][U];
+    for (int it = 0; it < kSpinLimit; ++it) {
+        uint32_t present = 1;
+        static_for<KP - 1>([&](auto oc) {
+            constexpr int o = decltype(oc)::value;
+            uint32_t off = slot(q, o < q ? o : o + 1);
+            asm volatile("" : "+v"(off));  // an opaque address: the loads are repeated, not hoisted out of the loop
+#pragma unroll
+            for (int uu = 0; uu < U; ++uu) {
+                // cache policy sc1: coherent at device scope, so every poll reads L2 again, never the L1
+                pv[o][uu] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 1024 * uu, 0, 16));
+                present &= (pv[o][uu][0] != 0u) & (pv[o][uu][1] != 0u) & (pv[o][uu][2] != 0u) & (pv[o][uu][3] != 0u);
+            }
+        });
+        if (__all(present)) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    v4f sum[U];
+    static_for<KP>([&](auto pc) {
+        constexpr int p = decltype(pc)::value;
+        constexpr int below = p < KP - 1 ? p : KP - 2;
+        constexpr int above = p > 0 ? p - 1 : 0;
+#pragma unroll
+        for (int uu = 0; uu < U; ++uu) {
+            const v4f v = p == q ? own[uu] : partial_values(p < q ? pv[below][uu] : pv[above][uu]);
+            if constexpr (p == 0) sum[uu] = v;
+            else sum[uu] += v;
+        }
+    });
+#pragma unroll
+    for (int uu = 0; uu < U; ++uu) {
+        const int u = U * q + uu;
+        store_one(u / 4, u % 4, sum[uu]);
+    }
+    static_for<KP - 1>([&](auto oc) {
+        constexpr int o = decltype(oc)::value;
+        v4u* const dst = reinterpret_cast<v4u*>(ws + slot(q, o < q ? o : o + 1));
+#pragma unroll
+        for (int uu = 0; uu < U; ++uu) dst[64 * uu] = v4u{0u, 0u, 0u, 0u};
+    });
+}
+}  // namespace sk
 
 // KP: K parts (K = 256 NSL KP).  FUSED: the activations arrive as BF16 X [M, K] (in qa; sa unused) and
 // each workgroup quantizes its K part into the LDS block itself (the one-launch decode layer).
@@ -180,7 +306,7 @@ __global__ __launch_bounds__(256, 1) void gemm_splitk_fp4(const uint8_t* __restr
 #pragma unroll
     for (int j = 0; j < S; ++j) issue(j);
     if constexpr (FUSED) {
-        quantize_part_impl<MF, S, NSL>(qa, M, K, s0, wave, lane, actb, scb);
+        quantize_part<MF, S, NSL>(qa, M, K, s0, wave, lane, actb, scb);
         __syncthreads();  // the quantized block, the scales and this wave's first slabs are in LDS
     } else {
         wait_vmcnt<S * 4>();           // activations and scales (issued before the ring) have landed
@@ -248,26 +374,21 @@ __global__ __launch_bounds__(256, 1) void gemm_splitk_fp4(const uint8_t* __restr
     //    4 i + e.  With KP > 1 the partials of the column group (tile t, wave) meet in the workspace.
     const int nw = n0 + 32 * wave + 4 * h;
     const bool vec_ok = (N & 3) == 0 && (reinterpret_cast<uintptr_t>(y) & 7) == 0;
-    auto store_bf16 = [&](const v4f (&v)[MF][4]) {
+    // BF16 of fragment g, registers 4 i .. 4 i + 3 (rows n .. n + 3 of column m)
+    auto store_one = [&](int g, int i, const v4f& v) {
+        const int m = 32 * g + l32;
+        if (m >= M) return;
+        const int n = nw + 8 * i;
+        uint16_t* dst = y + (int64_t)m * N + n;
+        if (vec_ok && n + 3 < N) {
+            uint2 pk;
+            pk.x = bf16x2_rne(v[0], v[1]);
+            pk.y = bf16x2_rne(v[2], v[3]);
+            *reinterpret_cast<uint2*>(dst) = pk;
+        } else {
 #pragma unroll
-        for (int g = 0; g < MF; ++g) {
-            const int m = 32 * g + l32;
-            if (m >= M) continue;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int n = nw + 8 * i;
-                uint16_t* dst = y + (int64_t)m * N + n;
-                if (vec_ok && n + 3 < N) {
-                    uint2 pk;
-                    pk.x = bf16x2_rne(v[g][i][0], v[g][i][1]);
-                    pk.y = bf16x2_rne(v[g][i][2], v[g][i][3]);
-                    *reinterpret_cast<uint2*>(dst) = pk;
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (n + e < N) dst[e] = (uint16_t)(bf16x2_rne(v[g][i][e], 0.f) & 0xffffu);
-                }
-            }
+            for (int e = 0; e < 4; ++e)
+                if (n + e < N) dst[e] = (uint16_t)(bf16x2_rne(v[e], 0.f) & 0xffffu);
         }
     };
     v4f mine[MF][4];
@@ -276,54 +397,13 @@ __global__ __launch_bounds__(256, 1) void gemm_splitk_fp4(const uint8_t* __restr
 #pragma unroll
         for (int i = 0; i < 4; ++i) mine[g][i] = v4f{acc[g][4 * i], acc[g][4 * i + 1], acc[g][4 * i + 2], acc[g][4 * i + 3]};
     if constexpr (KP == 1) {
-        store_bf16(mine);
-        return;
+#pragma unroll
+        for (int g = 0; g < MF; ++g)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) store_one(g, i, mine[g][i]);
+    } else {
+        sk::tail_sum<MF, KP>(mine, ws, (int)sk::workspace_bytes(tiles, KP, MF), t, q, wave, lane, store_one);
     }
-    // partial (t, q', wave, g): 4 KB, float4 i of lane l at + 1024 i + 16 l (whole 1 KB rows per store)
-    const size_t group = (size_t)t * 4 + wave;
-    auto partial = [&](int qq, int g) {
-        return reinterpret_cast<v4f*>(ws + sk::kCounterBytes + ((((size_t)t * KP + qq) * 4 + wave) * MF + g) * 4096) +
-               lane;
-    };
-    uint32_t* const ctr = reinterpret_cast<uint32_t*>(ws) + group;
-#pragma unroll
-    for (int g = 0; g < MF; ++g)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) partial(q, g)[64 * i] = mine[g][i];
-    wait_vmcnt<0>();  // the partial is in L2 before the count says so
-    uint32_t old = 0;
-    if (lane == 0) old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    old = __builtin_amdgcn_readfirstlane(old);
-    if (old != (uint32_t)(KP - 1)) return;  // another wave of the group arrives later and sums
-    asm volatile("" ::: "memory");          // the partial loads stay after the count
-    // last of the group: every partial is complete.  The KP - 1 other parts are loaded first, all
-    // unconditionally (other part o is part o, or o + 1 from q on); this wave's own part comes from its
-    // registers.  Then the sum in K-part order 0, 1, ..., KP - 1, picking each part by a uniform select.
-    v4f pv[KP - 1][MF][4];
-    static_for<KP - 1>([&](auto oc) {
-        constexpr int o = decltype(oc)::value;
-        const int part_o = o < q ? o : o + 1;
-#pragma unroll
-        for (int g = 0; g < MF; ++g)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) pv[o][g][i] = partial(part_o, g)[64 * i];
-    });
-    v4f sum[MF][4];
-    static_for<KP>([&](auto pc) {
-        constexpr int p = decltype(pc)::value;
-        constexpr int below = p < KP - 1 ? p : KP - 2;  // other-part slot of part p when p < q
-        constexpr int above = p > 0 ? p - 1 : 0;        // ... when p > q
-#pragma unroll
-        for (int g = 0; g < MF; ++g)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const v4f v = p == q ? mine[g][i] : (p < q ? pv[below][g][i] : pv[above][g][i]);
-                if constexpr (p == 0) sum[g][i] = v;
-                else sum[g][i] += v;
-            }
-    });
-    store_bf16(sum);
-    if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace mx

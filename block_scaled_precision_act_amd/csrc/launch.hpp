@@ -18,12 +18,13 @@ hipError_t launch_quant_ptpc_f32(const void* x, int64_t rows, int64_t K, void* q
 hipError_t launch_gemm_a4w4(const void* qa, const void* sa, const void* qw, const void* sw, void* y,
                             int64_t M, int64_t N, int64_t K, void* workspace, hipStream_t st);
 size_t gemm_a4w4_workspace_bytes(int64_t M, int64_t N, int64_t K);
-// The same GEMM with its workspace in a static per-device array of kGemmScratchBytes (no allocation);
-// the caller rejects shapes whose workspace is larger.
-constexpr size_t kGemmScratchBytes = (size_t)4 << 20 | 4096;
+// The same GEMM with its workspace in a static per-device array of kGemmScratchBytes (no allocation):
+// the largest workspace of any split-K plan (256 workgroups); the caller rejects shapes that need more.
+constexpr size_t kGemmScratchBytes = (size_t)8 << 20;
 hipError_t launch_gemm_a4w4_noalloc(const void* qa, const void* sa, const void* qw, const void* sw, void* y,
                                     int64_t M, int64_t N, int64_t K, hipStream_t st);
-// One-launch A4W4 layer: BF16 X -> MXFP4 (inside the GEMM's workgroups) -> BF16 Y.
+// A4W4 layer: BF16 X -> MXFP4 -> BF16 Y, in one launch for M <= 8 (quantization inside the split-K
+// GEMM's workgroups), else the quantizer and the GEMM.
 hipError_t launch_linear_a4w4(const void* x, const void* qw, const void* sw, void* y, int64_t M, int64_t N, int64_t K,
                               void* workspace, hipStream_t st);
 size_t linear_a4w4_workspace_bytes(int64_t M, int64_t N, int64_t K);

@@ -283,6 +283,13 @@ __device__ __forceinline__ uint32_t bf16x8_emax(uint4 x) {
     for (int j = 0; j < 4; ++j) emax = max(emax, max((w[j] >> 7) & 0xffu, (w[j] >> 23) & 0xffu));
     return emax;
 }
+// Maximum of v over the four lanes of a quad (lanes 4j .. 4j + 3), via DPP lane swaps (xor 1, then
+// xor 2): no LDS round trip.  Every lane of the quad must be active.
+__device__ __forceinline__ uint32_t quad_max(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));  // quad_perm [2,3,0,1]
+    return v;
+}
 // E8M0 scale byte of a block from its largest exponent field: max(E - 2, 0), 0xFF for NaN/Inf.
 __device__ __forceinline__ uint32_t mx_scale_of_emax(uint32_t emax) {
     return emax == 0xffu ? 0xffu : (emax > 2u ? emax - 2u : 0u);

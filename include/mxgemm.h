@@ -94,16 +94,15 @@ mx_status mx_quant_weight_f32(const float *w, int64_t N, int64_t K,
 
 /*
  * Bytes of workspace mx_gemm_a4w4_bf16 needs for this shape: nonzero for the
- * decode sizes that split K across workgroups - M <= 64, 32-column tiles that
- * would fill at most half the GPU (N <= 4096), K split into 4 or 8 parts of
- * 2048 K-values giving at least 128 workgroups of 128 columns; e.g. 4,198,400
- * bytes for (64, 4096, 8192) - and 0 otherwise (the (64, 7168, 8192) decode
- * layer runs the workspace-free decode kernel, measured faster there).
- * The workspace holds a 4 KB area of 32-bit counters (one per 32-column
- * group) and FP32 partial tiles after it.  It must be zero-filled (e.g.
- * hipMemset) before its first use; every call leaves it ready for the next
- * one (counters back at zero), for any shape.  Calls that share a workspace
- * must not run concurrently: issue them on one stream.
+ * decode sizes that split K across workgroups - M <= 64, K split into 4 or 8
+ * parts of 2048 K-values, 128-column tiles x parts between 128 and 256
+ * workgroups; e.g. 7,340,032 bytes for the (64, 7168, 8192) decode layer,
+ * 8 MiB at most - and 0 otherwise.  It depends on the shape only.  The
+ * workspace holds the FP32 partial slots through which the workgroups of a
+ * tile exchange their partial sums; a slot word reads 0 until written.  It
+ * must be zero-filled (e.g. hipMemset) before its first use; every call
+ * leaves it all zero again, for any shape.  Calls that share a workspace must
+ * not run concurrently: issue them on one stream.
  */
 size_t mx_gemm_a4w4_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
@@ -119,8 +118,13 @@ size_t mx_gemm_a4w4_workspace_bytes(int64_t M, int64_t N, int64_t K);
  * N, K) bytes, 16-byte aligned, zero-filled before first use (see there);
  * may be NULL when that size is 0, else MX_ERROR_WORKSPACE.  The split-K
  * decode kernel sums the K parts of each output in a fixed order, so results
- * do not depend on timing.  It relies on workgroups being dealt round-robin
- * to the XCDs (the parts of a tile meet in one XCD's L2).
+ * do not depend on timing.  Its workgroups wait for each other, so it runs
+ * only when its whole grid fits the device's CUs at once (one workgroup per
+ * CU); otherwise the workspace-free decode kernels run.  It relies on
+ * workgroups being dealt round-robin to the XCDs (the parts of a tile meet in
+ * one XCD's L2), and on no other work keeping CUs from the grid for long: a
+ * workgroup waiting for a partner gives up after about 0.3 s (the output is
+ * then wrong), so that no launch can hang.
  */
 mx_status mx_gemm_a4w4_bf16(const void *qa, const void *sa, const void *qw, const void *sw,
                             void *y_bf16, int64_t M, int64_t N, int64_t K,
@@ -130,11 +134,11 @@ mx_status mx_gemm_a4w4_bf16(const void *qa, const void *sa, const void *qw, cons
  * mx_gemm_a4w4_bf16 for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid allocation):
  * the same arguments without a workspace.  The split-K kernel's workspace is a
- * static device array of 4 MiB + 4 KiB per GPU, held from the library's load
- * until the process ends; it is zero when loaded and every call leaves it
- * ready for the next.  Shapes whose workspace would be larger (see
- * mx_gemm_a4w4_workspace_bytes) return MX_ERROR_WORKSPACE before anything is
- * enqueued.  The call itself allocates nothing.  All calls on one GPU share
+ * static device array of 8 MiB per GPU (the largest any shape needs), held
+ * from the library's load until the process ends; it is zero when loaded and
+ * every call leaves it zero again.  A shape whose workspace were larger would
+ * return MX_ERROR_WORKSPACE before anything is enqueued.  The call itself
+ * allocates nothing.  All calls on one GPU share
  * the array, so calls that overlap on one GPU (other streams, other threads)
  * race: issue them on one stream.  Results equal mx_gemm_a4w4_bf16's bit for
  * bit.
@@ -143,10 +147,12 @@ mx_status mx_gemm_a4w4_bf16_noalloc(const void *qa, const void *sa, const void *
                                     void *y_bf16, int64_t M, int64_t N, int64_t K, void *stream);
 
 /*
- * Bytes of workspace mx_linear_a4w4_bf16 needs for this shape (same rules as
- * mx_gemm_a4w4_workspace_bytes: zero-filled before first use, left ready by
- * every call, not shared by concurrent calls; one zero-filled buffer of the
- * larger size may serve both entry points on one stream).
+ * Bytes of workspace mx_linear_a4w4_bf16 needs for this shape: the split-K
+ * partial slots (first 8 MiB), then room for the activation codes and scales
+ * of the two-launch path; e.g. 8,667,136 for (64, 7168, 8192).  Same rules as
+ * mx_gemm_a4w4_workspace_bytes: zero-filled before first use, the first 8 MiB
+ * left zero by every call, not shared by concurrent calls; one zero-filled
+ * buffer of the larger size may serve both entry points on one stream.
  */
 size_t mx_linear_a4w4_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
@@ -161,13 +167,17 @@ size_t mx_linear_a4w4_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *   y_bf16 [M, N]  out, 2-byte aligned
  *   workspace  at least mx_linear_a4w4_workspace_bytes(M, N, K) bytes, 256-byte
  *              aligned, zero-filled before first use.
- * K > 0 and K % 128 == 0.  At decode sizes (M <= 64, K a multiple of 1024 that
- * splits into 2, 4 or 8 parts, enough 128-column tiles for half the GPU, sw
- * 16-byte aligned) this is ONE kernel launch: every workgroup quantizes its K
- * part of X into LDS, bit for bit as mx_quant_act_bf16, and runs the split-K
- * GEMM on it, so no activation codes are written to memory.  Other shapes run
- * mx_quant_act_bf16 (codes and scales in the workspace) and mx_gemm_a4w4_bf16
- * in two launches on the same stream.
+ * K > 0 and K % 128 == 0.  For M <= 8 (K a multiple of 1024 that splits into
+ * 2, 4 or 8 parts, enough 128-column tiles for half the GPU, sw 16-byte
+ * aligned, the grid resident at once) this is ONE kernel launch: every
+ * workgroup quantizes its K part of X into LDS, bit for bit as
+ * mx_quant_act_bf16, and runs the split-K GEMM on it, so no activation codes
+ * are written to memory.  Other shapes run mx_quant_act_bf16 (codes and
+ * scales in the workspace) and mx_gemm_a4w4_bf16 (its split-K partials in the
+ * workspace too) in two launches on the same stream: with more rows, every
+ * workgroup quantizing all M rows of its K part costs more than the second
+ * launch (measured at N = 7168, K = 8192: one launch 8.6 vs 9.9 us at M = 1,
+ * 11.4 vs 10.4 us at M = 16).
  */
 mx_status mx_linear_a4w4_bf16(const void *x_bf16, const void *qw, const void *sw, void *y_bf16,
                               int64_t M, int64_t N, int64_t K,

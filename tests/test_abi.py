@@ -76,15 +76,20 @@ def test_gemm_argument_errors(mx):
     assert g4(FAKE, FAKE, FAKE, FAKE, FAKE + 1, 8, 8, 128) == mx.MX_ERROR_MISALIGNED
     assert g4(None, None, None, None, None, 0, 8, 128) == mx.MX_SUCCESS
     assert g4(None, None, None, None, None, 8, 0, 128) == mx.MX_SUCCESS
-    # the split-K decode GEMM (only where the decode rings would fill at most half the CUs): a 4 KB counter
-    # area + tiles x K parts x 4 waves x fragments x 4 KB of partials
-    assert mx.mx_gemm_a4w4_workspace_bytes(64, 4096, 8192) == 4096 + 32 * 4 * 4 * 2 * 4096
-    assert mx.mx_gemm_a4w4_workspace_bytes(32, 2048, 16384) == 4096 + 16 * 8 * 4 * 1 * 4096
-    assert mx.mx_gemm_a4w4_workspace_bytes(64, 7168, 8192) == 0     # the decode rings
-    # the one-launch layer: split-K wherever a plan keeps half the CUs busy, else codes + GEMM
-    assert mx.mx_linear_a4w4_workspace_bytes(64, 7168, 8192) == 4096 + 56 * 4 * 4 * 2 * 4096
-    assert mx.mx_linear_a4w4_workspace_bytes(1, 7168, 8192) == 4096 + 56 * 4 * 4 * 1 * 4096
-    assert mx.mx_linear_a4w4_workspace_bytes(100, 7168, 8192) == 4096 + 100 * 4096 + 25600  # codes + scales
+    # the split-K decode GEMM (M <= 64, K parts of 2048, at least 4 of them, 128 .. 256 workgroups): tiles x
+    # K parts x 4 waves x fragments x 4 KB of partial slots
+    assert mx.mx_gemm_a4w4_workspace_bytes(64, 4096, 8192) == 32 * 4 * 4 * 2 * 4096
+    assert mx.mx_gemm_a4w4_workspace_bytes(32, 2048, 16384) == 16 * 8 * 4 * 1 * 4096
+    assert mx.mx_gemm_a4w4_workspace_bytes(64, 7168, 8192) == 56 * 4 * 4 * 2 * 4096
+    assert mx.mx_gemm_a4w4_workspace_bytes(1, 7168, 8192) == 56 * 4 * 4 * 1 * 4096
+    assert mx.mx_gemm_a4w4_workspace_bytes(64, 4096, 16384) == 8 << 20     # 256 workgroups: the largest
+    assert mx.mx_gemm_a4w4_workspace_bytes(64, 7168, 16384) == 0    # 448 workgroups: not resident at once
+    assert mx.mx_gemm_a4w4_workspace_bytes(64, 7168, 4096) == 0     # 2 parts: the decode rings
+    # the layer: room for the one-launch path's partial slots and for the two-launch path's codes and
+    # scales, which sit past the largest partial area (8 MiB)
+    assert mx.mx_linear_a4w4_workspace_bytes(64, 7168, 8192) == (8 << 20) + 64 * 4096 + 64 * 256
+    assert mx.mx_linear_a4w4_workspace_bytes(1, 7168, 8192) == (8 << 20) + 4096 + 256
+    assert mx.mx_linear_a4w4_workspace_bytes(100, 7168, 8192) == (8 << 20) + 100 * 4096 + 25600
     assert mx.mx_gemm_a4w4_workspace_bytes(64, 128 * 256 + 1, 8192) == 0  # more than 256 tiles
     assert mx.mx_gemm_a4w4_workspace_bytes(65, 7168, 8192) == 0     # two row halves, no workspace
     assert mx.mx_gemm_a4w4_workspace_bytes(64, 512, 8192) == 0      # too few tiles to split
@@ -92,7 +97,7 @@ def test_gemm_argument_errors(mx):
     assert g4(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 4096, 8192, None, 0) == mx.MX_ERROR_WORKSPACE
     assert g4(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 4096, 8192, FAKE, 1024) == mx.MX_ERROR_WORKSPACE
     na = mx.mx_gemm_a4w4_bf16_noalloc
-    assert na(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 4096, 16384) == mx.MX_ERROR_WORKSPACE   # needs 8 MiB of scratch
+    # (no call with valid arguments here: it would reach the device with fake pointers)
     assert na(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 8, 96) == mx.MX_ERROR_UNSUPPORTED_SHAPE
     assert na(FAKE, None, FAKE, FAKE, FAKE, 64, 4096, 8192) == mx.MX_ERROR_INVALID_VALUE
     assert na(FAKE, FAKE, FAKE, FAKE, FAKE + 1, 64, 4096, 8192) == mx.MX_ERROR_MISALIGNED

@@ -69,7 +69,9 @@ SHAPES = [(1, 256, 128), (3, 100, 384), (16, 7168, 1024), (17, 33, 256), (37, 10
           (1300, 7000, 512), (2600, 4001, 512), (65, 520, 4096), (127, 1000, 8192), (96, 77, 2048),
           # the 512-K LDS-staged decode kernel at 17..32 and 65..128 rows (K % 2048 != 0, or K > 8192), and
           # the register-staged decode kernel at 33..64 and 65..128 rows (K % 512 != 0), e.g. a 7168-wide input
-          (24, 300, 7168), (100, 300, 7168), (100, 77, 10240), (48, 100, 384), (100, 100, 640)]
+          (24, 300, 7168), (100, 300, 7168), (100, 77, 10240), (48, 100, 384), (100, 100, 640),
+          # the decode rings at the o_proj width where no split-K plan applies (2 or 3 parts of 2048)
+          (64, 7168, 4096), (1, 7168, 6144)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)

@@ -2,13 +2,13 @@
 activations with A4W4 dispatch: "Kimi-K3 DSpark O-Proj-only MXFP4", section "Exact quantization
 coverage"), through the C ABI.
 
-At decode sizes it is one kernel that quantizes each K part of X inside the split-K GEMM's workgroups.
+For M <= 8 it is one kernel that quantizes each K part of X inside the split-K GEMM's workgroups; above
+that (and where no split-K plan exists) it runs the quantizer, then the GEMM.
   * Against the oracle: the oracle quantizes X and forms the exact GEMM; the GPU layer must be within
     |gpu - exact| <= 2^-8 |exact| + 1e-6 sum|a w| on every output.
-  * Against the two calls (mx_quant_act_bf16, then mx_gemm_a4w4_bf16) on shapes where that GEMM takes
-    the same split-K kernel: identical bits, which also shows the in-kernel quantization matches the
-    quantizer bit for bit - including rows of zeros, subnormals, huge values, ties and NaN/Inf.
-Shapes with no one-launch plan (M > 64, K % 1024 != 0) take the two-launch path and are checked too.
+  * Against the two calls (mx_quant_act_bf16, then mx_gemm_a4w4_bf16) on one-launch shapes where that
+    GEMM takes the same split-K kernel: identical bits, which also shows the in-kernel quantization
+    matches the quantizer bit for bit - including rows of zeros, subnormals, huge values, ties and NaN/Inf.
 """
 import numpy as np
 import pytest
@@ -39,14 +39,16 @@ def _weight(orc, seed, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [
-    (64, 7168, 8192),   # the o_proj decode layer: 64 rows, 8 slabs per part, 4 parts
-    (16, 7168, 8192),   # 32-row fragments
-    (1, 7168, 8192),
-    (5, 4000, 4096),    # 32 rows, 4 slabs, 4 parts, ragged last tile
-    (33, 8100, 4096),   # 64 rows, 8 slabs, 2 parts
-    (64, 2900, 8192),   # 64 rows, 4 slabs, 8 parts, idle workgroups
-    (100, 3000, 2048),  # no one-launch plan (M > 64): quantizer + GEMM
-    (24, 5000, 640),    # no plan (K % 1024 != 0)
+    (1, 7168, 8192),    # one launch: the o_proj layer at M = 1, 8 slabs per part, 4 parts
+    (8, 7168, 8192),    # one launch, the largest M that takes it
+    (5, 4000, 4096),    # one launch: 4 slabs, 4 parts, ragged last tile
+    (3, 2900, 8192),    # one launch: 4 slabs, 8 parts, idle workgroups
+    (8, 2048, 16384),   # one launch: 8 slabs, 8 parts
+    (64, 7168, 8192),   # quantizer + split-K GEMM: the o_proj decode layer
+    (16, 7168, 8192),   # quantizer + split-K GEMM, 32-row fragments
+    (33, 8100, 4096),   # quantizer + decode ring (2 parts: no GEMM split)
+    (100, 3000, 2048),  # quantizer + GEMM (M > 64)
+    (24, 5000, 640),    # quantizer + GEMM (K % 1024 != 0)
 ])
 def test_linear_matches_oracle(mx, orc, M, N, K):
     import torch
@@ -74,7 +76,7 @@ def _special_rows(M, K, seed):
     return x
 
 
-@pytest.mark.parametrize("M,N,K", [(64, 4096, 8192), (32, 2048, 16384), (20, 2048, 16384)])
+@pytest.mark.parametrize("M,N,K", [(8, 4096, 8192), (8, 2048, 16384), (7, 7168, 8192)])
 def test_linear_bit_identical_to_two_calls(mx, orc, M, N, K):
     import torch
     assert mx.mx_gemm_a4w4_workspace_bytes(M, N, K) > 0, "the two-call GEMM should take the split-K kernel"
@@ -93,9 +95,9 @@ def test_linear_bit_identical_to_two_calls(mx, orc, M, N, K):
 
 def test_linear_repeatable_and_shares_workspace(mx, orc):
     """Repeated one-call layers give identical bits; one zero-filled workspace serves layer and GEMM calls
-    of different shapes in turn (each leaves the counters at zero)."""
+    of different shapes in turn (each leaves the partial area, the first 8 MiB, all zero)."""
     import torch
-    shapes = [(64, 7168, 8192), (5, 4000, 4096), (100, 3000, 2048)]
+    shapes = [(64, 7168, 8192), (5, 4000, 4096), (100, 3000, 2048), (2, 7168, 8192)]
     size = max(max(mx.mx_linear_a4w4_workspace_bytes(*s), mx.mx_gemm_a4w4_workspace_bytes(*s)) for s in shapes)
     size = max(size, mx.mx_gemm_a4w4_workspace_bytes(64, 4096, 8192))
     ws = torch.zeros(size, dtype=torch.uint8, device="cuda")
@@ -120,4 +122,4 @@ def test_linear_repeatable_and_shares_workspace(mx, orc):
         torch.cuda.synchronize()
         for a, b in zip(first, again):
             assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "repeat %d differs" % rep
-    assert int(ws[:4096].count_nonzero()) == 0
+    assert int(ws[:8 << 20].count_nonzero()) == 0

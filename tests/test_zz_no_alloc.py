@@ -1,7 +1,8 @@
 """The allocation-free GEMM entry point mx_gemm_a4w4_bf16_noalloc (workspace in a static per-GPU array),
 through the C ABI, against mx_gemm_a4w4_bf16 with a caller workspace: identical bits, on calls in a
-row - a split-K shape, then a smaller one, then a shape that needs no scratch, then the first again -
-and within tolerance of the oracle's exact GEMM."""
+row - the o_proj decode shape (split-K), then a smaller split-K shape, then a shape that needs no
+scratch, then another split-K shape and the first again - and within tolerance of the oracle's exact
+GEMM."""
 import numpy as np
 import pytest
 
@@ -20,8 +21,9 @@ def _ops(orc, seed, M, N, K):
 
 def test_noalloc_matches_workspace_entry(mx, orc):
     import torch
-    shapes = [(64, 4096, 8192), (20, 2000, 16384), (64, 7168, 8192), (64, 4096, 8192)]
+    shapes = [(64, 7168, 8192), (20, 2000, 16384), (65, 7168, 8192), (64, 4096, 8192), (64, 7168, 8192)]
     assert mx.mx_gemm_a4w4_workspace_bytes(*shapes[0]) > mx.mx_gemm_a4w4_workspace_bytes(*shapes[1]) > 0
+    assert mx.mx_gemm_a4w4_workspace_bytes(*shapes[2]) == 0
     s = torch.cuda.current_stream().cuda_stream
     cache = {}
     for i, (M, N, K) in enumerate(shapes):
