@@ -212,6 +212,9 @@ class A8W8Layer:
         self.qa = [torch.empty((M, K), dtype=torch.uint8, device=ctx.dev) for _ in range(rotate)]
         self.sa = [torch.empty((M,), dtype=torch.float32, device=ctx.dev) for _ in range(rotate)]
         self.y = [torch.empty((M, N), dtype=torch.bfloat16, device=ctx.dev) for _ in range(rotate)]
+        # split-K workspace (decode sizes): allocated and zeroed once, outside the timed region
+        self.ws = ctx.mx.gemm_a8w8_ptpc_workspace_bytes(M, N, K)
+        self.wbuf = torch.zeros(max(self.ws, 256), dtype=torch.uint8, device=ctx.dev)
 
     def quant(self, r):
         mx, ctx = self.ctx.mx, self.ctx
@@ -222,7 +225,7 @@ class A8W8Layer:
         mx, ctx = self.ctx.mx, self.ctx
         return lambda: ok(mx.gemm_a8w8_ptpc_bf16(self.qa[r].data_ptr(), self.sa[r].data_ptr(), self.qw[r].data_ptr(),
                                                  self.sw[r].data_ptr(), self.y[r].data_ptr(), self.M, self.N, self.K,
-                                                 ctx.stream()), "gemm_a8w8_ptpc_bf16")
+                                                 self.wbuf.data_ptr(), self.ws, ctx.stream()), "gemm_a8w8_ptpc_bf16")
 
     def step(self, r):
         q, g = self.quant(r), self.gemm(r)

@@ -179,14 +179,24 @@ MX_API mx_status ptpc_quant_weight_f32(const float* w, int64_t N, int64_t K, voi
     return quant_ptpc(true, w, N, K, q, s, stream);
 }
 
+MX_API size_t gemm_a8w8_ptpc_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (check_gemm(M, N, K) != MX_SUCCESS || M == 0 || N == 0) return 0;
+    return mx::gemm_a8w8_workspace_bytes(M, N, K);
+}
+
 MX_API mx_status gemm_a8w8_ptpc_bf16(const void* qa, const float* sa, const void* qw, const float* sw, void* y_bf16,
-                                     int64_t M, int64_t N, int64_t K, void* stream) {
+                                     int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
     mx_status st = check_gemm(M, N, K);
     if (st != MX_SUCCESS) return st;
     if (M == 0 || N == 0) return MX_SUCCESS;
     if (!qa || !sa || !qw || !sw || !y_bf16) return MX_ERROR_INVALID_VALUE;
-    if (!aligned(qa, 16) || !aligned(qw, 16) || !aligned(sa, 4) || !aligned(sw, 4) || !aligned(y_bf16, 2))
+    const size_t need = gemm_a8w8_ptpc_workspace_bytes(M, N, K);
+    if (workspace_bytes < need || (need && !workspace)) return MX_ERROR_WORKSPACE;
+    if (!aligned(qa, 16) || !aligned(qw, 16) || !aligned(sa, 4) || !aligned(sw, 4) || !aligned(y_bf16, 2) ||
+        (need && !aligned(workspace, 16)))
         return MX_ERROR_MISALIGNED;
     if ((st = check_device()) != MX_SUCCESS) return st;
-    return launched(mx::launch_gemm_a8w8(qa, sa, qw, sw, y_bf16, M, N, K, reinterpret_cast<hipStream_t>(stream)));
+    return launched(mx::launch_gemm_a8w8(qa, sa, qw, sw, y_bf16, M, N, K, workspace,
+                                         reinterpret_cast<hipStream_t>(stream)));
 }

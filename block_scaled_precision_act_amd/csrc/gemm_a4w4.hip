@@ -28,11 +28,8 @@
 
 namespace mx {
 
-namespace {
-
-// Compute units of the current device (cached per device); 0 if the query fails.
-constexpr int kMaxDevices = 64;
 int device_cus() {
+    constexpr int kMaxDevices = 64;
     static int cus[kMaxDevices];
     static std::once_flag once[kMaxDevices];
     int dev = 0;
@@ -43,6 +40,8 @@ int device_cus() {
     });
     return cus[dev];
 }
+
+namespace {
 
 // The split-K plan of a shape: slabs (K = 256) per part, parts, tiles, fragments; nsl == 0 if none.  Every
 // plan keeps at least half of the 256 CUs busy with at most 256 workgroups (it depends on the shape only, so

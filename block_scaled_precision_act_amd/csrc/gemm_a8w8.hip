@@ -1,14 +1,69 @@
 // gemm_a8w8.hip - PTPC FP8 A8W8 GEMM entry (E4M3 operands with per-token and
 // per-output-channel FP32 scales: "Kimi-K3-DSpark-FP8-PTPC", section "Phase 1
-// FP8 PTPC Quantization").  Same kernels as the A4W4 path, FP8 operands, unit
-// MFMA scales and the two FP32 scales applied in the epilogue.
+// FP8 PTPC Quantization").  E4M3 codes are widened exactly to FP16 for the
+// MFMAs; the two FP32 scales are applied in the epilogue.
+//
+// 33 <= M <= 64 with K a multiple of 8192 or 16384 (K parts of 2048) takes the
+// split-K kernel (gemm_splitk_fp8 in gemm_splitk.hpp), which needs the caller's
+// workspace, when its grid (128 .. 256 workgroups) fits the device at once.
+// Measured (graph-replayed, rotated weights, N = 7168, K = 8192): M = 64 15.7
+// vs 18.6 us for the decode ring, M = 48 14.6 vs 17.2 us; at M <= 32 the ring
+// is as fast or faster (M = 1 11.4 vs 13.0, M = 32 13.4 vs 13.1 us), so it
+// keeps those.  Everything else runs the kernels of gemm_kernels.hpp.
 #include "gemm_kernels.hpp"
+#include "gemm_splitk.hpp"
 #include "launch.hpp"
 
 namespace mx {
 
+namespace {
+
+constexpr int kNsl8 = 16;  // slabs (K = 128) per K part
+
+// parts and tiles of the FP8 split-K plan; kp == 0 if none (depends on the shape only)
+struct Split8 {
+    int kp = 0, tiles = 0;
+    int grid() const { return 8 * kp * ((tiles + 7) / 8); }
+    bool fits_device() const { return kp != 0 && grid() <= device_cus(); }
+};
+
+Split8 split8_plan(int64_t M, int64_t N, int64_t K) {
+    Split8 p;
+    if (M < 33 || M > 64 || K % (128 * kNsl8) != 0 || N < 1 || N > (int64_t)sk::kTN * sk::kMaxGrid) return p;
+    const int64_t kp = K / (128 * kNsl8);
+    if (kp != 4 && kp != 8) return p;
+    const int tiles = (int)((N + sk::kTN - 1) / sk::kTN);
+    if ((int64_t)tiles * kp < 128 || 8 * kp * ((tiles + 7) / 8) > sk::kMaxGrid) return p;
+    p.kp = (int)kp;
+    p.tiles = tiles;
+    return p;
+}
+
+}  // namespace
+
+size_t gemm_a8w8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    const Split8 p = split8_plan(M, N, K);
+    return p.kp ? sk::workspace_bytes(p.tiles, p.kp, 2) : 0;
+}
+
 hipError_t launch_gemm_a8w8(const void* qa, const float* sa, const void* qw, const float* sw, void* y, int64_t M,
-                            int64_t N, int64_t K, hipStream_t st) {
+                            int64_t N, int64_t K, void* workspace, hipStream_t st) {
+    const Split8 p = split8_plan(M, N, K);
+    if (workspace && p.fits_device()) {
+        const dim3 grid((unsigned)p.grid()), block(256);
+        const uint8_t* a = reinterpret_cast<const uint8_t*>(qa);
+        const uint8_t* w = reinterpret_cast<const uint8_t*>(qw);
+        uint16_t* out = reinterpret_cast<uint16_t*>(y);
+        uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+        // a 3-slot ring: 2 slabs in flight per wave measured faster than 3 or 5 (M = 64: 15.7, 16.3, 18.6 us)
+        if (p.kp == 4)
+            hipLaunchKernelGGL((gemm_splitk_fp8<2, 3, kNsl8, 4>), grid, block, 0, st, a, sa, w, sw, out, (int)M, (int)N,
+                               (int)K, p.tiles, ws);
+        else
+            hipLaunchKernelGGL((gemm_splitk_fp8<2, 3, kNsl8, 8>), grid, block, 0, st, a, sa, w, sw, out, (int)M, (int)N,
+                               (int)K, p.tiles, ws);
+        return hipGetLastError();
+    }
     return launch_gemm<true>(qa, sa, qw, sw, y, M, N, K, st);
 }
 

@@ -406,4 +406,163 @@ __global__ __launch_bounds__(256, 1) void gemm_splitk_fp4(const uint8_t* __restr
     }
 }
 
+// ---------------------------------------------------------------------------------------------------------
+// The A8W8 (PTPC FP8) decode GEMM in the same decomposition ("Kimi-K3-DSpark-FP8-PTPC", section "Phase 1
+// FP8 PTPC Quantization": E4M3 weights and per-token E4M3 activations, FP32 per-token and
+// per-output-channel scales).  An E4M3 activation row is 1 byte per value, so a K part of 64 rows does not
+// fit in LDS beside the weight rings; instead the activation slabs stream through a ring shared by the
+// workgroup's waves, each wave copying its share of every slab beside its own weight rows.  A slab is
+// K = 128 (128 bytes per row); its 32 MF activation rows are read by all 4 waves, so a barrier per slab
+// separates the copies of slab j from its reads, and a slot is refilled only after the next barrier (when
+// every wave has read it): S - 1 slabs stay in flight.  E4M3 widens exactly to FP16 and the products run
+// on the 32 x 32 x 16 FP16 MFMA, as in the ring kernel.  The K parts' partial sums meet in the same tail;
+// the scales are applied to the sum, acc sA sW in FP64, then BF16.
+namespace sk8 {
+constexpr int kSlab = 128;  // code bytes per row per slab (K = 128)
+template <int MF, int S>
+struct Cfg {
+    static constexpr int kArows = 32 * MF;
+    static constexpr int kActSlab = kArows * kSlab;      // shared activation slot
+    static constexpr int kWSlab = 32 * kSlab;            // a wave's weight slot
+    static constexpr int kSlot = kActSlab + 4 * kWSlab;
+    static constexpr int kLds = S * kSlot;
+    static constexpr int kCopies = MF + 4;              // per wave and slab: activation share, weight rows
+    static_assert(S >= 3 && S * kCopies <= 63, "vmcnt");
+    static_assert(kLds <= 160 * 1024, "LDS");
+};
+}  // namespace sk8
+
+template <int MF, int S, int NSL, int KP>
+__global__ __launch_bounds__(256, 1) void gemm_splitk_fp8(const uint8_t* __restrict__ qa, const float* __restrict__ sa,
+                                                          const uint8_t* __restrict__ qw, const float* __restrict__ sw,
+                                                          uint16_t* __restrict__ y, int M, int N, int K, int tiles,
+                                                          uint8_t* __restrict__ ws) {
+    using C = sk8::Cfg<MF, S>;
+    using sk::key;
+    const int b = blockIdx.x;
+    const int slot8 = b >> 3;
+    const int q = slot8 % KP;                    // K part
+    const int t = (slot8 / KP) * 8 + (b & 7);    // tile
+    if (t >= tiles) return;                      // the whole workgroup, before any barrier
+
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[C::kLds];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l32 = lane & 31, h = lane >> 5;
+    const int n0 = t * sk::kTN;
+    const int s0 = q * NSL;                      // first slab of the part (in K = 128 units)
+    const int rot = (t + 3 * q) % NSL;           // local slab j reads slab s0 + (j + rot) % NSL
+
+    // Copies of local slab j into slot j % S: activation rows 8c .. 8c+7 for c = MF wave .. MF wave + MF - 1
+    // (rows at or past M read row M - 1; a copy whose rows all lie past M reads one line for all its lanes:
+    // those rows only feed outputs that are never stored), then this wave's weight rows n0 + 32 wave + 8i ..
+    // +7.  The lane fills chunk lane % 8 of its row with logical chunk (lane % 8) ^ key(row).
+    const uint8_t* arow[MF];
+#pragma unroll
+    for (int e = 0; e < MF; ++e) {
+        const int c = wave * MF + e;
+        const int r = 8 * c + (lane >> 3);
+        arow[e] = 8 * c >= M ? qa + (int64_t)(M - 1) * K : qa + (int64_t)min(r, M - 1) * K + 16 * ((lane & 7) ^ key(r));
+    }
+    const uint8_t* wrow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 8 * i + (lane >> 3);
+        wrow[i] = qw + (int64_t)min(n0 + 32 * wave + r, N - 1) * K + 16 * ((lane & 7) ^ key(r));
+    }
+    auto issue = [&](int j) {
+        uint8_t* const slot = lds + (j % S) * C::kSlot;
+        const int64_t koff = (int64_t)(s0 + (j + rot) % NSL) * sk8::kSlab;
+#pragma unroll
+        for (int e = 0; e < MF; ++e) g2lds16(arow[e] + koff, slot + 1024 * (wave * MF + e));  // reused by 7 CUs
+#pragma unroll
+        for (int i = 0; i < 4; ++i) g2lds16_nt(wrow[i] + koff, slot + C::kActSlab + wave * C::kWSlab + 1024 * i);
+    };
+#pragma unroll
+    for (int j = 0; j < S; ++j) issue(j);
+
+    const uint32_t base = lds_addr(lds);
+    const int wkey = key(l32);
+    const uint32_t woff = C::kActSlab + wave * C::kWSlab + l32 * sk8::kSlab;
+    uint32_t xoff[MF];
+    int xkey[MF];
+#pragma unroll
+    for (int g = 0; g < MF; ++g) {
+        xoff[g] = (32 * g + l32) * sk8::kSlab;
+        xkey[g] = key(32 * g + l32);
+    }
+    v16f acc[MF];
+#pragma unroll
+    for (int g = 0; g < MF; ++g)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[g][i] = 0.f;
+
+    static_for<NSL>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        // issued so far: slabs 0 .. S - 1 by the prologue, then one per earlier slab from slab 1 on, i.e.
+        // 0 .. j + S - 2 for j >= 1; those after slab j may still be in flight
+        constexpr int kIssued = j == 0 ? S - 1 : (j + S - 2 < NSL - 1 ? j + S - 2 : NSL - 1);
+        constexpr int kLater = kIssued - j;
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<kLater * C::kCopies>();  // this wave's copies of slab j have landed
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();       // every wave's: slab j is whole, and slab j - 1 is read
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (j >= 1 && j - 1 + S < NSL) issue(j - 1 + S);  // into the slot of slab j - 1
+        __builtin_amdgcn_sched_barrier(0);
+        const uint32_t sb = base + (j % S) * C::kSlot;
+        v4u wv[4], xv[4][MF];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            wv[tt] = lds_read16(sb + woff + 16 * ((4 * h + tt) ^ wkey));
+#pragma unroll
+            for (int g = 0; g < MF; ++g) xv[tt][g] = lds_read16(sb + xoff[g] + 16 * ((4 * h + tt) ^ xkey[g]));
+        }
+        lds_wait_codes<MF>(wv, xv);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            const v8h w0 = e4m3x8_to_f16x8(wv[tt][0], wv[tt][1]);
+            const v8h w1 = e4m3x8_to_f16x8(wv[tt][2], wv[tt][3]);
+#pragma unroll
+            for (int g = 0; g < MF; ++g) {
+                acc[g] = mfma32_f16(w0, e4m3x8_to_f16x8(xv[tt][g][0], xv[tt][g][1]), acc[g]);
+                acc[g] = mfma32_f16(w1, e4m3x8_to_f16x8(xv[tt][g][2], xv[tt][g][3]), acc[g]);
+            }
+        }
+    });
+
+    // D[n][m] of fragment g: lane l holds column m = 32 g + l32 and rows n = 8 i + 4 h + e in register 4 i + e.
+    const int nw = n0 + 32 * wave + 4 * h;
+    const bool vec_ok = (N & 3) == 0 && (reinterpret_cast<uintptr_t>(y) & 7) == 0;
+    auto store_one = [&](int g, int i, const v4f& v) {  // acc sA sW, then BF16
+        const int m = 32 * g + l32;
+        if (m >= M) return;
+        const int n = nw + 8 * i;
+        const float sam = sa[m];
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = ptpc_scaled(v[e], sam, sw[min(n + e, N - 1)]);
+        uint16_t* dst = y + (int64_t)m * N + n;
+        if (vec_ok && n + 3 < N) {
+            uint2 pk;
+            pk.x = bf16x2_rne(o[0], o[1]);
+            pk.y = bf16x2_rne(o[2], o[3]);
+            *reinterpret_cast<uint2*>(dst) = pk;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (n + e < N) dst[e] = (uint16_t)(bf16x2_rne(o[e], 0.f) & 0xffffu);
+        }
+    };
+    v4f mine[MF][4];
+#pragma unroll
+    for (int g = 0; g < MF; ++g)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mine[g][i] = v4f{acc[g][4 * i], acc[g][4 * i + 1], acc[g][4 * i + 2], acc[g][4 * i + 3]};
+    wait_vmcnt<0>();  // no copy past the last slab is issued; nothing is in flight here
+    sk::tail_sum<MF, KP>(mine, ws, (int)sk::workspace_bytes(tiles, KP, MF), t, q, wave, lane, store_one);
+}
+
 }  // namespace mx

@@ -33,6 +33,10 @@ hipError_t launch_a4w4_grouped(const void* qa, const void* sa, const void* qw, c
                                const int32_t* offsets, int64_t G, int64_t max_rows, int64_t N, int64_t K,
                                hipStream_t st);
 hipError_t launch_gemm_a8w8(const void* qa, const float* sa, const void* qw, const float* sw, void* y,
-                            int64_t M, int64_t N, int64_t K, hipStream_t st);
+                            int64_t M, int64_t N, int64_t K, void* workspace, hipStream_t st);
+size_t gemm_a8w8_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+// Compute units of the current device (cached per device); 0 if the query fails.
+int device_cus();
 
 }  // namespace mx

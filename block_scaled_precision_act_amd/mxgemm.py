@@ -61,7 +61,9 @@ def lib() -> ctypes.CDLL:
         L.mx_gemm_a4w4_workspace_bytes.restype = ctypes.c_size_t
         L.mx_gemm_a4w4_bf16.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, ctypes.c_size_t, vp]
         L.mx_gemm_a4w4_bf16.restype = i32
-        L.gemm_a8w8_ptpc_bf16.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
+        L.gemm_a8w8_ptpc_workspace_bytes.argtypes = [i64, i64, i64]
+        L.gemm_a8w8_ptpc_workspace_bytes.restype = ctypes.c_size_t
+        L.gemm_a8w8_ptpc_bf16.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, ctypes.c_size_t, vp]
         L.gemm_a8w8_ptpc_bf16.restype = i32
         L.mx_gemm_a4w4_grouped_bf16.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp]
         L.mx_gemm_a4w4_bf16_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
@@ -124,8 +126,12 @@ def ptpc_quant_weight_f32(w, N, K, q, s, stream=None) -> int:
     return lib().ptpc_quant_weight_f32(w, N, K, q, s, stream)
 
 
-def gemm_a8w8_ptpc_bf16(qa, sa, qw, sw, y, M, N, K, stream=None) -> int:
-    return lib().gemm_a8w8_ptpc_bf16(qa, sa, qw, sw, y, M, N, K, stream)
+def gemm_a8w8_ptpc_workspace_bytes(M, N, K) -> int:
+    return lib().gemm_a8w8_ptpc_workspace_bytes(M, N, K)
+
+
+def gemm_a8w8_ptpc_bf16(qa, sa, qw, sw, y, M, N, K, workspace=None, workspace_bytes=0, stream=None) -> int:
+    return lib().gemm_a8w8_ptpc_bf16(qa, sa, qw, sw, y, M, N, K, workspace, workspace_bytes, stream)
 
 
 # ------------------------------------------------------------------ tensor helpers
@@ -309,8 +315,10 @@ def gemm_a8w8(qa, sa, qw, sw, y=None):
     if qw.shape[1] != K or sa.shape[0] != M or sw.shape[0] != N:
         raise ValueError("inconsistent A8W8 operand shapes")
     y = _out(y, torch.bfloat16, (M, N), qa, "y")
+    ws = gemm_a8w8_ptpc_workspace_bytes(M, N, K)
+    wbuf = _workspace(qa.device, ws) if ws else None
     _ok(gemm_a8w8_ptpc_bf16(qa.data_ptr(), sa.data_ptr(), qw.data_ptr(), sw.data_ptr(), y.data_ptr(), M, N, K,
-                            _stream()), "gemm_a8w8_ptpc_bf16")
+                            wbuf.data_ptr() if ws else None, ws, _stream()), "gemm_a8w8_ptpc_bf16")
     return y
 
 

@@ -228,6 +228,17 @@ mx_status ptpc_quant_weight_f32(const float *w, int64_t N, int64_t K,
                                 void *q, float *s, void *stream);
 
 /*
+ * Bytes of workspace gemm_a8w8_ptpc_bf16 needs for this shape: nonzero for the
+ * decode sizes that split K across workgroups - 33 <= M <= 64, K split into 4
+ * or 8 parts of 2048, 128-column tiles x parts between 128 and 256
+ * workgroups; e.g. 7,340,032 bytes for (64, 7168, 8192) - and 0 otherwise.
+ * Same rules as mx_gemm_a4w4_workspace_bytes: it depends on the shape only,
+ * must be zero-filled before first use, is left all zero by every call, and
+ * calls that share a workspace must not run concurrently.
+ */
+size_t gemm_a8w8_ptpc_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
  * PTPC A8W8 GEMM: Y[m,n] = sa[m] * sw[n] * sum_k e4m3(qa[m,k]) * e4m3(qw[n,k]),
  * BF16 out (ATOM A8W8 of "Kimi-K3 DSpark O-Proj-only MXFP4", section "Exact
  * quantization coverage"; scales as in "Kimi-K3-DSpark-FP8-PTPC", section
@@ -235,9 +246,15 @@ mx_status ptpc_quant_weight_f32(const float *w, int64_t N, int64_t K,
  *   qa [M, K], sa [M]; qw [N, K], sw [N] (the (out_features, 1) scale);
  *   y_bf16 [M, N] out.  K > 0 and K % 128 == 0; qa, qw 16-byte aligned;
  *   sa, sw 4-byte aligned; y_bf16 2-byte aligned.
+ *   workspace: at least gemm_a8w8_ptpc_workspace_bytes(M, N, K) bytes,
+ *   16-byte aligned, zero-filled before first use; may be NULL when that size
+ *   is 0, else MX_ERROR_WORKSPACE.  At those decode sizes the K parts of each
+ *   output are summed across workgroups in a fixed order (deterministic), as
+ *   in mx_gemm_a4w4_bf16, when the grid fits the device's CUs at once.
  */
 mx_status gemm_a8w8_ptpc_bf16(const void *qa, const float *sa, const void *qw, const float *sw,
-                              void *y_bf16, int64_t M, int64_t N, int64_t K, void *stream);
+                              void *y_bf16, int64_t M, int64_t N, int64_t K,
+                              void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

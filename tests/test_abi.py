@@ -115,6 +115,17 @@ def test_gemm_argument_errors(mx):
     assert g8(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 8, 64) == mx.MX_ERROR_UNSUPPORTED_SHAPE
     assert g8(FAKE, FAKE + 2, FAKE, FAKE, FAKE, 8, 8, 128) == mx.MX_ERROR_MISALIGNED
     assert g8(None, None, None, None, None, 0, 0, 128) == mx.MX_SUCCESS
+    # the FP8 split-K decode GEMM: 33 <= M <= 64, K parts of 2048 (4 or 8), 128 .. 256 workgroups
+    w8 = mx.gemm_a8w8_ptpc_workspace_bytes
+    assert w8(64, 7168, 8192) == 56 * 4 * 4 * 2 * 4096
+    assert w8(33, 4096, 16384) == 32 * 8 * 4 * 2 * 4096
+    assert w8(32, 7168, 8192) == 0      # the decode ring (measured as fast at M <= 32)
+    assert w8(64, 7168, 4096) == 0      # 2 parts
+    assert w8(64, 7168, 16384) == 0     # 448 workgroups
+    assert w8(65, 7168, 8192) == 0
+    assert g8(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 7168, 8192, None, 0) == mx.MX_ERROR_WORKSPACE
+    assert g8(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 7168, 8192, FAKE, 1024) == mx.MX_ERROR_WORKSPACE
+    assert g8(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 7168, 8192, FAKE + 8, w8(64, 7168, 8192)) == mx.MX_ERROR_MISALIGNED
 
 
 def test_grouped_gemm_argument_errors(mx):

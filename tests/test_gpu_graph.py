@@ -57,22 +57,24 @@ def test_a4w4_layer_graph_replay(mx, M, N, K):
     _replays_match(mx, torch, layer, [qa, sa, y])
 
 
-# the decode ring (64) and the 256 x 224 FP8 tile (300)
-@pytest.mark.parametrize("M", [64, 300])
-def test_a8w8_layer_graph_replay(mx, M):
+# the decode ring (64 x 512 x 1024), the split-K kernel (64 x 4096 x 8192) and the 256 x 224 FP8 tile (300)
+@pytest.mark.parametrize("M,N,K", [(64, 512, 1024), (64, 4096, 8192), (300, 512, 1024)])
+def test_a8w8_layer_graph_replay(mx, M, N, K):
     import torch
-    K, N = 1024, 512
     x = bf16_dev(synth.act_normal(63, M, K))
     qw, sw = mx.quant_weight_ptpc(torch.from_numpy(synth.weight_normal(64, N, K, 0.01)).cuda())
     qa = torch.empty((M, K), dtype=torch.uint8, device="cuda")
     sa = torch.empty((M,), dtype=torch.float32, device="cuda")
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    wsb = mx.gemm_a8w8_ptpc_workspace_bytes(M, N, K)
+    assert (wsb > 0) == (K == 8192)
+    ws = torch.zeros(max(wsb, 256), dtype=torch.uint8, device="cuda")
 
     def layer():
         s = torch.cuda.current_stream().cuda_stream
         assert mx.ptpc_quant_act_fp8(x.data_ptr(), M, K, qa.data_ptr(), sa.data_ptr(), s) == 0
         assert mx.gemm_a8w8_ptpc_bf16(qa.data_ptr(), sa.data_ptr(), qw.data_ptr(), sw.data_ptr(), y.data_ptr(),
-                                      M, N, K, s) == 0
+                                      M, N, K, ws.data_ptr(), wsb, s) == 0
 
     _replays_match(mx, torch, layer, [qa, sa, y])
 

@@ -139,6 +139,7 @@ A8W8_FAMILIES = [
     ("decode ring, 64 rows", 64, 256, 1024),
     ("decode ring, two row halves", 100, 256, 1024),
     ("decode, register-staged", 24, 256, 384),
+    ("split-K decode, 64 rows", 48, 4096, 8192),
     ("256 x 224 tile", 300, 256, 1024),
     ("256 x 256 tile", 4096, 4096, 512),
 ]

@@ -116,3 +116,51 @@ def test_splitk_unaligned_scales_fall_back(mx, orc):
     out = mx.gemm_a4w4(to_dev(qa), shifted(sa), to_dev(qw), shifted(sw))
     ok, ratio, nbad = gemm_within_tolerance(bf16_host(out), y, ad)
     assert ok, "%d elements outside tolerance (max err/bound %.3g)" % (nbad, ratio)
+
+
+# The PTPC FP8 A8W8 decode GEMM in the same decomposition ("Kimi-K3-DSpark-FP8-PTPC", section "Phase 1 FP8
+# PTPC Quantization"): 33 <= M <= 64, K parts of 2048, activation slabs through a ring shared by the waves.
+SPLIT8_SHAPES = [
+    (64, 7168, 8192),    # the o_proj decode layer: 4 parts, 224 workgroups
+    (33, 4000, 8192),    # ragged last tile, 128 workgroups
+    (40, 4096, 16384),   # 8 parts, 256 workgroups
+    (50, 2900, 16384),   # 8 parts, 23 tiles: idle workgroups
+]
+
+
+def _operands8(orc, seed, M, N, K):
+    qa, sa = orc.ptpc_quant_bf16(synth.act_normal(seed, M, K), nthreads=NT)
+    qw, sw = orc.ptpc_quant_f32(synth.weight_normal(seed + 1, N, K, 0.01), nthreads=NT)
+    return qa, sa, qw, sw
+
+
+def _gemm8(mx, torch, qa, sa, qw, sw, ws):
+    M, K = qa.shape
+    N = qw.shape[0]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    st = mx.gemm_a8w8_ptpc_bf16(qa.data_ptr(), sa.data_ptr(), qw.data_ptr(), sw.data_ptr(), y.data_ptr(), M, N, K,
+                                ws.data_ptr(), ws.numel(), s)
+    assert st == 0, mx.status_string(st)
+    return y
+
+
+@pytest.mark.parametrize("M,N,K", SPLIT8_SHAPES)
+def test_splitk_fp8_matches_oracle(mx, orc, M, N, K):
+    import torch
+    wsb = mx.gemm_a8w8_ptpc_workspace_bytes(M, N, K)
+    assert wsb > 0, "shape should take the FP8 split-K path"
+    host = _operands8(orc, M * 17 + N + K, M, N, K)
+    y, ad = orc.gemm_a8w8_at(*host, nthreads=NT)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    dev = tuple(to_dev(a) for a in host)
+    yg = _gemm8(mx, torch, *dev, ws)
+    torch.cuda.synchronize()
+    ok, ratio, nbad = gemm_within_tolerance(bf16_host(yg), y, ad)
+    print("FP8 split-K %dx%dx%d: max err/bound %.4f" % (M, N, K, ratio))
+    assert ok, "%d elements outside tolerance (max err/bound %.3g)" % (nbad, ratio)
+    assert int(ws.count_nonzero()) == 0
+    # repeated calls: identical bits
+    for _ in range(2):
+        assert torch.equal(_gemm8(mx, torch, *dev, ws).view(torch.int16), yg.view(torch.int16))
+
