@@ -165,8 +165,9 @@ constexpr int kSpinLimit = 1 << 18;       // polls before a tail gives up (about
 // owners' slots, without waiting; an owner then polls its slot of every other part (coherent loads that
 // skip the CU's L1) until no word reads 0, adds the KP slices in K-part order, stores BF16 and clears the
 // slots it read.  Every store it waits for was issued by a resident wave, so the poll ends; a bounded
-// count of polls keeps the kernel finite even if the co-residency the host checked were broken (the sums
-// are then wrong).
+// count of polls keeps the kernel finite even if the co-residency the host checked were broken: the slice
+// is then stored as NaN, and a partial arriving after the owner gave up leaves the workspace non-zero, so
+// it must be zero-filled again before its next use.
 template <int MF, int KP, typename Store>
 __device__ __forceinline__ void tail_sum(const v4f (&mine)[MF][4], uint8_t* ws, int ws_range, int t, int q, int wave,
                                           int lane, Store&& store_one) {
@@ -199,7 +200,8 @@ __device__ __forceinline__ void tail_sum(const v4f (&mine)[MF][4], uint8_t* ws, 
     });
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(ws, (short)0, ws_range, kBufferWord3);
     v4u pv[KP - 1][U];
-    for (int it = 0; it < kSpinLimit; ++it) {
+    bool complete = false;
+    for (int it = 0; it < kSpinLimit && !complete; ++it) {
         uint32_t present = 1;
         static_for<KP - 1>([&](auto oc) {
             constexpr int o = decltype(oc)::value;
@@ -212,8 +214,8 @@ __device__ __forceinline__ void tail_sum(const v4f (&mine)[MF][4], uint8_t* ws, 
                 present &= (pv[o][uu][0] != 0u) & (pv[o][uu][1] != 0u) & (pv[o][uu][2] != 0u) & (pv[o][uu][3] != 0u);
             }
         });
-        if (__all(present)) break;
-        __builtin_amdgcn_s_sleep(1);
+        complete = __all(present);
+        if (!complete) __builtin_amdgcn_s_sleep(1);
     }
     v4f sum[U];
     static_for<KP>([&](auto pc) {
@@ -230,7 +232,8 @@ __device__ __forceinline__ void tail_sum(const v4f (&mine)[MF][4], uint8_t* ws, 
 #pragma unroll
     for (int uu = 0; uu < U; ++uu) {
         const int u = U * q + uu;
-        store_one(u / 4, u % 4, sum[uu]);
+        const float nan = __uint_as_float(0x7FC00000u);
+        store_one(u / 4, u % 4, complete ? sum[uu] : v4f{nan, nan, nan, nan});  // a timed-out wait shows as NaN
     }
     static_for<KP - 1>([&](auto oc) {
         constexpr int o = decltype(oc)::value;
@@ -563,6 +566,188 @@ __global__ __launch_bounds__(256, 1) void gemm_splitk_fp8(const uint8_t* __restr
         for (int i = 0; i < 4; ++i) mine[g][i] = v4f{acc[g][4 * i], acc[g][4 * i + 1], acc[g][4 * i + 2], acc[g][4 * i + 3]};
     wait_vmcnt<0>();  // no copy past the last slab is issued; nothing is in flight here
     sk::tail_sum<MF, KP>(mine, ws, (int)sk::workspace_bytes(tiles, KP, MF), t, q, wave, lane, store_one);
+}
+
+// ---------------------------------------------------------------------------------------------------------
+// 64 < M <= 128: the A4W4 split-K decomposition over two row halves.  A workgroup owns a 128-column tile,
+// one of KP K parts and one 64-row half of the activations, so a tile takes 2 KP workgroups (224 at
+// (128, 7168, 8192) with KP = 2) and each CU reads 1/KP of its half's activations beside 1/KP of the tile's
+// weight rows; the two halves of a tile read the same weight rows through one XCD's L2.  A K part of 64
+// rows is too wide for LDS here (4096 K-values: 128 KB), so the activation slabs stream through a ring
+// shared by the waves, as in gemm_splitk_fp8: each wave copies its share of every slab (K = 256, 8 KB)
+// beside its own weight rows, a barrier per slab separates the copies of slab j from its reads, and a slot
+// is refilled after the next barrier.  The part's activation and weight scales are copied once.  The K
+// parts of a (tile, half) meet in the slice-owner tail.
+namespace skr {
+template <int S, int NSL>
+struct Cfg {
+    static constexpr int kArows = 64;                        // rows per half
+    static constexpr int kActSlab = kArows * sk::kSlab;      // shared activation slot
+    static constexpr int kWSlab = 32 * sk::kSlab;            // a wave's weight slot
+    static constexpr int kSlot = kActSlab + 4 * kWSlab;
+    static constexpr int kP = NSL / 2;                       // 16-byte scale pieces per row
+    static constexpr int kScRows = kArows + sk::kTN;         // activation rows, then weight rows
+    static constexpr int kSc = kScRows * 8 * NSL;
+    static constexpr int kScCopies = kScRows * kP / 64;
+    static constexpr int kLds = S * kSlot + kSc;
+    static constexpr int kCopies = 2 + 4;                    // per wave and slab: activation share, weight rows
+    static_assert(S >= 3 && S * kCopies <= 63, "vmcnt");
+    static_assert(NSL % 2 == 0 && NSL >= S, "slabs per part");
+    static_assert((kScRows * kP) % 64 == 0, "scale copies");
+    static_assert(kLds <= 160 * 1024, "LDS");
+};
+}  // namespace skr
+
+template <int S, int NSL, int KP>
+__global__ __launch_bounds__(256, 1) void gemm_splitk_fp4_rh(const uint8_t* __restrict__ qa,
+                                                             const uint8_t* __restrict__ sa,
+                                                             const uint8_t* __restrict__ qw,
+                                                             const uint8_t* __restrict__ sw, uint16_t* __restrict__ y,
+                                                             int M, int N, int K, int tiles, uint8_t* __restrict__ ws) {
+    using C = skr::Cfg<S, NSL>;
+    using sk::key;
+    constexpr int MF = 2;
+    const int b = blockIdx.x;
+    const int slot8 = b >> 3;
+    const int grp = slot8 % (2 * KP);
+    const int q = grp % KP, rh = grp / KP;       // K part, row half
+    const int t = (slot8 / (2 * KP)) * 8 + (b & 7);
+    if (t >= tiles) return;                      // the whole workgroup, before any barrier
+
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[C::kLds];
+    uint8_t* const scb = lds + S * C::kSlot;     // [kScRows][8 NSL]: 16-byte piece p of row r at (p + r) % kP
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l32 = lane & 31, h = lane >> 5;
+    const int64_t KB = (int64_t)K / 2;
+    const int KS = K / 32;
+    const int n0 = t * sk::kTN;
+    const int m0 = rh * C::kArows;               // first activation row of this half
+    const int mh = min(M - m0, C::kArows);       // rows of this half (>= 1)
+    const int s0 = q * NSL;                      // first slab of the part (K = 256 units)
+    const int rot = (t + 3 * q) % NSL;           // local slab j reads slab s0 + (j + rot) % NSL
+    const uint8_t* const qah = qa + (int64_t)m0 * KB;
+    const uint8_t* const sah = sa + (int64_t)m0 * KS;
+
+    // scales of the part (activation rows of this half first, then the tile's weight rows)
+    for (int c = wave; c < C::kScCopies; c += 4) {
+        const int u = 64 * c + lane;
+        const int r = u / C::kP, pos = u % C::kP;
+        const int p = (pos + C::kP - r % C::kP) % C::kP;
+        const uint8_t* src = r < C::kArows ? sah + (int64_t)min(r, mh - 1) * KS
+                                           : sw + (int64_t)min(n0 + r - C::kArows, N - 1) * KS;
+        g2lds16(src + 8 * s0 + 16 * p, scb + 1024 * c);
+    }
+    // per slab: this wave's two activation copies (rows 8c .. 8c+7, c = 2 wave, 2 wave + 1; rows past the half
+    // read its last row, a copy wholly past it one line) and four weight copies
+    const uint8_t* arow[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const int c = 2 * wave + e;
+        const int r = 8 * c + (lane >> 3);
+        arow[e] = 8 * c >= mh ? qah + (int64_t)(mh - 1) * KB : qah + (int64_t)min(r, mh - 1) * KB + 16 * ((lane & 7) ^ key(r));
+    }
+    const uint8_t* wrow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 8 * i + (lane >> 3);
+        wrow[i] = qw + (int64_t)min(n0 + 32 * wave + r, N - 1) * KB + 16 * ((lane & 7) ^ key(r));
+    }
+    auto issue = [&](int j) {
+        uint8_t* const slot = lds + (j % S) * C::kSlot;
+        const int64_t koff = (int64_t)(s0 + (j + rot) % NSL) * sk::kSlab;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) g2lds16(arow[e] + koff, slot + 1024 * (2 * wave + e));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) g2lds16_nt(wrow[i] + koff, slot + C::kActSlab + wave * C::kWSlab + 1024 * i);
+    };
+#pragma unroll
+    for (int j = 0; j < S; ++j) issue(j);
+
+    const uint32_t base = lds_addr(lds), sbase = lds_addr(scb);
+    const int wkey = key(l32);
+    const uint32_t woff = C::kActSlab + wave * C::kWSlab + l32 * sk::kSlab;
+    const int wsr = C::kArows + 32 * wave + l32;
+    uint32_t xoff[MF];
+    int xkey[MF], xsr[MF];
+#pragma unroll
+    for (int g = 0; g < MF; ++g) {
+        xoff[g] = (32 * g + l32) * sk::kSlab;
+        xkey[g] = key(32 * g + l32);
+        xsr[g] = 32 * g + l32;
+    }
+    auto scale_at = [&](int r, int jj) -> uint32_t {
+        const int pos = (jj / 2 + r) % C::kP;
+        return lds_read4(sbase + r * 8 * NSL + 16 * pos + 8 * (jj & 1) + 4 * h);
+    };
+    v16f acc[MF];
+#pragma unroll
+    for (int g = 0; g < MF; ++g)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[g][i] = 0.f;
+
+    static_for<NSL>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        // issued so far: slabs 0 .. S - 1 by the prologue, then one per earlier slab from slab 1 on
+        constexpr int kIssued = j == 0 ? S - 1 : (j + S - 2 < NSL - 1 ? j + S - 2 : NSL - 1);
+        constexpr int kLater = kIssued - j;
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<kLater * C::kCopies>();  // this wave's copies of slab j (and the scales) have landed
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();       // every wave's: slab j is whole, and slab j - 1 is read
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (j >= 1 && j - 1 + S < NSL) issue(j - 1 + S);  // into the slot of slab j - 1
+        __builtin_amdgcn_sched_barrier(0);
+        const int jj = (j + rot) % NSL;
+        const uint32_t sb = base + (j % S) * C::kSlot;
+        uint32_t ws_ = scale_at(wsr, jj);
+        uint32_t xs[MF];
+#pragma unroll
+        for (int g = 0; g < MF; ++g) xs[g] = scale_at(xsr[g], jj);
+        v4u wv[4], xv[4][MF];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            wv[tt] = lds_read16(sb + woff + 16 * ((4 * h + tt) ^ wkey));
+#pragma unroll
+            for (int g = 0; g < MF; ++g) xv[tt][g] = lds_read16(sb + xoff[g] + 16 * ((4 * h + tt) ^ xkey[g]));
+        }
+        lds_wait_dec<MF>(wv, xv, ws_, xs);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int g = 0; g < MF; ++g) {
+            acc[g] = mfma32<kFmtFP4, 0>(fp4_operand(wv[0]), fp4_operand(xv[0][g]), acc[g], (int)ws_, (int)xs[g]);
+            acc[g] = mfma32<kFmtFP4, 1>(fp4_operand(wv[1]), fp4_operand(xv[1][g]), acc[g], (int)ws_, (int)xs[g]);
+            acc[g] = mfma32<kFmtFP4, 2>(fp4_operand(wv[2]), fp4_operand(xv[2][g]), acc[g], (int)ws_, (int)xs[g]);
+            acc[g] = mfma32<kFmtFP4, 3>(fp4_operand(wv[3]), fp4_operand(xv[3][g]), acc[g], (int)ws_, (int)xs[g]);
+        }
+    });
+
+    const int nw = n0 + 32 * wave + 4 * h;
+    const bool vec_ok = (N & 3) == 0 && (reinterpret_cast<uintptr_t>(y) & 7) == 0;
+    auto store_one = [&](int g, int i, const v4f& v) {
+        const int m = m0 + 32 * g + l32;
+        if (m >= M) return;
+        const int n = nw + 8 * i;
+        uint16_t* dst = y + (int64_t)m * N + n;
+        if (vec_ok && n + 3 < N) {
+            uint2 pk;
+            pk.x = bf16x2_rne(v[0], v[1]);
+            pk.y = bf16x2_rne(v[2], v[3]);
+            *reinterpret_cast<uint2*>(dst) = pk;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (n + e < N) dst[e] = (uint16_t)(bf16x2_rne(v[e], 0.f) & 0xffffu);
+        }
+    };
+    v4f mine[MF][4];
+#pragma unroll
+    for (int g = 0; g < MF; ++g)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mine[g][i] = v4f{acc[g][4 * i], acc[g][4 * i + 1], acc[g][4 * i + 2], acc[g][4 * i + 3]};
+    // the column groups of (tile, half) pairs: 2 tiles' worth of slots
+    sk::tail_sum<MF, KP>(mine, ws, (int)sk::workspace_bytes(2 * tiles, KP, MF), 2 * t + rh, q, wave, lane, store_one);
 }
 
 }  // namespace mx

@@ -96,8 +96,10 @@ mx_status mx_quant_weight_f32(const float *w, int64_t N, int64_t K,
  * Bytes of workspace mx_gemm_a4w4_bf16 needs for this shape: nonzero for the
  * decode sizes that split K across workgroups - M <= 64, K split into 4 or 8
  * parts of 2048 K-values, 128-column tiles x parts between 128 and 256
- * workgroups; e.g. 7,340,032 bytes for the (64, 7168, 8192) decode layer,
- * 8 MiB at most - and 0 otherwise.  It depends on the shape only.  The
+ * workgroups; 64 < M <= 128 in two 64-row halves, K split into 2 or 4 parts
+ * of 4096 or 8192, 2 x tiles x parts between 128 and 256 - e.g. 7,340,032
+ * bytes for the (64, 7168, 8192) and (128, 7168, 8192) layers, 8 MiB at most
+ * - and 0 otherwise.  It depends on the shape only.  The
  * workspace holds the FP32 partial slots through which the workgroups of a
  * tile exchange their partial sums; a slot word reads 0 until written.  It
  * must be zero-filled (e.g. hipMemset) before its first use; every call
@@ -123,8 +125,9 @@ size_t mx_gemm_a4w4_workspace_bytes(int64_t M, int64_t N, int64_t K);
  * CU); otherwise the workspace-free decode kernels run.  It relies on
  * workgroups being dealt round-robin to the XCDs (the parts of a tile meet in
  * one XCD's L2), and on no other work keeping CUs from the grid for long: a
- * workgroup waiting for a partner gives up after about 0.3 s (the output is
- * then wrong), so that no launch can hang.
+ * workgroup waiting for a partner gives up after about 0.3 s, so that no
+ * launch can hang; the outputs it owns are then NaN, and the workspace must
+ * be zero-filled again before its next use.
  */
 mx_status mx_gemm_a4w4_bf16(const void *qa, const void *sa, const void *qw, const void *sw,
                             void *y_bf16, int64_t M, int64_t N, int64_t K,

@@ -91,7 +91,12 @@ def test_gemm_argument_errors(mx):
     assert mx.mx_linear_a4w4_workspace_bytes(1, 7168, 8192) == (8 << 20) + 4096 + 256
     assert mx.mx_linear_a4w4_workspace_bytes(100, 7168, 8192) == (8 << 20) + 100 * 4096 + 25600
     assert mx.mx_gemm_a4w4_workspace_bytes(64, 128 * 256 + 1, 8192) == 0  # more than 256 tiles
-    assert mx.mx_gemm_a4w4_workspace_bytes(65, 7168, 8192) == 0     # two row halves, no workspace
+    # 64 < M <= 128: the split over two row halves, 2 x tiles x parts x 4 waves x 2 fragments x 4 KB
+    assert mx.mx_gemm_a4w4_workspace_bytes(65, 7168, 8192) == 2 * 56 * 2 * 4 * 2 * 4096
+    assert mx.mx_gemm_a4w4_workspace_bytes(128, 7168, 16384) == 2 * 56 * 2 * 4 * 2 * 4096   # parts of 8192
+    assert mx.mx_gemm_a4w4_workspace_bytes(100, 2900, 16384) == 2 * 23 * 4 * 4 * 2 * 4096
+    assert mx.mx_gemm_a4w4_workspace_bytes(128, 7168, 4096) == 0    # the two-row-halves ring
+    assert mx.mx_gemm_a4w4_workspace_bytes(129, 7168, 8192) == 0
     assert mx.mx_gemm_a4w4_workspace_bytes(64, 512, 8192) == 0      # too few tiles to split
     assert mx.mx_gemm_a4w4_workspace_bytes(64, 7168, 8192 + 128) == 0
     assert g4(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 4096, 8192, None, 0) == mx.MX_ERROR_WORKSPACE

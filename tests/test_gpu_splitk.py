@@ -52,7 +52,16 @@ def _gemm(mx, torch, qa, sa, qw, sw, ws):
     return y
 
 
-@pytest.mark.parametrize("M,N,K", SPLIT_SHAPES)
+# 64 < M <= 128: two row halves, K parts of 4096 or 8192, activation slabs through a ring shared by the waves
+RH_SHAPES = [
+    (128, 7168, 8192),   # 2 parts of 4096, 224 workgroups
+    (65, 4000, 8192),    # one row in the second half, ragged last tile, 128 workgroups
+    (100, 2900, 16384),  # 4 parts of 4096, 23 tiles: idle workgroups
+    (128, 7168, 16384),  # 2 parts of 8192
+]
+
+
+@pytest.mark.parametrize("M,N,K", SPLIT_SHAPES + RH_SHAPES)
 def test_splitk_matches_oracle(mx, orc, M, N, K):
     import torch
     wsb = mx.mx_gemm_a4w4_workspace_bytes(M, N, K)
