@@ -255,9 +255,26 @@ hipError_t launch_gemm_a4w4_noalloc(const void* qa, const void* sa, const void* 
     return launch_gemm_a4w4(qa, sa, qw, sw, y, M, N, K, ws, st);
 }
 
+// Grouped GEMM: K = 2048 (8 slabs, one 128-column tile per workgroup and expert) takes gemm_grouped_fp4,
+// measured faster than the 32-column decode ring there; other K the grouped decode ring.
 hipError_t launch_a4w4_grouped(const void* qa, const void* sa, const void* qw, const void* sw, void* y,
                                const int32_t* offsets, int64_t G, int64_t max_rows, int64_t N, int64_t K,
                                hipStream_t st) {
+    if (K == 2048 && aligned16(sa, sw) && N <= (int64_t)sk::kTN * 65535) {
+        const dim3 grid((unsigned)((N + sk::kTN - 1) / sk::kTN), (unsigned)G);
+        const uint8_t* a = reinterpret_cast<const uint8_t*>(qa);
+        const uint8_t* w = reinterpret_cast<const uint8_t*>(qw);
+        const uint8_t* sa8 = reinterpret_cast<const uint8_t*>(sa);
+        const uint8_t* sw8 = reinterpret_cast<const uint8_t*>(sw);
+        uint16_t* out = reinterpret_cast<uint16_t*>(y);
+        if (max_rows <= 32)
+            hipLaunchKernelGGL((gemm_grouped_fp4<1, 5, 8>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, (int)N,
+                               (int)K, (int)grid.x, offsets);
+        else
+            hipLaunchKernelGGL((gemm_grouped_fp4<2, 4, 8>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, (int)N,
+                               (int)K, (int)grid.x, offsets);
+        return hipGetLastError();
+    }
     return launch_gemm_a4w4_grouped(qa, sa, qw, sw, y, offsets, G, max_rows, N, K, st);
 }
 

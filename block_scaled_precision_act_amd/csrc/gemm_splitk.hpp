@@ -250,20 +250,14 @@ __device__ __forceinline__ void tail_sum(const v4f (&mine)[MF][4], uint8_t* ws, 
 
 // KP: K parts (K = 256 NSL KP).  FUSED: the activations arrive as BF16 X [M, K] (in qa; sa unused) and
 // each workgroup quantizes its K part into the LDS block itself (the one-launch decode layer).
-template <int MF, int S, int NSL, int KP, bool FUSED = false>
-__global__ __launch_bounds__(256, 1) void gemm_splitk_fp4(const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa,
-                                                          const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw,
-                                                          uint16_t* __restrict__ y, int M, int N, int K, int tiles,
-                                                          uint8_t* __restrict__ ws) {
+// One workgroup's work: tile t, K part q (M rows of qa / sa / y), with the workgroup's LDS block.
+template <int MF, int S, int NSL, int KP, bool FUSED>
+__device__ __forceinline__ void splitk_fp4_tile(const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa,
+                                                const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw,
+                                                uint16_t* __restrict__ y, int M, int N, int K, int tiles,
+                                                uint8_t* __restrict__ ws, int t, int q, uint8_t* lds) {
     using C = sk::Cfg<MF, S, NSL>;
     using sk::key;
-    const int b = blockIdx.x;
-    const int slot8 = b >> 3;
-    const int q = slot8 % KP;                    // K part
-    const int t = (slot8 / KP) * 8 + (b & 7);    // tile
-    if (t >= tiles) return;                      // the whole workgroup, before any barrier
-
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[C::kLds];
     uint8_t* const actb = lds;                   // [kArows][NSL][128], chunks XOR-swizzled by key(row)
     uint8_t* const scb = lds + C::kAct;          // [kScRows][8 NSL]: 16-byte piece p of row r at (p + r) % kP
     const int lane = threadIdx.x & 63;
@@ -374,6 +368,7 @@ __global__ __launch_bounds__(256, 1) void gemm_splitk_fp4(const uint8_t* __restr
             acc[g] = mfma32<kFmtFP4, 1>(fp4_operand(wv[1]), fp4_operand(xv[1][g]), acc[g], (int)ws_, (int)xs[g]);
             acc[g] = mfma32<kFmtFP4, 2>(fp4_operand(wv[2]), fp4_operand(xv[2][g]), acc[g], (int)ws_, (int)xs[g]);
             acc[g] = mfma32<kFmtFP4, 3>(fp4_operand(wv[3]), fp4_operand(xv[3][g]), acc[g], (int)ws_, (int)xs[g]);
+            asm volatile("" : "+a"(acc[g]));  // the slab's MFMAs stay in this iteration (not sunk to the end)
         }
     });
 
@@ -410,6 +405,52 @@ __global__ __launch_bounds__(256, 1) void gemm_splitk_fp4(const uint8_t* __restr
             for (int i = 0; i < 4; ++i) store_one(g, i, mine[g][i]);
     } else {
         sk::tail_sum<MF, KP>(mine, ws, (int)sk::workspace_bytes(tiles, KP, MF), t, q, wave, lane, store_one);
+    }
+}
+
+template <int MF, int S, int NSL, int KP, bool FUSED = false>
+__global__ __launch_bounds__(256, 1) void gemm_splitk_fp4(const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa,
+                                                          const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw,
+                                                          uint16_t* __restrict__ y, int M, int N, int K, int tiles,
+                                                          uint8_t* __restrict__ ws) {
+    const int b = blockIdx.x;
+    const int slot8 = b >> 3;
+    const int q = slot8 % KP;                    // K part
+    const int t = (slot8 / KP) * 8 + (b & 7);    // tile
+    if (t >= tiles) return;                      // the whole workgroup, before any barrier
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[sk::Cfg<MF, S, NSL>::kLds];
+    splitk_fp4_tile<MF, S, NSL, KP, FUSED>(qa, sa, qw, sw, y, M, N, K, tiles, ws, t, q, lds);
+}
+
+// Grouped A4W4 GEMM over MoE experts ("Kimi-K3-Quark-MXFP4-AttnFP8", section "Model Quantization": expert
+// weights and activations in OCP MXFP4) in the same per-tile design without a K split (one part): workgroup
+// (t, e) computes the 128 columns of tile t for the rows goff[e] .. goff[e+1] - 1 of expert e, in chunks of
+// 32 MF rows (a barrier between chunks, which reuse the LDS block), so every row of every group is written.
+// The tiles of one expert are consecutive workgroups, dealt round-robin to the XCDs, so each XCD's tiles of
+// an expert read its activation rows through one L2.  An empty group's workgroups return at once.
+template <int MF, int S, int NSL>
+__global__ __launch_bounds__(256, 1) void gemm_grouped_fp4(const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa,
+                                                           const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw,
+                                                           uint16_t* __restrict__ y, int N, int K, int tiles,
+                                                           const int32_t* __restrict__ goff) {
+    constexpr int kRows = 32 * MF;
+    const int t = blockIdx.x, e = blockIdx.y;
+    const int r0 = __builtin_amdgcn_readfirstlane(goff[e]);
+    const int rows = __builtin_amdgcn_readfirstlane(goff[e + 1]) - r0;
+    if (rows <= 0) return;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[sk::Cfg<MF, S, NSL>::kLds];
+    const int64_t KB = (int64_t)K / 2, KS = K / 32;
+    const uint8_t* const qwe = qw + (int64_t)e * N * KB;
+    const uint8_t* const swe = sw + (int64_t)e * N * KS;
+#pragma nounroll
+    for (int c = 0; c < rows; c += kRows) {
+        if (c > 0) {
+            wait_vmcnt<0>();   // the previous chunk's stores are done before the next chunk's copies are counted
+            __syncthreads();   // and every wave is done with its LDS
+        }
+        const int64_t r = r0 + c;
+        splitk_fp4_tile<MF, S, NSL, 1, false>(qa + r * KB, sa + r * KS, qwe, swe, y + r * N, min(rows - c, kRows), N,
+                                              K, tiles, nullptr, t, 0, lds);
     }
 }
 

@@ -29,7 +29,8 @@ def _grouped_case(orc, seed, sizes, N, K):
 
 
 @pytest.mark.parametrize("sizes,N,K,max_rows", [
-    ([0, 1, 17, 32, 0, 5], 512, 2048, 32),          # 32-row kernel, empty groups
+    ([0, 1, 17, 32, 0, 5], 512, 2048, 32),          # K = 2048: 128-column tiles, 32-row chunks, empty groups
+    ([40, 3, 64, 0, 9], 1000, 2048, 64),            # K = 2048, 64-row chunks, ragged N
     ([64, 33, 0, 40, 2], 300, 4096, 64),            # 64-row kernel, ragged N
     ([3, 64, 1], 1000, 10240, 64),                  # K > 8192 (512-byte scale rows)
     ([9, 0, 30], 96, 10240, 32),
@@ -75,11 +76,11 @@ def test_grouped_every_row_of_large_groups(mx, orc, sizes, N, K, max_rows):
         assert ok, "group %d: %d elements outside tolerance (max err/bound %.3g)" % (e, nbad, ratio)
 
 
-@pytest.mark.parametrize("K", [2048, 4096])
+@pytest.mark.parametrize("K", [4096, 8192])
 def test_grouped_equals_per_group_gemm_bit_for_bit(mx, orc, K):
-    # the ungrouped decode GEMM runs the same kernel design (K = 2048: with a 2-slot ring; the order
-    # of the sums does not depend on the ring depth): each group's rows come out identical to
-    # mx_gemm_a4w4_bf16 on that group alone
+    # above K = 2048 the grouped GEMM runs the ungrouped decode ring's design (the same K order, whatever the
+    # ring depth): each group's rows come out identical to mx_gemm_a4w4_bf16 on that group alone.  (At
+    # K = 2048 it takes 128-column tiles over the whole K instead, checked against the oracle above.)
     import torch
     sizes, N = [5, 0, 20, 11], 640
     qa, sa, qw, sw, offsets = _grouped_case(orc, 99, sizes, N, K)
