@@ -427,9 +427,10 @@ __global__ __launch_bounds__(256, 1) void gemm_splitk_fp4(const uint8_t* __restr
 // (t, e) computes the 128 columns of tile t for the rows goff[e] .. goff[e+1] - 1 of expert e, in chunks of
 // 32 MF rows (a barrier between chunks, which reuse the LDS block), so every row of every group is written.
 // The tiles of one expert are consecutive workgroups, dealt round-robin to the XCDs, so each XCD's tiles of
-// an expert read its activation rows through one L2.  An empty group's workgroups return at once.
+// an expert read its activation rows through one L2.  An empty group's workgroups return at once.  A
+// configuration whose LDS block fits twice in a CU's 160 KB is compiled for two workgroups per CU.
 template <int MF, int S, int NSL>
-__global__ __launch_bounds__(256, 1) void gemm_grouped_fp4(const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa,
+__global__ __launch_bounds__(256, (2 * sk::Cfg<MF, S, NSL>::kLds <= 160 * 1024 ? 2 : 1)) void gemm_grouped_fp4(const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa,
                                                            const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw,
                                                            uint16_t* __restrict__ y, int N, int K, int tiles,
                                                            const int32_t* __restrict__ goff) {
