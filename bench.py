@@ -372,8 +372,11 @@ def one_call_layer_entry(ctx, args):
     out = {}
     for Ms in (1, 8, 16, 64):
         lay = make_a4w4(ctx, "oproj_decode_a4w4", M=Ms)
-        one_ms = kernel_ms(ctx, lay, "fused", args.kernel_reps)
-        two_ms = kernel_ms(ctx, lay, "step", args.kernel_reps)
+        # alternated, best of two each: the first of a run of timings can catch the clocks still rising
+        one_ms, two_ms = float("inf"), float("inf")
+        for _ in range(2):
+            one_ms = min(one_ms, kernel_ms(ctx, lay, "fused", args.kernel_reps))
+            two_ms = min(two_ms, kernel_ms(ctx, lay, "step", args.kernel_reps))
         # algorithmic bytes of the layer: BF16 X in, the MXFP4 weight and its scales in, BF16 Y out
         byt = 2 * Ms * lay.K + lay.N * lay.K // 2 + lay.N * lay.K // 32 + 2 * Ms * lay.N
         gbs = byt / (one_ms * 1e-3) / 1e9
