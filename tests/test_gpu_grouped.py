@@ -5,8 +5,9 @@ C ABI, against the oracle's exact GEMM applied group by group:
 
 Group e multiplies the packed activation rows offsets[e] .. offsets[e+1]-1 with expert
 weight e.  The pages give no expert shapes; these are synthetic: empty groups, single
-rows, ragged sizes up to the 64-row bound, ragged N, both scale-block sizes (K <= 8192
-and K = 10240).
+rows, ragged sizes from 1 to 1000 rows (above the bound the caller passes as well), ragged
+N, K = 2048 (128-column tiles) and above (the grouped decode ring), both scale-row sizes
+(K <= 8192 and K = 10240).
 """
 import numpy as np
 import pytest
@@ -56,6 +57,7 @@ def test_grouped_a4w4_matches_oracle(mx, orc, sizes, N, K, max_rows):
     ([100, 0, 65, 7], 512, 2048, 32),        # groups above the bound: 32-row chunks, every row written
     ([300, 1000, 3], 256, 4096, 64),         # prefill-sized groups in 64-row chunks
     ([64, 65, 128, 129], 300, 2048, 1),      # chunk edges; a bound far below the real sizes
+    ([200, 0, 129, 1], 640, 2048, 64),       # K = 2048 in 64-row chunks, groups above the bound
 ])
 def test_grouped_every_row_of_large_groups(mx, orc, sizes, N, K, max_rows):
     """max_rows only picks 32- or 64-row chunks: groups of 65 .. 1000 rows, and groups larger than the
@@ -91,3 +93,15 @@ def test_grouped_equals_per_group_gemm_bit_for_bit(mx, orc, K):
             continue
         ys = mx.gemm_a4w4(to_dev(qa[r0:r1]), to_dev(sa[r0:r1]), to_dev(qw[e]), to_dev(sw[e]))
         assert torch.equal(yg[r0:r1].view(torch.int16), ys.view(torch.int16)), "group %d differs" % e
+
+
+def test_grouped_k2048_chunk_sizes_agree_bit_for_bit(mx, orc):
+    # at K = 2048 both chunk sizes (max_rows <= 32: 32-row chunks, else 64) sum every output in the same
+    # K order, one 32-row fragment at a time: the results are identical
+    import torch
+    sizes, N = [70, 0, 33, 5, 31], 900
+    qa, sa, qw, sw, offsets = _grouped_case(orc, 1234, sizes, N, 2048)
+    args = (to_dev(qa), to_dev(sa), to_dev(qw), to_dev(sw), to_dev(offsets))
+    y32 = mx.gemm_a4w4_grouped(*args, 32)
+    y64 = mx.gemm_a4w4_grouped(*args, 64)
+    assert torch.equal(y32.view(torch.int16), y64.view(torch.int16))
