@@ -202,7 +202,7 @@ mx_status mx_linear_a4w4_bf16(const void *x_bf16, const void *qw, const void *sw
  *            rows (max_rows <= 32) or 64 rows (larger), and every row of every
  *            group is written whatever the value; 0 declares every group empty.
  *            Groups are streamed as decode work (the expert weight columns of a
- *            workgroup are re-read from L2 per 64-row chunk): sized for routed
+ *            workgroup are re-read from L2 for each chunk): sized for routed
  *            decode tokens, correct for groups of any size.
  * K % 2048 == 0 and K <= 16384; qa, sa, qw, sw 16-byte aligned; y_bf16 2-byte
  * aligned; offsets 4-byte aligned; G <= 65535.  G, N or max_rows == 0: no-op.
