@@ -100,14 +100,15 @@ def test_a4w4_extreme_scales(mx, orc, what, M, N, K):
     _check(yg if rows is None else yg[rows], y, ad, "a4w4 %s %dx%dx%d" % (what, M, N, K))
 
 
-def test_grouped_a4w4_extreme_scales(mx, orc):
-    sizes, N, K = [5, 0, 32, 20], 256, 2048
+@pytest.mark.parametrize("K", [2048, 4096])  # 128-column tiles over the whole K; the grouped decode ring
+def test_grouped_a4w4_extreme_scales(mx, orc, K):
+    sizes, N = [5, 0, 32, 20], 256
     G, T = len(sizes), sum(sizes)
     qa, sa, qw1, sw1, _ = a4w4_edge_operands(orc, 17, T, N, K)
     qw = np.stack([np.roll(qw1, 7 * e, axis=0) for e in range(G)])
     sw = np.stack([np.roll(sw1, 7 * e, axis=0) for e in range(G)])
     offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
-    for max_rows in (32, 64):                               # the 32-row and the 64-row kernel
+    for max_rows in (32, 64):                               # 32- and 64-row chunks
         y = mx.gemm_a4w4_grouped(to_dev(qa), to_dev(sa), to_dev(qw), to_dev(sw), to_dev(offsets), max_rows)
         yh = bf16_host(y)
         for e in range(G):
