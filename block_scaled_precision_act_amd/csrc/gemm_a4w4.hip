@@ -1,28 +1,27 @@
-// gemm_a4w4.hip - MXFP4 A4W4 GEMM and one-call layer entries ("A4W4 dispatch"
-// with dynamic MXFP4 activations: "Kimi-K3 DSpark O-Proj-only MXFP4", section
-// "Exact quantization coverage").
+// gemm_a4w4.hip - MXFP4 A4W4 GEMM, one-call layer and grouped entries ("A4W4 dispatch" with
+// dynamic MXFP4 activations: "Kimi-K3 DSpark O-Proj-only MXFP4", section "Exact quantization
+// coverage"; expert weights and activations in OCP MXFP4: "Kimi-K3-Quark-MXFP4-AttnFP8", section
+// "Model Quantization").
 //
-// GEMM.  Decode sizes (M <= 64) with K a multiple of 8192 take the split-K
-// kernel (gemm_splitk.hpp: 128-column tiles, K parts of 2048, the partials
-// summed across the tile's workgroups), and 64 < M <= 128 with K a multiple of
-// 8192 its two-row-halves form (K parts of 4096 or 8192; M = 128, N = 7168,
-// K = 8192: 12.9 vs 17.3 us for the two-row-halves ring); both need the
-// caller's workspace,
-// when its grid is at least half the CUs and fits the device at once (else,
-// e.g. on a device with fewer CUs, the ring kernels run and the workspace is
-// not touched).  Other
-// shapes take the kernels of gemm_kernels.hpp: the decode rings for M <= 128
-// (K split over the waves of a workgroup) and the LDS-tiled kernels above.
-// Measured (graph-replayed, rotated weights, us): split-K vs ring at K = 8192:
-// N = 7168 M = 64 10.4 vs 12.4, M = 1 7.8 vs 8.4; N = 2048 M = 64 6.6 vs 9.9;
-// at K = 16384, N = 4096, M = 64 11.1 vs 17.7; at K = 4096 the ring kernels
-// are as fast or faster (N = 7168, M = 64: 7.4 vs 7.2), so they keep it.
+// GEMM.  Decode sizes with K = 8192 or 16384 take the split-K kernels of gemm_splitk.hpp (128-column
+// tiles, the partials summed across the tile's workgroups in the caller's workspace): M <= 64 in K
+// parts of 2048, and 64 < M <= 128 in two 64-row halves with K parts of 4096 or 8192 (M = 128,
+// N = 7168, K = 8192: 12.9 vs 17.3 us for the two-row-halves ring).  A plan is taken when its grid
+// keeps at least half of the CUs busy and fits the device at once; otherwise (a device with fewer CUs,
+// say) the ring kernels run and the workspace is not touched.  Other shapes take the kernels of
+// gemm_kernels.hpp: the decode rings for M <= 128 (K split over the waves of a workgroup) and the
+// LDS-tiled kernels above.  Measured (graph-replayed, rotated weights, us), split-K vs ring: K = 8192,
+// N = 7168: M = 64 10.4 vs 12.4, M = 1 7.8 vs 8.4; K = 8192, N = 2048, M = 64: 6.6 vs 9.9; K = 16384,
+// N = 4096, M = 64: 11.1 vs 17.7.  At K = 4096 the rings are as fast or faster (N = 7168, M = 64: 7.4
+// vs 7.2), so they keep it.
 //
-// Layer.  mx_linear_a4w4_bf16 quantizes inside the split-K workgroups (one
-// launch) for M <= 8, where that beat the quantizer + GEMM pair (N = 7168,
-// K = 8192, M = 1: 8.6 vs 9.9 us); above that every workgroup quantizing its
-// K part of all M rows costs more than the second launch (M = 16: 11.4 vs
+// Layer.  mx_linear_a4w4_bf16 quantizes inside the split-K workgroups (one launch) for M <= 8, where
+// that beat the quantizer + GEMM pair (N = 7168, K = 8192, M = 1: 8.6 vs 9.9 us); above that every
+// workgroup quantizing its K part of all M rows costs more than the second launch (M = 16: 11.4 vs
 // 10.4 us), so the layer runs the quantizer and the GEMM.
+//
+// Grouped.  K = 2048 takes gemm_grouped_fp4 (128-column tiles over the whole K, 47.9 vs 57.4 us for
+// the grouped ring on 32 experts of [7168, 2048]); other K the grouped decode ring.
 #include <mutex>
 
 #include "gemm_kernels.hpp"
