@@ -261,7 +261,7 @@ hipError_t launch_gemm_a4w4_noalloc(const void* qa, const void* sa, const void* 
 hipError_t launch_a4w4_grouped(const void* qa, const void* sa, const void* qw, const void* sw, void* y,
                                const int32_t* offsets, int64_t G, int64_t max_rows, int64_t N, int64_t K,
                                hipStream_t st) {
-    if (K == 2048 && aligned16(sa, sw) && N <= (int64_t)sk::kTN * 65535) {
+    if (K == 2048) {  // the entry point has checked the 16-byte alignment of every operand
         const dim3 grid((unsigned)((N + sk::kTN - 1) / sk::kTN), (unsigned)G);
         const uint8_t* a = reinterpret_cast<const uint8_t*>(qa);
         const uint8_t* w = reinterpret_cast<const uint8_t*>(qw);

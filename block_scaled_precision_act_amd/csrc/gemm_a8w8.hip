@@ -3,7 +3,7 @@
 // FP8 PTPC Quantization").  E4M3 codes are widened exactly to FP16 for the
 // MFMAs; the two FP32 scales are applied in the epilogue.
 //
-// 33 <= M <= 64 with K a multiple of 8192 or 16384 (K parts of 2048) takes the
+// 33 <= M <= 64 with K = 8192 or 16384 (4 or 8 K parts of 2048) takes the
 // split-K kernel (gemm_splitk_fp8 in gemm_splitk.hpp), which needs the caller's
 // workspace, when its grid (128 .. 256 workgroups) fits the device at once.
 // Measured (graph-replayed, rotated weights, N = 7168, K = 8192): M = 64 15.7

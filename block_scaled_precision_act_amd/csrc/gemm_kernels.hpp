@@ -597,10 +597,8 @@ __device__ __forceinline__ void decode_fp4_rows(const uint8_t* __restrict__ qa, 
 // scales) into the same rows of y.  The workgroup takes the group's rows in chunks of 32 MF (a
 // barrier between chunks, which reuse the LDS block), so every row of every group is written whatever
 // bound the caller passed; an empty group's workgroups return before their first barrier.
-// KSMAX = 64 (K <= 2048, 68 KB of LDS at MF = 1, S = 2) lets two workgroups share a CU: with so
-// few slabs per wave, concurrency rather than ring depth hides the memory latency.
 template <int MF, int S, int KSMAX, bool GROUPED = false, int RH = 1>
-__global__ __launch_bounds__(256, KSMAX == 64 ? 2 : 1) void gemm_decode_fp4(const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa,
+__global__ __launch_bounds__(256, 1) void gemm_decode_fp4(const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa,
                                                           const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw,
                                                           uint16_t* __restrict__ y, int M, int N, int K,
                                                           const int32_t* __restrict__ goff) {
@@ -2406,8 +2404,9 @@ inline hipError_t launch_gemm(const void* qa, const void* sa, const void* qw, co
 }
 
 // Grouped A4W4 decode GEMM (MoE experts): grid (N / 32, G); max_rows (the largest group, or a bound on it)
-// picks 32- or 64-row chunks - every row of every group is written either way; K % 2048 == 0, K <= 16384,
-// all code and scale pointers 16-byte aligned (checked by the caller).
+// picks 32- or 64-row chunks - every row of every group is written either way; K % 2048 == 0,
+// 4096 <= K <= 16384 (K = 2048 runs gemm_grouped_fp4 of gemm_splitk.hpp), all code and scale pointers
+// 16-byte aligned (checked by the caller).
 inline hipError_t launch_gemm_a4w4_grouped(const void* qa, const void* sa, const void* qw, const void* sw, void* y,
                                            const int32_t* offsets, int64_t G, int64_t max_rows, int64_t N, int64_t K,
                                            hipStream_t st) {
@@ -2418,10 +2417,7 @@ inline hipError_t launch_gemm_a4w4_grouped(const void* qa, const void* sa, const
     uint16_t* out = reinterpret_cast<uint16_t*>(y);
     const int n = (int)N, k = (int)K;
     const dim3 grid((unsigned)((N + dec4::kNT - 1) / dec4::kNT), (unsigned)G);
-    if (max_rows <= 32 && K <= 2048)
-        hipLaunchKernelGGL((gemm_decode_fp4<1, 2, 64, true>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, 0, n, k,
-                           offsets);
-    else if (max_rows <= 32 && K <= 8192)
+    if (max_rows <= 32 && K <= 8192)
         hipLaunchKernelGGL((gemm_decode_fp4<1, 2, 256, true>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, 0, n, k,
                            offsets);
     else if (max_rows <= 32)
