@@ -145,7 +145,7 @@ MX_API mx_status mx_gemm_a4w4_grouped_bf16(const void* qa, const void* sa, const
                                            void* y_bf16, const int32_t* offsets, int64_t G, int64_t max_rows,
                                            int64_t N, int64_t K, void* stream) {
     if (G < 0 || N < 0 || max_rows < 0) return MX_ERROR_INVALID_VALUE;
-    if (max_rows > INT32_MAX || G > 65535 || N > INT32_MAX || K <= 0 || K % 2048 != 0 || K > 16384)
+    if (max_rows > INT32_MAX || G > 65535 || N > INT32_MAX || K <= 0 || K % 512 != 0 || K > 16384)
         return MX_ERROR_UNSUPPORTED_SHAPE;
     if (N > (INT64_C(1) << 40) / K / (G > 0 ? G : 1)) return MX_ERROR_UNSUPPORTED_SHAPE;
     if (G == 0 || N == 0 || max_rows == 0) return MX_SUCCESS;

@@ -219,15 +219,22 @@ struct DecodeRegs {
     uint4 scale;
 };
 
+// LDS bytes of the kernel: two stages, or the four waves' partial tiles for the final sum
 template <int MF>
-__global__ __launch_bounds__(256) void gemm_decode_lds_fp4(const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa,
-                                                           const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw,
-                                                           uint16_t* __restrict__ y, int M, int N, int K) {
+constexpr int decode_lds_bytes() {
+    constexpr int V = MF * 2 * 4;
+    return 2 * DecodeLds<MF>::kStage > 4 * V * 64 * 4 ? 2 * DecodeLds<MF>::kStage : 4 * V * 64 * 4;
+}
+
+// One workgroup's work: the 32 output columns of blockIdx.x for rows 0 .. M - 1 (M <= 16 MF) of qa / sa / y,
+// with the workgroup's LDS block.
+template <int MF>
+__device__ __forceinline__ void decode_lds_rows(const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa,
+                                                const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw,
+                                                uint16_t* __restrict__ y, int M, int N, int K, uint8_t* lds) {
     using C = DecodeLds<MF>;
     constexpr int NF = 2;
     constexpr int V = MF * NF * 4;
-    constexpr int kLds = 2 * C::kStage > 4 * V * 64 * 4 ? 2 * C::kStage : 4 * V * 64 * 4;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r16 = lane & 15, q = lane >> 4;
@@ -358,6 +365,34 @@ __global__ __launch_bounds__(256) void gemm_decode_lds_fp4(const uint8_t* __rest
         const int r = v & 3, ij = v >> 2, j = ij % NF, i = ij / NF;
         const int m = 16 * i + 4 * (l >> 4) + r, n = n0 + 16 * j + (l & 15);
         if (m < M && n < N) y[(int64_t)m * N + n] = (uint16_t)bf16_rne(sum);
+    }
+}
+
+// GROUPED (MoE experts, grid.y = expert e): the rows goff[e] .. goff[e+1] - 1 of the packed activations with
+// weight e of the stacked weights ([G, N, K/2] codes, [G, N, K/32] scales) into the same rows of y, in chunks
+// of 16 MF rows (a barrier between chunks, which reuse the LDS block), so every row of every group is
+// written; an empty group's workgroups return before their first barrier.  Otherwise M rows (M <= 16 MF).
+template <int MF, bool GROUPED = false>
+__global__ __launch_bounds__(256) void gemm_decode_lds_fp4(const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa,
+                                                           const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw,
+                                                           uint16_t* __restrict__ y, int M, int N, int K,
+                                                           const int32_t* __restrict__ goff) {
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[decode_lds_bytes<MF>()];
+    if constexpr (GROUPED) {
+        const int e = blockIdx.y;
+        const int r0 = __builtin_amdgcn_readfirstlane(goff[e]);
+        const int rows = __builtin_amdgcn_readfirstlane(goff[e + 1]) - r0;  // uniform over the workgroup
+        if (rows <= 0) return;  // the whole workgroup, before any barrier
+        const int64_t KB = (int64_t)K / 2, KS = (int64_t)K / 32;
+        qw += (int64_t)e * N * KB;
+        sw += (int64_t)e * N * KS;
+        for (int c = 0; c < rows; c += 16 * MF) {
+            if (c > 0) __syncthreads();  // every wave has read the previous chunk's partial tiles
+            const int64_t r = (int64_t)r0 + c;
+            decode_lds_rows<MF>(qa + r * KB, sa + r * KS, qw, sw, y + r * N, min(rows - c, 16 * MF), N, K, lds);
+        }
+    } else {
+        decode_lds_rows<MF>(qa, sa, qw, sw, y, M, N, K, lds);
     }
 }
 
@@ -2295,13 +2330,17 @@ inline hipError_t launch_gemm(const void* qa, const void* sa, const void* qw, co
         const uint8_t* sa8 = reinterpret_cast<const uint8_t*>(sa);
         const uint8_t* sw8 = reinterpret_cast<const uint8_t*>(sw);
         if (M <= 16)
-            hipLaunchKernelGGL(gemm_decode_lds_fp4<1>, grid, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k);
+            hipLaunchKernelGGL((gemm_decode_lds_fp4<1>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k,
+                               nullptr);
         else if (M <= 32)
-            hipLaunchKernelGGL(gemm_decode_lds_fp4<2>, grid, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k);
+            hipLaunchKernelGGL((gemm_decode_lds_fp4<2>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k,
+                               nullptr);
         else if (M <= 64)
-            hipLaunchKernelGGL(gemm_decode_lds_fp4<4>, grid, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k);
+            hipLaunchKernelGGL((gemm_decode_lds_fp4<4>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k,
+                               nullptr);
         else
-            hipLaunchKernelGGL(gemm_decode_lds_fp4<8>, grid, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k);
+            hipLaunchKernelGGL((gemm_decode_lds_fp4<8>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k,
+                               nullptr);
     } else if (FP8 && M <= 64 && K % 512 == 0) {
         const dim3 grid((unsigned)((N + dec8::kNT - 1) / dec8::kNT));
         const float* sa32 = reinterpret_cast<const float*>(sa);
@@ -2404,9 +2443,9 @@ inline hipError_t launch_gemm(const void* qa, const void* sa, const void* qw, co
 }
 
 // Grouped A4W4 decode GEMM (MoE experts): grid (N / 32, G); max_rows (the largest group, or a bound on it)
-// picks 32- or 64-row chunks - every row of every group is written either way; K % 2048 == 0,
-// 4096 <= K <= 16384 (K = 2048 runs gemm_grouped_fp4 of gemm_splitk.hpp), all code and scale pointers
-// 16-byte aligned (checked by the caller).
+// picks 32- or 64-row chunks - every row of every group is written either way.  K % 512 == 0, K <= 16384
+// (K = 2048 runs gemm_grouped_fp4 of gemm_splitk.hpp), all code and scale pointers 16-byte aligned
+// (checked by the caller): K % 2048 == 0 takes the decode ring, other K the LDS-staged decode kernel.
 inline hipError_t launch_gemm_a4w4_grouped(const void* qa, const void* sa, const void* qw, const void* sw, void* y,
                                            const int32_t* offsets, int64_t G, int64_t max_rows, int64_t N, int64_t K,
                                            hipStream_t st) {
@@ -2417,6 +2456,15 @@ inline hipError_t launch_gemm_a4w4_grouped(const void* qa, const void* sa, const
     uint16_t* out = reinterpret_cast<uint16_t*>(y);
     const int n = (int)N, k = (int)K;
     const dim3 grid((unsigned)((N + dec4::kNT - 1) / dec4::kNT), (unsigned)G);
+    if (K % 2048 != 0) {
+        if (max_rows <= 32)
+            hipLaunchKernelGGL((gemm_decode_lds_fp4<2, true>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, 0, n, k,
+                               offsets);
+        else
+            hipLaunchKernelGGL((gemm_decode_lds_fp4<4, true>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, 0, n, k,
+                               offsets);
+        return hipGetLastError();
+    }
     if (max_rows <= 32 && K <= 8192)
         hipLaunchKernelGGL((gemm_decode_fp4<1, 2, 256, true>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, 0, n, k,
                            offsets);

@@ -204,7 +204,8 @@ mx_status mx_linear_a4w4_bf16(const void *x_bf16, const void *qw, const void *sw
  *            Groups are streamed as decode work (the expert weight columns of a
  *            workgroup are re-read from L2 for each chunk): sized for routed
  *            decode tokens, correct for groups of any size.
- * K % 2048 == 0 and K <= 16384; qa, sa, qw, sw 16-byte aligned; y_bf16 2-byte
+ * K % 512 == 0 and K <= 16384 (e.g. K = 2048 for an expert down projection,
+ * K = 7168 for up / gate); qa, sa, qw, sw 16-byte aligned; y_bf16 2-byte
  * aligned; offsets 4-byte aligned; G <= 65535.  G, N or max_rows == 0: no-op.
  */
 mx_status mx_gemm_a4w4_grouped_bf16(const void *qa, const void *sa, const void *qw, const void *sw,

@@ -139,7 +139,7 @@ def test_grouped_gemm_argument_errors(mx):
     assert gg(*ok_args, -1, 16, 512, 2048) == mx.MX_ERROR_INVALID_VALUE       # G
     assert gg(*ok_args, 4, -1, 512, 2048) == mx.MX_ERROR_INVALID_VALUE        # max_rows
     assert gg(*ok_args, 4, 16, -1, 2048) == mx.MX_ERROR_INVALID_VALUE         # N
-    assert gg(*ok_args, 4, 16, 512, 1024) == mx.MX_ERROR_UNSUPPORTED_SHAPE    # K % 2048
+    assert gg(*ok_args, 4, 16, 512, 1000) == mx.MX_ERROR_UNSUPPORTED_SHAPE    # K % 512
     assert gg(*ok_args, 4, 16, 512, 18432) == mx.MX_ERROR_UNSUPPORTED_SHAPE   # K > 16384
     assert gg(*ok_args, 65536, 16, 512, 2048) == mx.MX_ERROR_UNSUPPORTED_SHAPE
     assert gg(FAKE, FAKE, FAKE, FAKE, FAKE, None, 4, 16, 512, 2048) == mx.MX_ERROR_INVALID_VALUE

@@ -35,6 +35,10 @@ def _grouped_case(orc, seed, sizes, N, K):
     ([64, 33, 0, 40, 2], 300, 4096, 64),            # 64-row kernel, ragged N
     ([3, 64, 1], 1000, 10240, 64),                  # K > 8192 (512-byte scale rows)
     ([9, 0, 30], 96, 10240, 32),
+    ([0, 7, 32, 19], 640, 7168, 32),                # K % 2048 != 0 (an up / gate projection's K): the
+    ([40, 2, 64], 300, 7168, 64),                   #   LDS-staged decode kernel, 32- and 64-row chunks
+    ([5, 33], 200, 512, 64),                        # one 512-K stage
+    ([3, 0, 12], 100, 1536, 32),
 ])
 def test_grouped_a4w4_matches_oracle(mx, orc, sizes, N, K, max_rows):
     import torch
@@ -58,6 +62,8 @@ def test_grouped_a4w4_matches_oracle(mx, orc, sizes, N, K, max_rows):
     ([300, 1000, 3], 256, 4096, 64),         # prefill-sized groups in 64-row chunks
     ([64, 65, 128, 129], 300, 2048, 1),      # chunk edges; a bound far below the real sizes
     ([200, 0, 129, 1], 640, 2048, 64),       # K = 2048 in 64-row chunks, groups above the bound
+    ([130, 0, 65], 256, 7168, 32),           # K % 2048 != 0 in 32-row chunks, groups above the bound
+    ([100, 129], 128, 1536, 64),
 ])
 def test_grouped_every_row_of_large_groups(mx, orc, sizes, N, K, max_rows):
     """max_rows only picks 32- or 64-row chunks: groups of 65 .. 1000 rows, and groups larger than the
@@ -78,11 +84,12 @@ def test_grouped_every_row_of_large_groups(mx, orc, sizes, N, K, max_rows):
         assert ok, "group %d: %d elements outside tolerance (max err/bound %.3g)" % (e, nbad, ratio)
 
 
-@pytest.mark.parametrize("K", [4096, 8192])
+@pytest.mark.parametrize("K", [4096, 8192, 7168])
 def test_grouped_equals_per_group_gemm_bit_for_bit(mx, orc, K):
-    # above K = 2048 the grouped GEMM runs the ungrouped decode ring's design (the same K order, whatever the
-    # ring depth): each group's rows come out identical to mx_gemm_a4w4_bf16 on that group alone.  (At
-    # K = 2048 it takes 128-column tiles over the whole K instead, checked against the oracle above.)
+    # above K = 2048 the grouped GEMM runs the ungrouped decode kernels' designs (the ring for K % 2048 == 0,
+    # the LDS-staged kernel otherwise; the same K order whatever the ring depth or fragment count): each
+    # group's rows come out identical to mx_gemm_a4w4_bf16 on that group alone.  (At K = 2048 it takes
+    # 128-column tiles over the whole K instead, checked against the oracle above.)
     import torch
     sizes, N = [5, 0, 20, 11], 640
     qa, sa, qw, sw, offsets = _grouped_case(orc, 99, sizes, N, K)

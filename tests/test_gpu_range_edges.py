@@ -100,7 +100,7 @@ def test_a4w4_extreme_scales(mx, orc, what, M, N, K):
     _check(yg if rows is None else yg[rows], y, ad, "a4w4 %s %dx%dx%d" % (what, M, N, K))
 
 
-@pytest.mark.parametrize("K", [2048, 4096])  # 128-column tiles over the whole K; the grouped decode ring
+@pytest.mark.parametrize("K", [2048, 4096, 7168])  # 128-column tiles; the grouped decode ring; LDS-staged
 def test_grouped_a4w4_extreme_scales(mx, orc, K):
     sizes, N = [5, 0, 32, 20], 256
     G, T = len(sizes), sum(sizes)
