@@ -422,13 +422,14 @@ def weight_conversion_entry(ctx, args):
     return out
 
 
-def grouped_entry(ctx, args):
+def grouped_entry(ctx, args, name="moe_grouped_a4w4"):
     """Grouped A4W4 GEMM over MoE experts (synthetic shapes: 64 tokens x top-8 over 32 experts of
-    [7168, 2048]), two rotated sets of expert weights, graph-replayed."""
+    [7168, 2048], the down projections; or of [2048, 7168], the up projections), two rotated sets of
+    expert weights, graph-replayed."""
     import numpy as np
     torch, mx = ctx.torch, ctx.mx
     from block_scaled_precision_act_amd import synth
-    cfg = synth.CONFIGS["moe_grouped_a4w4"]
+    cfg = synth.CONFIGS[name]
     G, N, K = cfg["G"], cfg["N"], cfg["K"]
     counts = synth.route_counts(cfg["route"], cfg["tokens"], cfg["topk"], G)
     T, max_rows = int(counts.sum()), int(counts.max())
@@ -716,6 +717,7 @@ def main():
         also["weight_conversion"] = weight_conversion_entry(ctx, args)
         log("grouped MoE A4W4")
         also["moe_grouped_a4w4"] = grouped_entry(ctx, args)
+        also["moe_grouped_up_a4w4"] = grouped_entry(ctx, args, "moe_grouped_up_a4w4")
         out["also"] = also
 
     if not args.no_cpu_baseline:

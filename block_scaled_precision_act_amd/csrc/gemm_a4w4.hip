@@ -21,7 +21,8 @@
 // 10.4 us), so the layer runs the quantizer and the GEMM.
 //
 // Grouped.  K = 2048 takes gemm_grouped_fp4 (128-column tiles over the whole K, 47.9 vs 57.4 us for
-// the grouped ring on 32 experts of [7168, 2048]); other K the grouped decode ring.
+// the grouped ring on 32 experts of [7168, 2048]); other K the grouped decode ring (K % 2048 == 0) or the
+// grouped LDS-staged decode kernel (other K % 512 == 0).
 #include <mutex>
 
 #include "gemm_kernels.hpp"
@@ -255,7 +256,7 @@ hipError_t launch_gemm_a4w4_noalloc(const void* qa, const void* sa, const void* 
 }
 
 // Grouped GEMM: K = 2048 (8 slabs, one 128-column tile per workgroup and expert) takes gemm_grouped_fp4,
-// measured faster than the 32-column decode ring there; other K the grouped decode ring.  32-row chunks
+// measured faster than the 32-column decode ring there; other K the kernels of gemm_kernels.hpp.  32-row chunks
 // run with a 2-slot ring, two workgroups per CU (each one's ramp-up overlaps the other's stream):
 // measured 47.9 us against 50.3 us with a 5-slot ring, one per CU, on 32 experts of [7168, 2048].
 hipError_t launch_a4w4_grouped(const void* qa, const void* sa, const void* qw, const void* sw, void* y,

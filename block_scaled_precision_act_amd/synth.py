@@ -138,6 +138,9 @@ CONFIGS = {
     # 32 experts, each expert a [7168, 2048] MXFP4 projection (hidden 7168, intermediate 2048)
     "moe_grouped_a4w4": dict(kind="a4w4_grouped", tokens=64, topk=8, G=32, N=OPROJ_N, K=2048,
                              x=("normal", 11), w=("normal", 12, 0.02), route=13),
+    # the same routing into each expert's up (or gate) projection: [2048, 7168], K = the hidden size
+    "moe_grouped_up_a4w4": dict(kind="a4w4_grouped", tokens=64, topk=8, G=32, N=2048, K=OPROJ_N,
+                                x=("normal", 14), w=("normal", 15, 0.02), route=13),
 }
 
 
