@@ -20,9 +20,9 @@
 // workgroup quantizing its K part of all M rows costs more than the second launch (M = 16: 11.4 vs
 // 10.4 us), so the layer runs the quantizer and the GEMM.
 //
-// Grouped.  K = 2048 takes gemm_grouped_fp4 (128-column tiles over the whole K, 47.9 vs 57.4 us for
-// the grouped ring on 32 experts of [7168, 2048]); other K the grouped decode ring (K % 2048 == 0) or the
-// grouped LDS-staged decode kernel (other K % 512 == 0).
+// Grouped.  gemm_grouped_fp4 (128-column tiles, K walked in parts) for K % 1024 == 0 where it measured
+// faster (see launch_a4w4_grouped), else the grouped decode ring (K % 2048 == 0) or the grouped LDS-staged
+// decode kernel (other K % 512 == 0).
 #include <mutex>
 
 #include "gemm_kernels.hpp"
@@ -255,29 +255,42 @@ hipError_t launch_gemm_a4w4_noalloc(const void* qa, const void* sa, const void* 
     return launch_gemm_a4w4(qa, sa, qw, sw, y, M, N, K, ws, st);
 }
 
-// Grouped GEMM: K = 2048 (8 slabs, one 128-column tile per workgroup and expert) takes gemm_grouped_fp4,
-// measured faster than the 32-column decode ring there; other K the kernels of gemm_kernels.hpp.  32-row chunks
-// run with a 2-slot ring, two workgroups per CU (each one's ramp-up overlaps the other's stream):
-// measured 47.9 us against 50.3 us with a 5-slot ring, one per CU, on 32 experts of [7168, 2048].
+// Grouped GEMM.  gemm_grouped_fp4 (one 128-column tile per workgroup and expert, K walked in parts of 8 or
+// 4 slabs) where it measured faster than the 32-column kernels of gemm_kernels.hpp (graph-replayed, two
+// rotated weight sets, 64 tokens x top-8 routed over the experts; us, this kernel vs the other):
+//   K = 2048, 32 experts of [7168, 2048]: 47.9 vs 57.4 (the ring), parts of 8 slabs, a 2-slot ring, two
+//             workgroups per CU for 32-row chunks (50.3 us with a 5-slot ring, one per CU);
+//   K = 7168, 32 experts of [2048, 7168]: 43.0 vs 56.7 (the LDS-staged kernel); 64-row chunks (256
+//             tokens): 83.6 vs 152;
+//   K = 4096, 32 experts of [7168, 4096]: 86 vs 97 (the ring); 64-row chunks: 153 vs 229;
+//   K = 16384, 32 experts of [2048, 16384], 64-row chunks: 193 vs 212.
+// The ring stays faster for 32-row chunks over few 128-column tiles (32 experts of [2048, 8192]: 65 vs 53;
+// 16 of [4096, 16384]: 180 vs 160): with under 1024 workgroups the tiles leave CUs idle.  K % 1024 != 0
+// (parts of 4 slabs do not fit) takes the LDS-staged kernel.
 hipError_t launch_a4w4_grouped(const void* qa, const void* sa, const void* qw, const void* sw, void* y,
                                const int32_t* offsets, int64_t G, int64_t max_rows, int64_t N, int64_t K,
                                hipStream_t st) {
-    if (K == 2048) {  // the entry point has checked the 16-byte alignment of every operand
-        const dim3 grid((unsigned)((N + sk::kTN - 1) / sk::kTN), (unsigned)G);
-        const uint8_t* a = reinterpret_cast<const uint8_t*>(qa);
-        const uint8_t* w = reinterpret_cast<const uint8_t*>(qw);
-        const uint8_t* sa8 = reinterpret_cast<const uint8_t*>(sa);
-        const uint8_t* sw8 = reinterpret_cast<const uint8_t*>(sw);
-        uint16_t* out = reinterpret_cast<uint16_t*>(y);
-        if (max_rows <= 32)
-            hipLaunchKernelGGL((gemm_grouped_fp4<1, 2, 8>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, (int)N,
-                               (int)K, (int)grid.x, offsets);
-        else
-            hipLaunchKernelGGL((gemm_grouped_fp4<2, 4, 8>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, (int)N,
-                               (int)K, (int)grid.x, offsets);
-        return hipGetLastError();
-    }
-    return launch_gemm_a4w4_grouped(qa, sa, qw, sw, y, offsets, G, max_rows, N, K, st);
+    const int64_t tiles = (N + sk::kTN - 1) / sk::kTN;
+    const bool wide = max_rows > 32;
+    const bool tile_path = K == 2048 || (K % 1024 == 0 && (wide || K % 2048 != 0 || tiles * G >= 1024));
+    if (!tile_path) return launch_gemm_a4w4_grouped(qa, sa, qw, sw, y, offsets, G, max_rows, N, K, st);
+    // the entry point has checked the 16-byte alignment of every operand
+    const dim3 grid((unsigned)tiles, (unsigned)G);
+    const uint8_t* a = reinterpret_cast<const uint8_t*>(qa);
+    const uint8_t* w = reinterpret_cast<const uint8_t*>(qw);
+    const uint8_t* sa8 = reinterpret_cast<const uint8_t*>(sa);
+    const uint8_t* sw8 = reinterpret_cast<const uint8_t*>(sw);
+    uint16_t* out = reinterpret_cast<uint16_t*>(y);
+    const int n = (int)N, k = (int)K, t = (int)tiles;
+    if (K == 2048 && !wide)
+        hipLaunchKernelGGL((gemm_grouped_fp4<1, 2, 8>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, n, k, t, offsets);
+    else if (K == 2048)
+        hipLaunchKernelGGL((gemm_grouped_fp4<2, 4, 8>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, n, k, t, offsets);
+    else if (!wide)
+        hipLaunchKernelGGL((gemm_grouped_fp4<1, 2, 4>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, n, k, t, offsets);
+    else
+        hipLaunchKernelGGL((gemm_grouped_fp4<2, 2, 4>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, n, k, t, offsets);
+    return hipGetLastError();
 }
 
 }  // namespace mx

@@ -251,12 +251,12 @@ __device__ __forceinline__ void tail_sum(const v4f (&mine)[MF][4], uint8_t* ws, 
 
 // KP: K parts (K = 256 NSL KP).  FUSED: the activations arrive as BF16 X [M, K] (in qa; sa unused) and
 // each workgroup quantizes its K part into the LDS block itself (the one-launch decode layer).
-// One workgroup's work: tile t, K part q (M rows of qa / sa / y), with the workgroup's LDS block.
-template <int MF, int S, int NSL, int KP, bool FUSED>
-__device__ __forceinline__ void splitk_fp4_tile(const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa,
+// The main loop of one workgroup: tile t, K part q (slabs NSL q .. NSL q + NSL - 1; M rows of qa / sa), with
+// the workgroup's LDS block, adding into acc.
+template <int MF, int S, int NSL, bool FUSED>
+__device__ __forceinline__ void splitk_fp4_part(const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa,
                                                 const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw,
-                                                uint16_t* __restrict__ y, int M, int N, int K, int tiles,
-                                                uint8_t* __restrict__ ws, int t, int q, uint8_t* lds) {
+                                                int M, int N, int K, int t, int q, uint8_t* lds, v16f (&acc)[MF]) {
     using C = sk::Cfg<MF, S, NSL>;
     using sk::key;
     uint8_t* const actb = lds;                   // [kArows][NSL][128], chunks XOR-swizzled by key(row)
@@ -333,12 +333,6 @@ __device__ __forceinline__ void splitk_fp4_tile(const uint8_t* __restrict__ qa, 
         return lds_read4(sbase + r * 8 * NSL + 16 * pos + 8 * (jj & 1) + 4 * h);
     };
 
-    v16f acc[MF];
-#pragma unroll
-    for (int g = 0; g < MF; ++g)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[g][i] = 0.f;
-
     static_for<NSL>([&](auto jc) {
         constexpr int j = decltype(jc)::value;
         constexpr int kNewer = (S - 1 < NSL - 1 - j) ? S - 1 : NSL - 1 - j;  // later slabs already issued
@@ -373,6 +367,17 @@ __device__ __forceinline__ void splitk_fp4_tile(const uint8_t* __restrict__ qa, 
         }
     });
 
+}
+
+// The workgroup's results: BF16 of acc into y (KP = 1), or the partials of K part q summed across the tile's
+// workgroups in the workspace first.
+template <int MF, int KP>
+__device__ __forceinline__ void splitk_fp4_finish(const v16f (&acc)[MF], uint16_t* __restrict__ y, int M, int N,
+                                                  int tiles, uint8_t* __restrict__ ws, int t, int q) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l32 = lane & 31, h = lane >> 5;
+    const int n0 = t * sk::kTN;
     // 4. D[n][m] of fragment g: lane l holds column m = 32 g + l32 and rows n = 8 i + 4 h + e in register
     //    4 i + e.  With KP > 1 the partials of the column group (tile t, wave) meet in the workspace.
     const int nw = n0 + 32 * wave + 4 * h;
@@ -409,6 +414,21 @@ __device__ __forceinline__ void splitk_fp4_tile(const uint8_t* __restrict__ qa, 
     }
 }
 
+// One workgroup's work: tile t, K part q (M rows of qa / sa / y), with the workgroup's LDS block.
+template <int MF, int S, int NSL, int KP, bool FUSED>
+__device__ __forceinline__ void splitk_fp4_tile(const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa,
+                                                const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw,
+                                                uint16_t* __restrict__ y, int M, int N, int K, int tiles,
+                                                uint8_t* __restrict__ ws, int t, int q, uint8_t* lds) {
+    v16f acc[MF];
+#pragma unroll
+    for (int g = 0; g < MF; ++g)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[g][i] = 0.f;
+    splitk_fp4_part<MF, S, NSL, FUSED>(qa, sa, qw, sw, M, N, K, t, q, lds, acc);
+    splitk_fp4_finish<MF, KP>(acc, y, M, N, tiles, ws, t, q);
+}
+
 template <int MF, int S, int NSL, int KP, bool FUSED = false>
 __global__ __launch_bounds__(256, 1) void gemm_splitk_fp4(const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa,
                                                           const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw,
@@ -424,9 +444,11 @@ __global__ __launch_bounds__(256, 1) void gemm_splitk_fp4(const uint8_t* __restr
 }
 
 // Grouped A4W4 GEMM over MoE experts ("Kimi-K3-Quark-MXFP4-AttnFP8", section "Model Quantization": expert
-// weights and activations in OCP MXFP4) in the same per-tile design without a K split (one part): workgroup
-// (t, e) computes the 128 columns of tile t for the rows goff[e] .. goff[e+1] - 1 of expert e, in chunks of
-// 32 MF rows (a barrier between chunks, which reuse the LDS block), so every row of every group is written.
+// weights and activations in OCP MXFP4) in the same per-tile design without a K split across workgroups:
+// workgroup (t, e) computes the 128 columns of tile t for the rows goff[e] .. goff[e+1] - 1 of expert e, in
+// chunks of 32 MF rows, and walks K in parts of NSL slabs (K % (256 NSL) == 0), adding each part's products
+// into the same accumulators; a barrier separates parts and row chunks, which reuse the LDS block.  Every
+// row of every group is written, and the sums run in the K order of the split-K kernel's parts.
 // The tiles of one expert are consecutive workgroups, dealt round-robin to the XCDs, so each XCD's tiles of
 // an expert read its activation rows through one L2.  An empty group's workgroups return at once.  A
 // configuration whose LDS block fits twice in a CU's 160 KB is compiled for two workgroups per CU.
@@ -444,15 +466,25 @@ __global__ __launch_bounds__(256, (2 * sk::Cfg<MF, S, NSL>::kLds <= 160 * 1024 ?
     const int64_t KB = (int64_t)K / 2, KS = K / 32;
     const uint8_t* const qwe = qw + (int64_t)e * N * KB;
     const uint8_t* const swe = sw + (int64_t)e * N * KS;
+    const int parts = K / (256 * NSL);
 #pragma nounroll
     for (int c = 0; c < rows; c += kRows) {
-        if (c > 0) {
-            wait_vmcnt<0>();   // the previous chunk's stores are done before the next chunk's copies are counted
-            __syncthreads();   // and every wave is done with its LDS
-        }
         const int64_t r = r0 + c;
-        splitk_fp4_tile<MF, S, NSL, 1, false>(qa + r * KB, sa + r * KS, qwe, swe, y + r * N, min(rows - c, kRows), N,
-                                              K, tiles, nullptr, t, 0, lds);
+        const int mc = min(rows - c, kRows);
+        v16f acc[MF];
+#pragma unroll
+        for (int g = 0; g < MF; ++g)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[g][i] = 0.f;
+#pragma nounroll
+        for (int q = 0; q < parts; ++q) {
+            if (c > 0 || q > 0) {
+                wait_vmcnt<0>();   // the earlier stores and copies are done before the next copies are counted
+                __syncthreads();   // and every wave is done with its LDS
+            }
+            splitk_fp4_part<MF, S, NSL, false>(qa + r * KB, sa + r * KS, qwe, swe, mc, N, K, t, q, lds, acc);
+        }
+        splitk_fp4_finish<MF, 1>(acc, y + r * N, mc, N, tiles, nullptr, t, 0);
     }
 }
 

@@ -39,6 +39,7 @@ def _grouped_case(orc, seed, sizes, N, K):
     ([40, 2, 64], 300, 7168, 64),                   #   LDS-staged decode kernel, 32- and 64-row chunks
     ([5, 33], 200, 512, 64),                        # one 512-K stage
     ([3, 0, 12], 100, 1536, 32),
+    ([1, 2, 0, 3] * 8, 4096, 4096, 32),             # 32 experts x 32 tiles: 128-column tiles, K in 4 parts
 ])
 def test_grouped_a4w4_matches_oracle(mx, orc, sizes, N, K, max_rows):
     import torch
