@@ -87,10 +87,10 @@ def test_grouped_every_row_of_large_groups(mx, orc, sizes, N, K, max_rows):
 
 @pytest.mark.parametrize("K", [4096, 8192, 7168])
 def test_grouped_equals_per_group_gemm_bit_for_bit(mx, orc, K):
-    # above K = 2048 the grouped GEMM runs the ungrouped decode kernels' designs (the ring for K % 2048 == 0,
-    # the LDS-staged kernel otherwise; the same K order whatever the ring depth or fragment count): each
-    # group's rows come out identical to mx_gemm_a4w4_bf16 on that group alone.  (At K = 2048 it takes
-    # 128-column tiles over the whole K instead, checked against the oracle above.)
+    # above K = 2048 every grouped kernel (the decode ring, the LDS-staged kernel, or 128-column tiles walking
+    # K in parts) sums each output in the K order of the ungrouped decode kernels these groups take: each
+    # group's rows come out identical to mx_gemm_a4w4_bf16 on that group alone (here: 20 tile workgroups and
+    # 32-row chunks, so K = 4096 and 8192 take the ring and K = 7168 the tiles).
     import torch
     sizes, N = [5, 0, 20, 11], 640
     qa, sa, qw, sw, offsets = _grouped_case(orc, 99, sizes, N, K)
