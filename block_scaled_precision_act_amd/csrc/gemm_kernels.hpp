@@ -2443,9 +2443,10 @@ inline hipError_t launch_gemm(const void* qa, const void* sa, const void* qw, co
 }
 
 // Grouped A4W4 decode GEMM (MoE experts): grid (N / 32, G); max_rows (the largest group, or a bound on it)
-// picks 32- or 64-row chunks - every row of every group is written either way.  K % 512 == 0, K <= 16384
-// (K = 2048 runs gemm_grouped_fp4 of gemm_splitk.hpp), all code and scale pointers 16-byte aligned
-// (checked by the caller): K % 2048 == 0 takes the decode ring, other K the LDS-staged decode kernel.
+// picks 32- or 64-row chunks - every row of every group is written either way.  K % 512 == 0, K <= 16384,
+// all code and scale pointers 16-byte aligned (checked by the caller, which takes gemm_grouped_fp4 of
+// gemm_splitk.hpp instead where that measured faster): K % 2048 == 0 takes the decode ring, other K the
+// LDS-staged decode kernel.
 inline hipError_t launch_gemm_a4w4_grouped(const void* qa, const void* sa, const void* qw, const void* sw, void* y,
                                            const int32_t* offsets, int64_t G, int64_t max_rows, int64_t N, int64_t K,
                                            hipStream_t st) {

@@ -2,8 +2,8 @@
 //   gemm_splitk_fp4     A4W4, M <= 64 (and the one-launch layer, FUSED)
 //   gemm_splitk_fp4_rh  A4W4, 64 < M <= 128, in two 64-row halves
 //   gemm_splitk_fp8     PTPC A8W8, 33 <= M <= 64
-// all sharing one tail (sk::tail_sum), and gemm_grouped_fp4 (MoE experts at K = 2048), the first's
-// tile body without a K split.  The design, described for the first:
+// all sharing one tail (sk::tail_sum), and gemm_grouped_fp4 (MoE experts, K % 1024 == 0), the first's
+// tile body walking K in parts within the workgroup.  The design, described for the first:
 //
 // The layer ("Kimi-K3 DSpark O-Proj-only MXFP4", section "Exact quantization
 // coverage": weight (7168, 8192) MXFP4 with (7168, 256) E8M0 scales, dynamic
