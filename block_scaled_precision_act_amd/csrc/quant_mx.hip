@@ -5,56 +5,29 @@
 // MXFP4 activations); standard "OCP MXFP4" named by "Kimi-K3-Quark-MXFP4-
 // AttnFP8", section "Model Quantization".
 //
-// BF16 input (activations): one lane owns one 32-value block (four 16-byte loads,
-// one 16-byte code store, one scale byte), using gfx950's scaled FP4 conversion,
-// which takes the decisions below (the GPU tests compare every finite BF16
-// pattern with the oracle).  FP32 input (offline weights): four lanes own one
-// block, eight values (two 16-byte loads) each:
-//   * shared exponent: the largest biased exponent field E of the block (a
-//     4-lane max); scale byte = max(E - 2, 0), which is floor(log2 amax) - 2
-//     + 127 clamped at the bottom of the E8M0 range; E == 255 (NaN/Inf in the
-//     block) gives scale 0xFF and codes 0.
-//   * element: with significand sig (hidden bit included; P fraction bits) and
-//     effective exponent Ee = max(E, 1), |x| / 2^(scale-127) times 4 equals
-//     sig / 2^u with u = scale + P - 2 - Ee >= P - 4, so every round-to-nearest-
-//     even decision on the E2M1 grid {0,.5,1,1.5,2,3,4,6} is an exact integer
-//     compare of sig against (midpoint*4) << u; ties at 0.25, 1.25, 2.5 and 5
-//     stay below (even code), ties at 0.75, 1.75 and 3.5 go up; above 6 the
-//     code saturates at 7.
-//   * one 32-bit store of 8 nibbles per lane (element 2j in the low nibble of
-//     byte j), one scale byte per block.
-// HBM-bound: 2 (or 4) bytes in, 0.5 + 1/32 bytes out per value.
+// Both inputs go through gfx950's scaled FP4 conversion, which divides by the power-of-two scale
+// and rounds to the nearest E2M1 value {0, .5, 1, 1.5, 2, 3, 4, 6}: ties to the even code, magnitudes
+// above 6 saturate at 6, the sign is kept.  The shared exponent is the block's largest biased exponent
+// field E; scale byte = max(E - 2, 0), which is floor(log2 amax) - 2 + 127 clamped at the bottom of the
+// E8M0 range; E == 255 (NaN/Inf in the block) gives scale 0xFF and codes 0.  The GPU tests compare
+// every finite BF16 pattern, and every FP32 mantissa of each binade that can round to a non-zero code
+// at several scale bytes (subnormal ones included), with the oracle.
+//   * BF16 input (activations): one lane owns one 32-value block (four 16-byte loads, one 16-byte code
+//     store, one scale byte).
+//   * FP32 input (offline weights): four lanes own one block, eight values (two 16-byte loads) each;
+//     the block's exponent maximum is a 4-lane DPP max; one 32-bit store of 8 nibbles per lane
+//     (element 2j in the low nibble of byte j), one scale byte per block.  The conversion replaced an
+//     exact integer-compare ladder (the same decisions, about 200 VALU operations per 8 values), which
+//     left this kernel ALU-bound: 7168 x 8192 FP32 went from 64-68 us to 47.6 us (5.6 TB/s).
 #include "launch.hpp"
 #include "mx_device.hpp"
 
 namespace mx {
 namespace {
 
-// magnitude code 0..7 of sig / 2^(u+2) on the E2M1 grid (see file comment)
-__device__ __forceinline__ uint32_t e2m1_magnitude(uint32_t sig, uint32_t u) {
-    return (uint32_t)(sig > (1u << u)) + (uint32_t)(sig >= (3u << u)) + (uint32_t)(sig > (5u << u)) +
-           (uint32_t)(sig >= (7u << u)) + (uint32_t)(sig > (10u << u)) + (uint32_t)(sig >= (14u << u)) +
-           (uint32_t)(sig > (20u << u));
-}
-
-template <int P>  // fraction bits of the input format (7 for BF16, 23 for FP32)
-__device__ __forceinline__ uint32_t encode8(const uint32_t (&mag)[8], uint32_t scale) {
-    uint32_t codes = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        uint32_t e = mag[i] >> P;
-        uint32_t sig = (mag[i] & ((1u << P) - 1u)) | (e ? (1u << P) : 0u);
-        uint32_t ee = e ? e : 1u;
-        uint32_t u = scale + (uint32_t)P - 2u - ee;
-        u = u < (uint32_t)(P + 1) ? u : (uint32_t)(P + 1);  // beyond P+1 every threshold exceeds sig
-        codes |= e2m1_magnitude(sig, u) << (4 * i);
-    }
-    return codes;
-}
-
 // One "unit" = 8 consecutive values = one quarter of a block.  units % 4 == 0
 // and every stride is a multiple of 4, so the four lanes of a block always
-// iterate together (the 4-lane shuffles below stay inside active lanes).
+// iterate together (the 4-lane DPP max below sees only active lanes).
 // FP32: eight values (two 16-byte loads) per lane, four lanes per block
 struct Unit {
     uint4 a, b;
@@ -67,25 +40,19 @@ __device__ __forceinline__ Unit load_unit(const void* __restrict__ xin, int64_t 
 
 __device__ __forceinline__ void convert_unit(const Unit& x, uint32_t* __restrict__ q, uint8_t* __restrict__ s,
                                              int64_t u) {
-    constexpr int P = 23;
-    uint32_t codes, scale;
-    uint32_t mag[8];
-    uint32_t sgn = 0, emax = 0;
     const uint32_t w[8] = {x.a.x, x.a.y, x.a.z, x.a.w, x.b.x, x.b.y, x.b.z, x.b.w};
+    uint32_t mag = 0;  // largest magnitude bit pattern: its exponent field is the largest one
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        sgn |= (w[i] >> 31) << (4 * i + 3);
-        mag[i] = w[i] & 0x7fffffffu;
-        emax = max(emax, mag[i] >> 23);
-    }
-    emax = max(emax, (uint32_t)__shfl_xor((int)emax, 1));
-    emax = max(emax, (uint32_t)__shfl_xor((int)emax, 2));
-    if (emax == 0xffu) {  // NaN or Inf in the block
-        scale = 0xffu;
-        codes = 0;
-    } else {
-        scale = emax > 2u ? emax - 2u : 0u;
-        codes = encode8<P>(mag, scale) | sgn;
+    for (int i = 0; i < 8; ++i) mag = max(mag, w[i] & 0x7fffffffu);
+    const uint32_t scale = mx_scale_of_emax(quad_max(mag >> 23));
+    uint32_t codes = 0;
+    if (scale != 0xffu) {
+        // 2^(scale - 127) as an FP32 bit pattern (subnormal for scale byte 0)
+        const float sc = __uint_as_float(scale ? scale << 23 : 1u << 22);
+        codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, __uint_as_float(w[0]), __uint_as_float(w[1]), sc, 0);
+        codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, __uint_as_float(w[2]), __uint_as_float(w[3]), sc, 1);
+        codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, __uint_as_float(w[4]), __uint_as_float(w[5]), sc, 2);
+        codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, __uint_as_float(w[6]), __uint_as_float(w[7]), sc, 3);
     }
     q[u] = codes;
     if ((u & 3) == 0) s[u >> 2] = (uint8_t)scale;

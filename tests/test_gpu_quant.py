@@ -131,6 +131,38 @@ def test_mx_f32_narrow_blocks(mx, orc):
     _assert_same(q, qo, "codes")
 
 
+def _every_mantissa_blocks(scale, col):
+    """Every FP32 mantissa, both signs, of the six binades just below and at the top of scale byte
+    `scale`'s range: magnitudes 2^(scale-127) * [1/8, 8) (from exponent field 0 where they reach it),
+    i.e. every value that rounds to a non-zero E2M1 code plus the binade below, which must round to
+    zero.  31 of them per block; column `col` holds the anchor 4 * 2^(scale-127) that fixes the block's
+    scale byte at `scale`."""
+    E = np.arange(max(0, scale - 3), scale + 3, dtype=np.uint32)
+    m = np.arange(1 << 23, dtype=np.uint32)
+    vals = ((E[:, None] << np.uint32(23)) | m[None, :]).ravel()
+    vals = np.concatenate([vals, vals | np.uint32(1 << 31)])
+    rows = -(-vals.size // 31)
+    flat = np.zeros(rows * 31, np.uint32)
+    flat[:vals.size] = vals
+    blk = np.empty((rows, 32), np.uint32)
+    blk[:, col] = np.uint32((scale + 2) << 23)
+    blk[:, np.delete(np.arange(32), col)] = flat.reshape(rows, 31)
+    rows = rows // 32 * 32  # whole 1024-value rows
+    return blk[:rows].reshape(-1, 1024).view(np.float32)
+
+
+@pytest.mark.parametrize("scale,col", [(0, 13), (1, 0), (2, 31), (127, 20), (252, 7)])
+def test_mx_f32_every_mantissa_near_the_grid(mx, orc, scale, col):
+    # scale bytes 0 and 1 divide by an FP32 subnormal or the smallest normal power of two, and their
+    # blocks hold FP32 subnormals; 252 is the largest scale byte a finite block can get
+    w = _every_mantissa_blocks(scale, col)
+    q, s = _gpu_mx_f32(mx, w)
+    qo, so = orc.mx_quant_f32(w, nthreads=16)
+    assert np.all(so == scale)
+    _assert_same(s, so, "scales")
+    _assert_same(q, qo, "codes")
+
+
 @pytest.mark.parametrize("name", ["tiny_a4w4", "oproj_decode_a4w4", "msweep_outlier_a4w4"])
 def test_mx_f32_weight_configs(mx, orc, name):
     w = synth.make_weight(synth.CONFIGS[name])
