@@ -10,7 +10,10 @@
 // keeps at least half of the CUs busy and fits the device at once; otherwise (a device with fewer CUs,
 // say) the ring kernels run and the workspace is not touched.  Other shapes take the kernels of
 // gemm_kernels.hpp: the decode rings for M <= 128 (K split over the waves of a workgroup) and the
-// LDS-tiled kernels above.  Measured (graph-replayed, rotated weights, us), split-K vs ring: K = 8192,
+// LDS-tiled kernels above, whose 128 x 128 tile kernel also splits K in two parts over 2 x tiles workgroups
+// when there are at most 128 tiles (M = 136 / 200 / 256, N = 7168, K = 8192: 20.6 / 20.8 / 20.9 vs 26.5 /
+// 26.3 / 26.9 us; past 128 tiles two workgroups per CU on a 2-slot ring gained 3% at M = 384 and nothing at
+// M = 512, and K parts of 256 x 224 tiles lost: their partials overflow the L2s).  Measured (graph-replayed, rotated weights, us), split-K vs ring: K = 8192,
 // N = 7168: M = 64 10.4 vs 12.4, M = 1 7.8 vs 8.4; K = 8192, N = 2048, M = 64: 6.6 vs 9.9; K = 16384,
 // N = 4096, M = 64: 11.1 vs 17.7.  At K = 4096 the rings are as fast or faster (N = 7168, M = 64: 7.4
 // vs 7.2), so they keep it.
@@ -101,6 +104,46 @@ RhPlan rh_plan(int64_t M, int64_t N, int64_t K) {
     return p;
 }
 
+// M > 128 with at most 128 output tiles of 128 x 128 (M <= 256 at N = 7168): one tile per workgroup would
+// leave half of the CUs idle or more, so K is split in two parts over 2 x tiles workgroups
+// (gemm_tile_fp4<VEC, 128, 4, 2>, one per CU) whose partials meet in the workspace (compact slots, 64 KB per
+// tile, at most 8 MiB).  K % 2048 == 0 (parts of whole scale blocks); tile t's two workgroups share an XCD.
+struct TilePlan {
+    int tiles_m = 0, tiles_n = 0;
+    int tiles() const { return tiles_m * tiles_n; }
+    int grid() const { return 16 * ((tiles() + 7) / 8); }
+    bool fits_device() const { return tiles_m != 0 && grid() <= device_cus(); }
+};
+
+TilePlan tile_plan(int64_t M, int64_t N, int64_t K) {
+    TilePlan p;
+    if (M <= 128 || N < 1 || K % 2048 != 0) return p;
+    const int64_t tm = (M + 127) / 128, tn = (N + 127) / 128;
+    if (tm * tn > 128) return p;
+    p.tiles_m = (int)tm;
+    p.tiles_n = (int)tn;
+    return p;
+}
+
+hipError_t launch_tile_split(const TilePlan& p, const void* qa, const void* sa, const void* qw, const void* sw,
+                             void* y, int64_t M, int64_t N, int64_t K, void* ws, hipStream_t st) {
+    const uint8_t* a = reinterpret_cast<const uint8_t*>(qa);
+    const uint8_t* w = reinterpret_cast<const uint8_t*>(qw);
+    const uint8_t* sa8 = reinterpret_cast<const uint8_t*>(sa);
+    const uint8_t* sw8 = reinterpret_cast<const uint8_t*>(sw);
+    uint16_t* out = reinterpret_cast<uint16_t*>(y);
+    uint8_t* w8 = reinterpret_cast<uint8_t*>(ws);
+    const dim3 grid((unsigned)p.grid()), block(256);
+    const int m = (int)M, n = (int)N, k = (int)K;
+    if (N % 8 == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0)
+        hipLaunchKernelGGL((gemm_tile_fp4<true, 128, 4, 2>), grid, block, 0, st, a, sa8, w, sw8, out, m, n, k,
+                           p.tiles_m, p.tiles_n, w8);
+    else
+        hipLaunchKernelGGL((gemm_tile_fp4<false, 128, 4, 2>), grid, block, 0, st, a, sa8, w, sw8, out, m, n, k,
+                           p.tiles_m, p.tiles_n, w8);
+    return hipGetLastError();
+}
+
 template <int NSL>
 hipError_t launch_rh_nsl(const RhPlan& p, const void* qa, const void* sa, const void* qw, const void* sw, void* y,
                          int64_t M, int64_t N, int64_t K, void* ws, hipStream_t st) {
@@ -176,7 +219,9 @@ size_t gemm_a4w4_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     const SplitPlan p = split_plan(M, N, K, false);
     if (p.nsl) return sk::workspace_bytes(p.tiles, p.kp, p.mf);
     const RhPlan r = rh_plan(M, N, K);
-    return r.kp ? sk::workspace_bytes(2 * r.tiles, r.kp, 2) : 0;
+    if (r.kp) return sk::workspace_bytes(2 * r.tiles, r.kp, 2);
+    const TilePlan t = tile_plan(M, N, K);
+    return t.tiles_m ? sk::workspace_bytes_compact(t.tiles(), 2, 4) : 0;
 }
 
 hipError_t launch_gemm_a4w4(const void* qa, const void* sa, const void* qw, const void* sw, void* y, int64_t M,
@@ -188,6 +233,9 @@ hipError_t launch_gemm_a4w4(const void* qa, const void* sa, const void* qw, cons
     if (workspace && aligned16(sa, sw) && r.fits_device())
         return r.nsl == 16 ? launch_rh_nsl<16>(r, qa, sa, qw, sw, y, M, N, K, workspace, st)
                            : launch_rh_nsl<32>(r, qa, sa, qw, sw, y, M, N, K, workspace, st);
+    const TilePlan t = tile_plan(M, N, K);
+    if (workspace && aligned16(sa, sw) && t.fits_device())
+        return launch_tile_split(t, qa, sa, qw, sw, y, M, N, K, workspace, st);
     return launch_gemm<false>(qa, sa, qw, sw, y, M, N, K, st);
 }
 

@@ -26,6 +26,7 @@
 // no scale shuffling.
 #pragma once
 
+#include "gemm_splitk.hpp"
 #include "mx_device.hpp"
 
 namespace mx {
@@ -1275,23 +1276,43 @@ struct Cfg {
 
 // VEC: N % 8 == 0 and y 16-byte aligned (whole 16-byte output stores allowed).  S: code slots of
 // the ring (2, or 4 for 128-row tiles when there is at most one tile per CU).
-template <bool VEC, int TM, int S = 2>
+// KP > 1 (128-row tiles): K split into KP parts of K / KP (a multiple of 1024) over KP workgroups per
+// tile, whose FP32 partials are summed by the split-K tail of gemm_splitk.hpp (sk::tail_sum, the
+// wave's 2 x 2 fragments as MF = 4, compact slots) in ws (zero-filled before first use and left zero;
+// sk::workspace_bytes_compact(tiles, KP, 4) bytes), so every workgroup of the grid must be resident at
+// once.
+// Workgroup b belongs to XCD b % 8's run of tiles x TX .. x TX + TX - 1 (x = b % 8, TX = ceil(tiles /
+// 8), tile t = tm + tiles_m tn, so an XCD's tiles share weight panels), as part (b / 8) % KP of tile
+// x TX + (b / 8) / KP: the parts of a tile sit on one XCD.  For KP == 1 the tiles follow tile_coords.
+template <bool VEC, int TM, int S = 2, int KP = 1>
 __global__ __launch_bounds__(256, 1) void gemm_tile_fp4(const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa,
                                                         const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw,
                                                         uint16_t* __restrict__ y, int M, int N, int K, int tiles_m,
-                                                        int tiles_n) {
+                                                        int tiles_n, uint8_t* __restrict__ ws) {
     using C = tile_fp4::Cfg<TM, S>;
     constexpr int FW = C::kFW;
+    static_assert(KP == 1 || TM == 128, "K parts for 128-row tiles");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[C::kLds];
 
-    int tm, tn;
-    tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    int tm, tn, kq = 0, tile = 0;  // kq: this workgroup's K part
+    if constexpr (KP == 1) {
+        tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    } else {
+        const int T = tiles_m * tiles_n, TX = (T + 7) >> 3, r = (int)blockIdx.x >> 3;
+        kq = r % KP;
+        tile = ((int)blockIdx.x & 7) * TX + r / KP;
+        if (tile >= T) return;  // padding of the last XCD's run: no part of any tile
+        tm = tile % tiles_m;
+        tn = tile / tiles_m;
+    }
     const int m0 = tm * TM, n0 = tn * TM;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wn = wave & 1, wm = wave >> 1;
     const int l32 = lane & 31, h = lane >> 5;
     const int64_t KB = (int64_t)K / 2, KS = (int64_t)K / 32;
-    const int nsup = K / 256;
+    const int nsup = K / KP / 256;              // superstages of this workgroup's K part
+    const int64_t kbase = kq * (KB / KP);       // code bytes of a row before the part
+    const int64_t sbase = kq * (KS / KP);       // scale bytes of a row before the part
 
     // code copy i (0 .. kCodeCopies-1): W rows for i < kHalfCopies, then A rows; copy i' = i mod
     // kHalfCopies moves rows 8 (kHalfCopies * wave + i') + lane / 8, the lane filling physical chunk
@@ -1307,7 +1328,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_fp4(const uint8_t* __restric
     }
     auto issue_code = [&](int u, int i) {  // copy i of superstage min(u, nsup - 1) into the slot of u
         uint8_t* slot = lds + (u % C::kS) * C::kSlot;
-        const int64_t koff = (int64_t)min(u, nsup - 1) * C::kRowBytes;
+        const int64_t koff = kbase + (int64_t)min(u, nsup - 1) * C::kRowBytes;
         if (i < C::kHalfCopies) g2lds16(wrow[i] + koff, slot + (C::kHalfCopies * wave + i) * 1024);
         else g2lds16(xrow[i - C::kHalfCopies] + koff, slot + C::kOpBytes + (C::kHalfCopies * wave + i - C::kHalfCopies) * 1024);
     };
@@ -1322,7 +1343,8 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_fp4(const uint8_t* __restric
         constexpr int half = C::kScaleCopies / 2;
         const int row = C::kScRowsPerCopy * (q % half) + lane / C::kScLanesPerRow;
         int64_t off = 32 * (int64_t)b + C::kScLane * (lane % C::kScLanesPerRow);
-        if (off >= KS) off = 0;  // past the last block: any in-row address, never read
+        if (off >= KS / KP) off = 0;  // past the end of the part's scale bytes: any in-row address, never read
+        off += sbase;
         const uint8_t* src = q < half ? sw + (int64_t)min(n0 + row, N - 1) * KS + off
                                       : sa + (int64_t)min(m0 + row, M - 1) * KS + off;
         uint8_t* dst = lds + C::kS * C::kSlot + (b % C::kNB) * C::kScaleBuf + q * 64 * C::kScLane;
@@ -1490,6 +1512,37 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_fp4(const uint8_t* __restric
     lds_wait_n_of<0, FW>(r1w, r1x);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
+
+    if constexpr (KP > 1) {
+        // the K parts' sum: fragment (f, g) is tail fragment FW f + g, its registers 4 j .. 4 j + 3 the 4
+        // consecutive n of one m stored below
+        v4f mine[FW * FW][4];
+#pragma unroll
+        for (int f = 0; f < FW; ++f)
+#pragma unroll
+            for (int g = 0; g < FW; ++g)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    mine[FW * f + g][j] = v4f{acc[f][g][4 * j], acc[f][g][4 * j + 1], acc[f][g][4 * j + 2],
+                                              acc[f][g][4 * j + 3]};
+        auto store_one = [&](int fr, int j, const v4f& v) {
+            const int f = fr / FW, g = fr % FW;
+            const int m = m0 + (TM / 2) * wm + 32 * g + l32, n = n0 + (TM / 2) * wn + 32 * f + 8 * j + 4 * h;
+            if (m >= M) return;
+            uint16_t* dst = y + (int64_t)m * N + n;
+            const uint32_t w2[2] = {bf16x2_rne(v[0], v[1]), bf16x2_rne(v[2], v[3])};
+            if (VEC && n + 3 < N) {
+                *reinterpret_cast<uint2*>(dst) = make_uint2(w2[0], w2[1]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (n + e < N) dst[e] = (uint16_t)(w2[e >> 1] >> (16 * (e & 1)));
+            }
+        };
+        sk::tail_sum<FW * FW, KP>(mine, ws, (int)sk::workspace_bytes_compact(tiles_m * tiles_n, KP, FW * FW), tile, kq,
+                                  wave, lane, store_one, std::true_type{});
+        return;
+    }
 
     // Epilogue through LDS: each wave writes its BF16 sub-tile row-major (padded pitch), then the
     // workgroup stores whole tile rows (2 TM bytes each).
@@ -2408,16 +2461,16 @@ inline hipError_t launch_gemm(const void* qa, const void* sa, const void* qw, co
             const bool deep = (int64_t)tm128 * tn128 <= kCUs;
             if (small && deep && vec16)
                 hipLaunchKernelGGL((gemm_tile_fp4<true, 128, 4>), g128, dim3(256), 0, st, a, sa8, w, sw8, out, m, n,
-                                   k, tm128, tn128);
+                                   k, tm128, tn128, nullptr);
             else if (small && deep)
                 hipLaunchKernelGGL((gemm_tile_fp4<false, 128, 4>), g128, dim3(256), 0, st, a, sa8, w, sw8, out, m, n,
-                                   k, tm128, tn128);
+                                   k, tm128, tn128, nullptr);
             else if (small && vec16)
                 hipLaunchKernelGGL((gemm_tile_fp4<true, 128>), g128, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k,
-                                   tm128, tn128);
+                                   tm128, tn128, nullptr);
             else if (small)
                 hipLaunchKernelGGL((gemm_tile_fp4<false, 128>), g128, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k,
-                                   tm128, tn128);
+                                   tm128, tn128, nullptr);
             else if (use224 && vec16)
                 hipLaunchKernelGGL(gemm_tile224_fp4<true>, g224, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k,
                                    tiles_m, tn224);
@@ -2426,10 +2479,10 @@ inline hipError_t launch_gemm(const void* qa, const void* sa, const void* qw, co
                                    tiles_m, tn224);
             else if (vec16)
                 hipLaunchKernelGGL((gemm_tile_fp4<true, 256>), g256, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k,
-                                   tiles_m, tiles_n);
+                                   tiles_m, tiles_n, nullptr);
             else
                 hipLaunchKernelGGL((gemm_tile_fp4<false, 256>), g256, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k,
-                                   tiles_m, tiles_n);
+                                   tiles_m, tiles_n, nullptr);
         }
         else if (!FP8 && K % 256 == 0)
             hipLaunchKernelGGL(gemm_tile_dma_fp4<4>, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, st, a,

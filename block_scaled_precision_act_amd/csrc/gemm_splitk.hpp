@@ -79,6 +79,10 @@ __host__ __device__ inline size_t workspace_bytes(int tiles, int KP, int MF) {
     return (size_t)tiles * KP * 4 * MF * 4096;
 }
 constexpr size_t kMaxWorkspaceBytes = (size_t)kMaxGrid * 4 * 2 * 4096;
+// The compact layout (tail_sum<..., true>) keeps only the slots that are written: KP - 1 per slice.
+__host__ __device__ inline size_t workspace_bytes_compact(int tiles, int KP, int MF) {
+    return (size_t)tiles * (KP - 1) * 4 * MF * 4096;
+}
 }  // namespace sk
 
 // FUSED prologue: quantize rows 0 .. M-1 of BF16 X, K-values 256 s0 .. 256 (s0 + NSL) - 1, into the LDS
@@ -173,16 +177,21 @@ constexpr int kSpinLimit = 1 << 18;       // polls before a tail gives up (about
 // count of polls keeps the kernel finite even if the co-residency the host checked were broken: the slice
 // is then stored as NaN, and a partial arriving after the owner gave up leaves the workspace non-zero, so
 // it must be zero-filled again before its next use.
-template <int MF, int KP, typename Store>
+template <int MF, int KP, typename Store, bool COMPACT = false>
 __device__ __forceinline__ void tail_sum(const v4f (&mine)[MF][4], uint8_t* ws, int ws_range, int t, int q, int wave,
-                                          int lane, Store&& store_one) {
+                                          int lane, Store&& store_one, std::bool_constant<COMPACT> = {}) {
     constexpr int R = KP < 4 * MF ? KP : 4 * MF;  // parts that own a slice
     constexpr int U = 4 * MF / R;                 // float4s per lane in a slice
     static_assert(U * R == 4 * MF, "slices of whole float4s");
     // slot (p, qq) of column group (t, wave): slice p of part qq, written by qq, read by p; float4 uu of lane
-    // l at + 1024 uu + 16 l.  R KP slots of 1024 U bytes per group: the group's share of the workspace.
+    // l at + 1024 uu + 16 l.  R KP slots of 1024 U bytes per group: the group's share of the workspace
+    // (COMPACT: R (KP - 1), leaving out the slots (p, p), which are never written).
     auto slot = [&](int p, int qq) -> uint32_t {
-        return (uint32_t)(((((size_t)t * 4 + wave) * R + p) * KP + qq) * (1024 * U) + 16 * lane);
+        if constexpr (COMPACT)
+            return (uint32_t)(((((size_t)t * 4 + wave) * R + p) * (KP - 1) + (qq < p ? qq : qq - 1)) * (1024 * U) +
+                              16 * lane);
+        else
+            return (uint32_t)(((((size_t)t * 4 + wave) * R + p) * KP + qq) * (1024 * U) + 16 * lane);
     };
     static_for<R>([&](auto pc) {
         constexpr int p = decltype(pc)::value;

@@ -94,12 +94,14 @@ mx_status mx_quant_weight_f32(const float *w, int64_t N, int64_t K,
 
 /*
  * Bytes of workspace mx_gemm_a4w4_bf16 needs for this shape: nonzero for the
- * decode sizes that split K across workgroups - M <= 64, K split into 4 or 8
- * parts of 2048 K-values, 128-column tiles x parts between 128 and 256
- * workgroups; 64 < M <= 128 in two 64-row halves, K split into 2 or 4 parts
- * of 4096 or 8192, 2 x tiles x parts between 128 and 256 - e.g. 7,340,032
- * bytes for the (64, 7168, 8192) and (128, 7168, 8192) layers, 8 MiB at most
- * - and 0 otherwise.  It depends on the shape only.  The
+ * sizes that split K across workgroups - M <= 64, K split into 4 or 8 parts
+ * of 2048 K-values, 128-column tiles x parts between 128 and 256 workgroups;
+ * 64 < M <= 128 in two 64-row halves, K split into 2 or 4 parts of 4096 or
+ * 8192, 2 x tiles x parts between 128 and 256; M > 128 with at most 128
+ * output tiles of 128 x 128 and K % 2048 == 0, K split into 2 parts (64 KB per
+ * tile) - e.g. 7,340,032 bytes for the (64, 7168, 8192), (128, 7168, 8192)
+ * and (256, 7168, 8192) layers, 8 MiB at most - and 0 otherwise.  It depends
+ * on the shape only.  The
  * workspace holds the FP32 partial slots through which the workgroups of a
  * tile exchange their partial sums; a slot word reads 0 until written.  It
  * must be zero-filled (e.g. hipMemset) before its first use; every call
@@ -119,10 +121,10 @@ size_t mx_gemm_a4w4_workspace_bytes(int64_t M, int64_t N, int64_t K);
  * y_bf16 2-byte aligned.  workspace: at least mx_gemm_a4w4_workspace_bytes(M,
  * N, K) bytes, 16-byte aligned, zero-filled before first use (see there);
  * may be NULL when that size is 0, else MX_ERROR_WORKSPACE.  The split-K
- * decode kernel sums the K parts of each output in a fixed order, so results
- * do not depend on timing.  Its workgroups wait for each other, so it runs
- * only when its whole grid fits the device's CUs at once (one workgroup per
- * CU); otherwise the workspace-free decode kernels run.  It relies on
+ * kernels sum the K parts of each output in a fixed order, so results
+ * do not depend on timing.  Their workgroups wait for each other, so they run
+ * only when the whole grid fits the device's CUs at once (one workgroup per
+ * CU); otherwise the workspace-free kernels run.  They rely on
  * workgroups being dealt round-robin to the XCDs (the parts of a tile meet in
  * one XCD's L2), and on no other work keeping CUs from the grid for long: a
  * workgroup waiting for a partner gives up after about 0.3 s, so that no

@@ -96,7 +96,14 @@ def test_gemm_argument_errors(mx):
     assert mx.mx_gemm_a4w4_workspace_bytes(128, 7168, 16384) == 2 * 56 * 2 * 4 * 2 * 4096   # parts of 8192
     assert mx.mx_gemm_a4w4_workspace_bytes(100, 2900, 16384) == 2 * 23 * 4 * 4 * 2 * 4096
     assert mx.mx_gemm_a4w4_workspace_bytes(128, 7168, 4096) == 0    # the two-row-halves ring
-    assert mx.mx_gemm_a4w4_workspace_bytes(129, 7168, 8192) == 0
+    # M > 128, at most 128 tiles of 128 x 128, K % 2048 == 0: two K parts, tiles x 4 waves x 4 fragments x 4 KB
+    # (compact slots: only the one written per slice and wave)
+    assert mx.mx_gemm_a4w4_workspace_bytes(129, 7168, 8192) == 112 * 4 * 4 * 4096
+    assert mx.mx_gemm_a4w4_workspace_bytes(256, 7168, 8192) == 112 * 4 * 4 * 4096
+    assert mx.mx_gemm_a4w4_workspace_bytes(200, 1000, 4096) == 16 * 4 * 4 * 4096
+    assert mx.mx_gemm_a4w4_workspace_bytes(2048, 1024, 2048) == 128 * 4 * 4 * 4096 == 8 << 20  # the largest
+    assert mx.mx_gemm_a4w4_workspace_bytes(257, 7168, 8192) == 0    # 168 tiles: one per workgroup
+    assert mx.mx_gemm_a4w4_workspace_bytes(256, 7168, 8192 + 1024) == 0   # K % 2048 != 0
     assert mx.mx_gemm_a4w4_workspace_bytes(64, 512, 8192) == 0      # too few tiles to split
     assert mx.mx_gemm_a4w4_workspace_bytes(64, 7168, 8192 + 128) == 0
     assert g4(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 4096, 8192, None, 0) == mx.MX_ERROR_WORKSPACE

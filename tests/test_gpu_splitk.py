@@ -1,6 +1,6 @@
-"""GPU parity of the split-K decode A4W4 GEMM (K split across workgroups, the partial tiles summed
-slice by slice across the tile's workgroups in K-part order), through the C ABI, against the oracle's
-exact GEMM: |gpu - exact| <= 2^-8 |exact| + 1e-6 sum|a w| per element, all outputs.
+"""GPU parity of the split-K A4W4 GEMMs (K split across workgroups, the partial tiles summed slice by
+slice across the tile's workgroups in K-part order), through the C ABI, against the oracle's exact
+GEMM: |gpu - exact| <= 2^-8 |exact| + 1e-6 sum|a w| per element, all outputs.
 
 Layer: the attention output projection of "Kimi-K3 DSpark O-Proj-only MXFP4", section "Exact
 quantization coverage" (weight (7168, 8192) MXFP4, (7168, 256) E8M0 scales, dynamic MXFP4
@@ -61,7 +61,18 @@ RH_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("M,N,K", SPLIT_SHAPES + RH_SHAPES)
+# M > 128 with at most 128 output tiles of 128 x 128 and K % 2048 == 0: the 128-row tile kernel with K in two
+# parts over 2 x tiles workgroups, one per CU (compact partial slots)
+TILE_SPLIT_SHAPES = [
+    (256, 7168, 8192),   # 112 tiles, 224 workgroups: the largest grid at the o_proj width
+    (129, 7168, 8192),   # one row in the second tile row
+    (200, 1000, 4096),   # N % 8 != 0 (element stores), ragged last tile, 16 tiles
+    (300, 2900, 2048),   # 69 tiles: idle workgroups in the last XCD's run
+    (1024, 1024, 8192),  # 64 tiles of a square GEMM
+]
+
+
+@pytest.mark.parametrize("M,N,K", SPLIT_SHAPES + RH_SHAPES + TILE_SPLIT_SHAPES)
 def test_splitk_matches_oracle(mx, orc, M, N, K):
     import torch
     wsb = mx.mx_gemm_a4w4_workspace_bytes(M, N, K)
@@ -83,7 +94,7 @@ def test_splitk_deterministic_and_workspace_reuse(mx, orc):
     the workgroups finish in); one workspace serves calls of different shapes in turn; and no
     write lands outside Y."""
     import torch
-    shapes = [(64, 4096, 8192), (20, 2000, 16384), (64, 2900, 16384)]
+    shapes = [(64, 4096, 8192), (20, 2000, 16384), (64, 2900, 16384), (200, 1000, 4096)]
     ops = [tuple(to_dev(a) for a in _operands(orc, 500 + i, *s)) for i, s in enumerate(shapes)]
     wsb = max(mx.mx_gemm_a4w4_workspace_bytes(*s) for s in shapes)
     ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")

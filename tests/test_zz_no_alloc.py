@@ -21,7 +21,8 @@ def _ops(orc, seed, M, N, K):
 
 def test_noalloc_matches_workspace_entry(mx, orc):
     import torch
-    shapes = [(64, 7168, 8192), (20, 2000, 16384), (64, 7168, 4096), (128, 4096, 8192), (64, 7168, 8192)]
+    shapes = [(64, 7168, 8192), (20, 2000, 16384), (64, 7168, 4096), (128, 4096, 8192), (200, 1000, 4096),
+              (64, 7168, 8192)]
     assert mx.mx_gemm_a4w4_workspace_bytes(*shapes[0]) > mx.mx_gemm_a4w4_workspace_bytes(*shapes[1]) > 0
     assert mx.mx_gemm_a4w4_workspace_bytes(*shapes[2]) == 0
     s = torch.cuda.current_stream().cuda_stream
