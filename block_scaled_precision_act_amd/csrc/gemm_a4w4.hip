@@ -10,10 +10,11 @@
 // keeps at least half of the CUs busy and fits the device at once; otherwise (a device with fewer CUs,
 // say) the ring kernels run and the workspace is not touched.  Other shapes take the kernels of
 // gemm_kernels.hpp: the decode rings for M <= 128 (K split over the waves of a workgroup) and the
-// LDS-tiled kernels above, whose 128 x 128 tile kernel also splits K in two parts over 2 x tiles workgroups
-// when there are at most 128 tiles (M = 136 / 200 / 256, N = 7168, K = 8192: 20.6 / 20.8 / 20.9 vs 26.5 /
-// 26.3 / 26.9 us; past 128 tiles two workgroups per CU on a 2-slot ring gained 3% at M = 384 and nothing at
-// M = 512, and K parts of 256 x 224 tiles lost: their partials overflow the L2s).  Measured (graph-replayed, rotated weights, us), split-K vs ring: K = 8192,
+// LDS-tiled kernels above, whose 128 x 128 tile kernel with copy and MFMA waves also splits K in two parts
+// over 2 x tiles workgroups when there are at most 128 tiles (M = 136 / 256, N = 7168, K = 8192: 16.7 /
+// 17.9-18.7 us against 19.4 / 21.0 us with full K; the 4-wave kernel's two parts took 20.6 / 20.9 us and
+// full K 26.5 / 26.9 us).  Past 128 tiles, two 4-wave workgroups per CU on a 2-slot ring gained 3% at
+// M = 384 and nothing at M = 512, and K parts of 256 x 224 tiles lost: their partials overflow the L2s.  Measured (graph-replayed, rotated weights, us), split-K vs ring: K = 8192,
 // N = 7168: M = 64 10.4 vs 12.4, M = 1 7.8 vs 8.4; K = 8192, N = 2048, M = 64: 6.6 vs 9.9; K = 16384,
 // N = 4096, M = 64: 11.1 vs 17.7.  At K = 4096 the rings are as fast or faster (N = 7168, M = 64: 7.4
 // vs 7.2), so they keep it.
@@ -106,7 +107,7 @@ RhPlan rh_plan(int64_t M, int64_t N, int64_t K) {
 
 // M > 128 with at most 128 output tiles of 128 x 128 (M <= 256 at N = 7168): one tile per workgroup would
 // leave half of the CUs idle or more, so K is split in two parts over 2 x tiles workgroups
-// (gemm_tile_fp4<VEC, 128, 4, 2>, one per CU) whose partials meet in the workspace (compact slots, 64 KB per
+// (gemm_tile128_pc_fp4<VEC, 2>, one per CU) whose partials meet in the workspace (compact slots, 64 KB per
 // tile, at most 8 MiB).  K % 2048 == 0 (parts of whole scale blocks); tile t's two workgroups share an XCD.
 struct TilePlan {
     int tiles_m = 0, tiles_n = 0;
@@ -133,13 +134,13 @@ hipError_t launch_tile_split(const TilePlan& p, const void* qa, const void* sa, 
     const uint8_t* sw8 = reinterpret_cast<const uint8_t*>(sw);
     uint16_t* out = reinterpret_cast<uint16_t*>(y);
     uint8_t* w8 = reinterpret_cast<uint8_t*>(ws);
-    const dim3 grid((unsigned)p.grid()), block(256);
+    const dim3 grid((unsigned)p.grid()), block(512);
     const int m = (int)M, n = (int)N, k = (int)K;
     if (N % 8 == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0)
-        hipLaunchKernelGGL((gemm_tile_fp4<true, 128, 4, 2>), grid, block, 0, st, a, sa8, w, sw8, out, m, n, k,
+        hipLaunchKernelGGL((gemm_tile128_pc_fp4<true, 2>), grid, block, 0, st, a, sa8, w, sw8, out, m, n, k,
                            p.tiles_m, p.tiles_n, w8);
     else
-        hipLaunchKernelGGL((gemm_tile_fp4<false, 128, 4, 2>), grid, block, 0, st, a, sa8, w, sw8, out, m, n, k,
+        hipLaunchKernelGGL((gemm_tile128_pc_fp4<false, 2>), grid, block, 0, st, a, sa8, w, sw8, out, m, n, k,
                            p.tiles_m, p.tiles_n, w8);
     return hipGetLastError();
 }

@@ -1276,43 +1276,23 @@ struct Cfg {
 
 // VEC: N % 8 == 0 and y 16-byte aligned (whole 16-byte output stores allowed).  S: code slots of
 // the ring (2, or 4 for 128-row tiles when there is at most one tile per CU).
-// KP > 1 (128-row tiles): K split into KP parts of K / KP (a multiple of 1024) over KP workgroups per
-// tile, whose FP32 partials are summed by the split-K tail of gemm_splitk.hpp (sk::tail_sum, the
-// wave's 2 x 2 fragments as MF = 4, compact slots) in ws (zero-filled before first use and left zero;
-// sk::workspace_bytes_compact(tiles, KP, 4) bytes), so every workgroup of the grid must be resident at
-// once.
-// Workgroup b belongs to XCD b % 8's run of tiles x TX .. x TX + TX - 1 (x = b % 8, TX = ceil(tiles /
-// 8), tile t = tm + tiles_m tn, so an XCD's tiles share weight panels), as part (b / 8) % KP of tile
-// x TX + (b / 8) / KP: the parts of a tile sit on one XCD.  For KP == 1 the tiles follow tile_coords.
-template <bool VEC, int TM, int S = 2, int KP = 1>
+template <bool VEC, int TM, int S = 2>
 __global__ __launch_bounds__(256, 1) void gemm_tile_fp4(const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa,
                                                         const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw,
                                                         uint16_t* __restrict__ y, int M, int N, int K, int tiles_m,
-                                                        int tiles_n, uint8_t* __restrict__ ws) {
+                                                        int tiles_n) {
     using C = tile_fp4::Cfg<TM, S>;
     constexpr int FW = C::kFW;
-    static_assert(KP == 1 || TM == 128, "K parts for 128-row tiles");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[C::kLds];
 
-    int tm, tn, kq = 0, tile = 0;  // kq: this workgroup's K part
-    if constexpr (KP == 1) {
-        tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
-    } else {
-        const int T = tiles_m * tiles_n, TX = (T + 7) >> 3, r = (int)blockIdx.x >> 3;
-        kq = r % KP;
-        tile = ((int)blockIdx.x & 7) * TX + r / KP;
-        if (tile >= T) return;  // padding of the last XCD's run: no part of any tile
-        tm = tile % tiles_m;
-        tn = tile / tiles_m;
-    }
+    int tm, tn;
+    tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * TM, n0 = tn * TM;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wn = wave & 1, wm = wave >> 1;
     const int l32 = lane & 31, h = lane >> 5;
     const int64_t KB = (int64_t)K / 2, KS = (int64_t)K / 32;
-    const int nsup = K / KP / 256;              // superstages of this workgroup's K part
-    const int64_t kbase = kq * (KB / KP);       // code bytes of a row before the part
-    const int64_t sbase = kq * (KS / KP);       // scale bytes of a row before the part
+    const int nsup = K / 256;
 
     // code copy i (0 .. kCodeCopies-1): W rows for i < kHalfCopies, then A rows; copy i' = i mod
     // kHalfCopies moves rows 8 (kHalfCopies * wave + i') + lane / 8, the lane filling physical chunk
@@ -1328,7 +1308,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_fp4(const uint8_t* __restric
     }
     auto issue_code = [&](int u, int i) {  // copy i of superstage min(u, nsup - 1) into the slot of u
         uint8_t* slot = lds + (u % C::kS) * C::kSlot;
-        const int64_t koff = kbase + (int64_t)min(u, nsup - 1) * C::kRowBytes;
+        const int64_t koff = (int64_t)min(u, nsup - 1) * C::kRowBytes;
         if (i < C::kHalfCopies) g2lds16(wrow[i] + koff, slot + (C::kHalfCopies * wave + i) * 1024);
         else g2lds16(xrow[i - C::kHalfCopies] + koff, slot + C::kOpBytes + (C::kHalfCopies * wave + i - C::kHalfCopies) * 1024);
     };
@@ -1343,8 +1323,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_fp4(const uint8_t* __restric
         constexpr int half = C::kScaleCopies / 2;
         const int row = C::kScRowsPerCopy * (q % half) + lane / C::kScLanesPerRow;
         int64_t off = 32 * (int64_t)b + C::kScLane * (lane % C::kScLanesPerRow);
-        if (off >= KS / KP) off = 0;  // past the end of the part's scale bytes: any in-row address, never read
-        off += sbase;
+        if (off >= KS) off = 0;  // past the last block: any in-row address, never read
         const uint8_t* src = q < half ? sw + (int64_t)min(n0 + row, N - 1) * KS + off
                                       : sa + (int64_t)min(m0 + row, M - 1) * KS + off;
         uint8_t* dst = lds + C::kS * C::kSlot + (b % C::kNB) * C::kScaleBuf + q * 64 * C::kScLane;
@@ -1513,37 +1492,6 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_fp4(const uint8_t* __restric
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
 
-    if constexpr (KP > 1) {
-        // the K parts' sum: fragment (f, g) is tail fragment FW f + g, its registers 4 j .. 4 j + 3 the 4
-        // consecutive n of one m stored below
-        v4f mine[FW * FW][4];
-#pragma unroll
-        for (int f = 0; f < FW; ++f)
-#pragma unroll
-            for (int g = 0; g < FW; ++g)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    mine[FW * f + g][j] = v4f{acc[f][g][4 * j], acc[f][g][4 * j + 1], acc[f][g][4 * j + 2],
-                                              acc[f][g][4 * j + 3]};
-        auto store_one = [&](int fr, int j, const v4f& v) {
-            const int f = fr / FW, g = fr % FW;
-            const int m = m0 + (TM / 2) * wm + 32 * g + l32, n = n0 + (TM / 2) * wn + 32 * f + 8 * j + 4 * h;
-            if (m >= M) return;
-            uint16_t* dst = y + (int64_t)m * N + n;
-            const uint32_t w2[2] = {bf16x2_rne(v[0], v[1]), bf16x2_rne(v[2], v[3])};
-            if (VEC && n + 3 < N) {
-                *reinterpret_cast<uint2*>(dst) = make_uint2(w2[0], w2[1]);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (n + e < N) dst[e] = (uint16_t)(w2[e >> 1] >> (16 * (e & 1)));
-            }
-        };
-        sk::tail_sum<FW * FW, KP>(mine, ws, (int)sk::workspace_bytes_compact(tiles_m * tiles_n, KP, FW * FW), tile, kq,
-                                  wave, lane, store_one, std::true_type{});
-        return;
-    }
-
     // Epilogue through LDS: each wave writes its BF16 sub-tile row-major (padded pitch), then the
     // workgroup stores whole tile rows (2 TM bytes each).
 #pragma unroll
@@ -1567,6 +1515,307 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_fp4(const uint8_t* __restric
 #pragma unroll 4
     for (int r = 0; r < TM / 4 / kRowsPerStore; ++r) {
         const int ml = (TM / 4) * wave + kRowsPerStore * r + lr;
+        const int m = m0 + ml;
+        const int n = n0 + 8 * lc;
+        const uint4 v = *reinterpret_cast<const uint4*>(lds + ml * C::kOutPitch + 16 * lc);
+        if (m >= M) continue;
+        uint16_t* dst = y + (int64_t)m * N + n;
+        if (VEC && n + 7 < N) {
+            *reinterpret_cast<uint4*>(dst) = v;
+        } else {
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (n + e < N) dst[e] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+        }
+    }
+}
+
+// ============================================================================
+// Tile path, FP4, 128 x 128 tiles when they fit one round (at most 256 tiles): the staging, ring and
+// MFMA schedule of gemm_tile_fp4<VEC, 128, 4>, split over 8 waves.  Waves 4..7 (producers) issue the
+// global -> LDS copies of codes and scales that wave w - 4 of the 4-wave kernel issues, and wait for
+// them; waves 0..3 (consumers) only read LDS and run the MFMAs of their 64 x 64 quarter.  Both meet at
+// the same barriers (one per superstage: every consumer done reading superstage u, every copy of u + 1
+// landed; then the producers refill u's slot with u + 4).  With one wave per SIMD the 4-wave kernel
+// serialised the copy issue and waits, the LDS reads and the MFMAs (their costs added up); here each
+// SIMD holds a consumer and a producer (159 registers per wave, so two fit), and the copies leave the
+// MFMA waves' instruction stream.  Measured at N = 7168, K = 8192 (graph-replayed, 4 rotated weight
+// copies, bit-identical outputs): M = 300 / 384 / 512: 20.4 / 20.9–21.2 / 22.9–24.9 us against 26.6 /
+// 26.9–27.2 / 28.1–30.2 us.
+// KP > 1: K split into KP parts of K / KP (a multiple of 1024) over KP workgroups per tile, whose FP32
+// partials the consumers sum through the split-K tail of gemm_splitk.hpp (sk::tail_sum, a consumer's
+// 2 x 2 fragments as MF = 4, compact slots) in ws (zero-filled before first use and left zero;
+// sk::workspace_bytes_compact(tiles, KP, 4) bytes), so every workgroup of the grid must be resident at
+// once.  Workgroup b belongs to XCD b % 8's run of tiles x TX .. x TX + TX - 1 (x = b % 8, TX =
+// ceil(tiles / 8), tile t = tm + tiles_m tn, so an XCD's tiles share weight panels), as part (b / 8) % KP
+// of tile x TX + (b / 8) / KP: the parts of a tile sit on one XCD.  KP == 1 follows tile_coords.
+// ============================================================================
+template <bool VEC, int KP = 1>
+__global__ __launch_bounds__(512, 1) void gemm_tile128_pc_fp4(const uint8_t* __restrict__ qa,
+                                                              const uint8_t* __restrict__ sa,
+                                                              const uint8_t* __restrict__ qw,
+                                                              const uint8_t* __restrict__ sw, uint16_t* __restrict__ y,
+                                                              int M, int N, int K, int tiles_m, int tiles_n,
+                                                              uint8_t* __restrict__ ws) {
+    constexpr int TM = 128;
+    using C = tile_fp4::Cfg<TM, 4>;
+    constexpr int FW = C::kFW;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[C::kLds];
+
+    int tm, tn, kq = 0, tile = 0;  // kq: this workgroup's K part
+    if constexpr (KP == 1) {
+        tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    } else {
+        const int T = tiles_m * tiles_n, TX = (T + 7) >> 3, r = (int)blockIdx.x >> 3;
+        kq = r % KP;
+        tile = ((int)blockIdx.x & 7) * TX + r / KP;
+        if (tile >= T) return;  // padding of the last XCD's run: no part of any tile
+        tm = tile % tiles_m;
+        tn = tile / tiles_m;
+    }
+    const int m0 = tm * TM, n0 = tn * TM;
+    const int lane = threadIdx.x & 63;
+    const int wave8 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform role
+    const int wave = wave8 & 3;  // the 4-wave kernel's wave whose copies (producer) or quarter (consumer) this is
+    const int64_t KB = (int64_t)K / 2, KS = (int64_t)K / 32;
+    const int nsup = K / KP / 256;                     // superstages of this workgroup's K part
+    const int64_t kbase = kq * (KB / KP), sbase = kq * (KS / KP);  // code / scale bytes of a row before it
+    constexpr int kBatch = C::kCodeCopies + C::kScPerWave;          // copies per producer and superstage
+
+    if (wave8 >= 4) {
+        // Producer.  Code copy i (0 .. kCodeCopies-1): W rows for i < kHalfCopies, then A rows; copy
+        // i' = i mod kHalfCopies moves rows 8 (kHalfCopies * wave + i') + lane / 8, the lane filling
+        // physical chunk lane % 8 with logical chunk (lane % 8) ^ ((row / 2) % 8).
+        const uint8_t* wrow[C::kHalfCopies];
+        const uint8_t* xrow[C::kHalfCopies];
+#pragma unroll
+        for (int i = 0; i < C::kHalfCopies; ++i) {
+            const int row = 8 * (C::kHalfCopies * wave + i) + (lane >> 3);
+            const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+            wrow[i] = qw + (int64_t)min(n0 + row, N - 1) * KB + 16 * chunk;
+            xrow[i] = qa + (int64_t)min(m0 + row, M - 1) * KB + 16 * chunk;
+        }
+        auto issue_code = [&](int u, int i) {  // copy i of superstage min(u, nsup - 1) into the slot of u
+            uint8_t* slot = lds + (u % C::kS) * C::kSlot;
+            const int64_t koff = kbase + (int64_t)min(u, nsup - 1) * C::kRowBytes;
+            if (i < C::kHalfCopies) g2lds16(wrow[i] + koff, slot + (C::kHalfCopies * wave + i) * 1024);
+            else
+                g2lds16(xrow[i - C::kHalfCopies] + koff,
+                        slot + C::kOpBytes + (C::kHalfCopies * wave + i - C::kHalfCopies) * 1024);
+        };
+        // scale copy q of block b: as in gemm_tile_fp4 (4 bytes per lane; part j of a block travels with
+        // the codes of superstage 4b - 3 + j), within this workgroup's K part
+        auto issue_scale_copy = [&](int q, int b) {
+            constexpr int half = C::kScaleCopies / 2;
+            const int row = C::kScRowsPerCopy * (q % half) + lane / C::kScLanesPerRow;
+            int64_t off = 32 * (int64_t)b + C::kScLane * (lane % C::kScLanesPerRow);
+            if (off >= KS / KP) off = 0;  // past the part's scale bytes: any in-row address, never read
+            off += sbase;
+            const uint8_t* src = q < half ? sw + (int64_t)min(n0 + row, N - 1) * KS + off
+                                          : sa + (int64_t)min(m0 + row, M - 1) * KS + off;
+            g2lds4(src, lds + C::kS * C::kSlot + (b % C::kNB) * C::kScaleBuf + q * 64 * C::kScLane);
+        };
+        auto issue_scale = [&](int u) {  // the scale part travelling with superstage u
+#pragma unroll
+            for (int c = 0; c < C::kScPerWave; ++c)
+                issue_scale_copy(4 * C::kScPerWave * ((u + 3) & 3) + C::kScPerWave * wave + c, (u + 3) >> 2);
+        };
+        auto batch = [&](int u) {
+            issue_scale(u);
+#pragma unroll
+            for (int i = 0; i < C::kCodeCopies; ++i) issue_code(u, i);
+        };
+        // prologue: scale block 0, the codes of superstage 0, then the batches of superstages 1 .. S - 1
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int c = 0; c < C::kScPerWave; ++c) issue_scale_copy(4 * C::kScPerWave * j + C::kScPerWave * wave + c, 0);
+#pragma unroll
+        for (int i = 0; i < C::kCodeCopies; ++i) issue_code(0, i);
+#pragma unroll
+        for (int v = 1; v < C::kS; ++v) batch(v);
+        wait_vmcnt<(C::kS - 1) * kBatch>();  // superstage 0 and scale block 0 are in
+        __builtin_amdgcn_s_barrier();
+        // barrier of superstage u: this wave's copies of u + 1 have landed (those of u + 2 .. u + S - 1
+        // may be in flight); then the slot of u takes u + S.  The last S barriers refill nothing, and their
+        // waits count down to the batches still in flight (with fewer superstages than slots the prologue's
+        // extra batches only make them wait longer).
+        for (int u = 0; u < nsup - C::kS; ++u) {
+            wait_vmcnt<(C::kS - 2) * kBatch>();
+            __builtin_amdgcn_s_barrier();
+            batch(u + C::kS);
+        }
+        static_for<C::kS>([&](auto t) {
+            constexpr int T = decltype(t)::value;
+            if (nsup - C::kS + T >= 0) {
+                wait_vmcnt<(C::kS - 2 - T > 0 ? C::kS - 2 - T : 0) * kBatch>();
+                __builtin_amdgcn_s_barrier();
+            }
+        });
+        wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();  // the consumers' barrier before the epilogue: no copy lands after it
+    } else {
+        // Consumer: the LDS reads and MFMAs of the 4-wave kernel's wave, 2 x 2 fragments of 32 x 32.
+        const int wn = wave & 1, wm = wave >> 1;
+        const int l32 = lane & 31, h = lane >> 5;
+        int woff[FW], xoff[FW], wsoff[FW], xsoff[FW];
+#pragma unroll
+        for (int f = 0; f < FW; ++f) {
+            const int wr = (TM / 2) * wn + 32 * f + l32, xr = (TM / 2) * wm + 32 * f + l32;
+            woff[f] = wr * C::kRowBytes + ((wr >> 1) & 7);  // low bits: the swizzle key, split off below
+            xoff[f] = C::kOpBytes + xr * C::kRowBytes + ((xr >> 1) & 7);
+            wsoff[f] = wr * C::kScaleRow + 4 * h;
+            xsoff[f] = (C::kRows + xr) * C::kScaleRow + 4 * h;
+        }
+        const uint32_t base = lds_addr(lds);
+        auto rd_step = [&](v4u (&rw)[FW], v4u (&rx)[FW], int u, int t) {
+            const uint32_t sb = base + (u % C::kS) * C::kSlot;
+#pragma unroll
+            for (int f = 0; f < FW; ++f) {
+                rw[f] = lds_read16(sb + (woff[f] & ~7) + 16 * ((4 * h + t) ^ (woff[f] & 7)));
+                rx[f] = lds_read16(sb + (xoff[f] & ~7) + 16 * ((4 * h + t) ^ (xoff[f] & 7)));
+            }
+        };
+        // read i (0 .. 2 FW - 1) of k-step t of superstage u: fragment i / 2 of W (even i) or of A (odd i)
+        auto rd_one = [&](v4u (&rw)[FW], v4u (&rx)[FW], int u, int t, int i) {
+            const uint32_t sb = base + (u % C::kS) * C::kSlot;
+            const int f = i >> 1;
+            if (i & 1) rx[f] = lds_read16(sb + (xoff[f] & ~7) + 16 * ((4 * h + t) ^ (xoff[f] & 7)));
+            else rw[f] = lds_read16(sb + (woff[f] & ~7) + 16 * ((4 * h + t) ^ (woff[f] & 7)));
+        };
+        auto rd_scales = [&](uint32_t (&ws4)[FW], uint32_t (&xs4)[FW], int u) {
+            const uint32_t scb = base + C::kS * C::kSlot + ((u >> 2) % C::kNB) * C::kScaleBuf + 8 * (u & 3);
+#pragma unroll
+            for (int f = 0; f < FW; ++f) {
+                ws4[f] = lds_read4(scb + wsoff[f]);
+                xs4[f] = lds_read4(scb + xsoff[f]);
+            }
+        };
+        v16f acc[FW][FW];
+#pragma unroll
+        for (int f = 0; f < FW; ++f)
+#pragma unroll
+            for (int g = 0; g < FW; ++g)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[f][g][r] = 0.f;
+        __builtin_amdgcn_s_barrier();  // superstage 0 and scale block 0 are in
+        __builtin_amdgcn_sched_barrier(0);
+        uint32_t wsc[FW], xsc[FW];
+        v4u r0w[FW], r0x[FW], r1w[FW], r1x[FW], r2w[FW], r2x[FW], r3w[FW], r3x[FW];
+        rd_scales(wsc, xsc, 0);
+        rd_step(r0w, r0x, 0, 0);
+        rd_step(r1w, r1x, 0, 1);
+        // the FW^2 MFMAs of k-step T with the 2 FW operand reads of k-step TN between them
+#define MX_STEP_RD(RW, RX, T, NW, NX, TN)                                                                          \
+    _Pragma("unroll") for (int f = 0; f < FW; ++f) _Pragma("unroll") for (int g = 0; g < FW; ++g) {               \
+        acc[f][g] = mfma32<kFmtFP4, T>(fp4_operand(RW[f]), fp4_operand(RX[g]), acc[f][g], (int)wsc[f], (int)xsc[g]); \
+        if (((f * FW + g) % (FW / 2)) == FW / 2 - 1) rd_one(NW, NX, u, TN, (f * FW + g) / (FW / 2));             \
+        __builtin_amdgcn_sched_barrier(0);                                                                         \
+    }
+        // superstage u: k-steps 0 and 1, the barrier, then k-steps 2 and 3 with the scale reads and the
+        // k-step 0 and 1 reads of u + 1 between the MFMAs (past the end these read stale data, never used)
+        auto step = [&](int u) __attribute__((always_inline)) {
+            lds_wait_first_n<FW>(r0w, r0x, wsc, xsc);  // scales and k-step 0
+            __builtin_amdgcn_sched_barrier(0);
+            MX_STEP_RD(r0w, r0x, 0, r2w, r2x, 2)
+            lds_wait_n_of<2 * FW, FW>(r1w, r1x);
+            __builtin_amdgcn_sched_barrier(0);
+            MX_STEP_RD(r1w, r1x, 1, r3w, r3x, 3)
+            lds_wait_n_of<0, FW>(r2w, r2x);
+            lds_wait_n_of<0, FW>(r3w, r3x);
+            __builtin_amdgcn_s_barrier();  // every consumer done reading u; every copy of u + 1 landed
+            __builtin_amdgcn_sched_barrier(0);
+            uint32_t wsk[FW], xsk[FW];  // the scales of u, still needed for k-steps 2 and 3
+#pragma unroll
+            for (int f = 0; f < FW; ++f) {
+                wsk[f] = wsc[f];
+                xsk[f] = xsc[f];
+            }
+            rd_scales(wsc, xsc, u + 1);
+            constexpr int kRdEvery = (2 * FW * FW) / (4 * FW);
+#pragma unroll
+            for (int t = 2; t < 4; ++t)
+#pragma unroll
+                for (int f = 0; f < FW; ++f)
+#pragma unroll
+                    for (int g = 0; g < FW; ++g) {
+                        const int i = (t - 2) * FW * FW + f * FW + g;
+                        if (t == 2)
+                            acc[f][g] = mfma32<kFmtFP4, 2>(fp4_operand(r2w[f]), fp4_operand(r2x[g]), acc[f][g],
+                                                           (int)wsk[f], (int)xsk[g]);
+                        else
+                            acc[f][g] = mfma32<kFmtFP4, 3>(fp4_operand(r3w[f]), fp4_operand(r3x[g]), acc[f][g],
+                                                           (int)wsk[f], (int)xsk[g]);
+                        if ((i % kRdEvery) == kRdEvery - 1) {
+                            const int ri = i / kRdEvery;
+                            if (ri < 2 * FW) rd_one(r0w, r0x, u + 1, 0, ri);
+                            else rd_one(r1w, r1x, u + 1, 1, ri - 2 * FW);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+        };
+        for (int u = 0; u < nsup; ++u) step(u);
+#undef MX_STEP_RD
+        lds_wait_n_of<0, FW>(r0w, r0x);
+        lds_wait_n_of<0, FW>(r1w, r1x);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (KP > 1) {
+            // the K parts' sum: fragment (f, g) is tail fragment FW f + g, its registers 4 j .. 4 j + 3
+            // the 4 consecutive n of one m
+            v4f mine[FW * FW][4];
+#pragma unroll
+            for (int f = 0; f < FW; ++f)
+#pragma unroll
+                for (int g = 0; g < FW; ++g)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        mine[FW * f + g][j] = v4f{acc[f][g][4 * j], acc[f][g][4 * j + 1], acc[f][g][4 * j + 2],
+                                                  acc[f][g][4 * j + 3]};
+            auto store_one = [&](int fr, int j, const v4f& v) {
+                const int f = fr / FW, g = fr % FW;
+                const int m = m0 + (TM / 2) * wm + 32 * g + l32, n = n0 + (TM / 2) * wn + 32 * f + 8 * j + 4 * h;
+                if (m >= M) return;
+                uint16_t* dst = y + (int64_t)m * N + n;
+                const uint32_t w2[2] = {bf16x2_rne(v[0], v[1]), bf16x2_rne(v[2], v[3])};
+                if (VEC && n + 3 < N) {
+                    *reinterpret_cast<uint2*>(dst) = make_uint2(w2[0], w2[1]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < N) dst[e] = (uint16_t)(w2[e >> 1] >> (16 * (e & 1)));
+                }
+            };
+            sk::tail_sum<FW * FW, KP>(mine, ws, (int)sk::workspace_bytes_compact(tiles_m * tiles_n, KP, FW * FW), tile,
+                                      kq, wave, lane, store_one, std::true_type{});
+        } else {
+            // BF16 sub-tile into LDS (padded pitch) for whole-row stores below
+#pragma unroll
+            for (int g = 0; g < FW; ++g) {
+                const int ml = (TM / 2) * wm + 32 * g + l32;
+#pragma unroll
+                for (int f = 0; f < FW; ++f)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int nl = (TM / 2) * wn + 32 * f + 8 * j + 4 * h;
+                        uint2 pk;
+                        pk.x = bf16x2_rne(acc[f][g][4 * j], acc[f][g][4 * j + 1]);
+                        pk.y = bf16x2_rne(acc[f][g][4 * j + 2], acc[f][g][4 * j + 3]);
+                        *reinterpret_cast<uint2*>(lds + ml * C::kOutPitch + 2 * nl) = pk;
+                    }
+            }
+        }
+    }
+    if constexpr (KP > 1) return;
+    __syncthreads();
+    // all 8 waves store whole tile rows (2 TM bytes each): wave w rows 16 w .. 16 w + 15
+    constexpr int kLanesPerRow = TM / 8;  // 16-byte pieces per tile row
+    constexpr int kRowsPerStore = 64 / kLanesPerRow;
+    const int lr = lane / kLanesPerRow, lc = lane % kLanesPerRow;
+#pragma unroll
+    for (int r = 0; r < TM / 8 / kRowsPerStore; ++r) {
+        const int ml = (TM / 8) * wave8 + kRowsPerStore * r + lr;
         const int m = m0 + ml;
         const int n = n0 + 8 * lc;
         const uint4 v = *reinterpret_cast<const uint4*>(lds + ml * C::kOutPitch + 16 * lc);
@@ -2457,20 +2706,21 @@ inline hipError_t launch_gemm(const void* qa, const void* sa, const void* qw, co
             const bool use224 = 7 * ((t224 + kCUs - 1) / kCUs) < 8 * ((t256 + kCUs - 1) / kCUs) &&
                                 (M > N ? M : N) * (K / 2) < ((int64_t)1 << 31);
             const dim3 g256((unsigned)t256), g128((unsigned)(tm128 * tn128)), g224((unsigned)t224);
-            // at most one 128-tile per CU: the deeper ring (152 KB of LDS); more: two workgroups per CU
+            // at most one 128-tile per CU: the deeper ring (152 KB of LDS) with copy and MFMA waves; more: two
+            // 4-wave workgroups per CU
             const bool deep = (int64_t)tm128 * tn128 <= kCUs;
             if (small && deep && vec16)
-                hipLaunchKernelGGL((gemm_tile_fp4<true, 128, 4>), g128, dim3(256), 0, st, a, sa8, w, sw8, out, m, n,
+                hipLaunchKernelGGL((gemm_tile128_pc_fp4<true, 1>), g128, dim3(512), 0, st, a, sa8, w, sw8, out, m, n,
                                    k, tm128, tn128, nullptr);
             else if (small && deep)
-                hipLaunchKernelGGL((gemm_tile_fp4<false, 128, 4>), g128, dim3(256), 0, st, a, sa8, w, sw8, out, m, n,
+                hipLaunchKernelGGL((gemm_tile128_pc_fp4<false, 1>), g128, dim3(512), 0, st, a, sa8, w, sw8, out, m, n,
                                    k, tm128, tn128, nullptr);
             else if (small && vec16)
                 hipLaunchKernelGGL((gemm_tile_fp4<true, 128>), g128, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k,
-                                   tm128, tn128, nullptr);
+                                   tm128, tn128);
             else if (small)
                 hipLaunchKernelGGL((gemm_tile_fp4<false, 128>), g128, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k,
-                                   tm128, tn128, nullptr);
+                                   tm128, tn128);
             else if (use224 && vec16)
                 hipLaunchKernelGGL(gemm_tile224_fp4<true>, g224, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k,
                                    tiles_m, tn224);
@@ -2479,10 +2729,10 @@ inline hipError_t launch_gemm(const void* qa, const void* sa, const void* qw, co
                                    tiles_m, tn224);
             else if (vec16)
                 hipLaunchKernelGGL((gemm_tile_fp4<true, 256>), g256, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k,
-                                   tiles_m, tiles_n, nullptr);
+                                   tiles_m, tiles_n);
             else
                 hipLaunchKernelGGL((gemm_tile_fp4<false, 256>), g256, dim3(256), 0, st, a, sa8, w, sw8, out, m, n, k,
-                                   tiles_m, tiles_n, nullptr);
+                                   tiles_m, tiles_n);
         }
         else if (!FP8 && K % 256 == 0)
             hipLaunchKernelGGL(gemm_tile_dma_fp4<4>, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, st, a,

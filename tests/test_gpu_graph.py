@@ -35,7 +35,7 @@ def _replays_match(mx, torch, thunk, outs):
         del junk
 
 
-# decode rings (64, 16 rows), the 128-row tile with the 4-slot ring (300), the 256 x 224 tile (1300 x 7000),
+# decode rings (64, 16 rows), the 128-row tile with copy and MFMA waves (300), the 256 x 224 tile (1300 x 7000),
 # the split-K decode kernel (64 x 7168 x 8192) and the 128-row tile with K in two parts (256 x 2048 x 8192)
 @pytest.mark.parametrize("M,N,K", [(64, 512, 1024), (300, 512, 1024), (64, 7168, 8192), (16, 2000, 4096),
                                    (1300, 7000, 512), (256, 2048, 8192)])

@@ -80,7 +80,7 @@ A4W4_FAMILIES = [
     ("split-K decode, 32 rows", 24, 4000, 8192),
     ("split-K decode, 64 rows", 64, 4000, 8192),
     ("split-K decode, two row halves", 100, 4000, 8192),
-    ("128-row tile, 4-slot ring", 300, 256, 1024),
+    ("128-row tile, copy and MFMA waves", 300, 256, 1024),
     ("128-row tile, two K parts", 300, 512, 2048),
     ("128-row tile, 2-slot ring", 2200, 3896, 512),
     ("256 x 224 tile", 1300, 7000, 512),
