@@ -9,7 +9,17 @@
 // Measured (graph-replayed, rotated weights, N = 7168, K = 8192): M = 64 15.7
 // vs 18.6 us for the decode ring, M = 48 14.6 vs 17.2 us; at M <= 32 the ring
 // is as fast or faster (M = 1 11.4 vs 13.0, M = 32 13.4 vs 13.1 us), so it
-// keeps those.  Everything else runs the kernels of gemm_kernels.hpp.
+// keeps those.
+//
+// M > 128 where the 256 x 224 tiles number at most 128: each tile takes one
+// workgroup about 133 us at K = 8192 (the FP16 MFMAs bound it), so a few tiles
+// would leave most CUs idle.  K is split into KP = 8, 4 or 2 parts (the largest
+// whose grid, 8 KP ceil(tiles / 8) workgroups, fits the CUs, with parts of at
+// least 1024), summed in the caller's workspace (gemm_tile224_fp8<VEC, KP>).
+// Measured (graph-replayed, rotated weights, N = 7168, K = 8192), split vs one
+// workgroup per tile: M = 136 / 256 48.8 / 51.6 us (KP = 8) vs 133; M = 512
+// 70.4 us (KP = 4; 86.0 with 2) vs 134; M = 768 / 1024 93.0 / 103.8 us (KP = 2)
+// vs 135.  Everything else runs the kernels of gemm_kernels.hpp.
 #include "gemm_kernels.hpp"
 #include "gemm_splitk.hpp"
 #include "launch.hpp"
@@ -39,11 +49,53 @@ Split8 split8_plan(int64_t M, int64_t N, int64_t K) {
     return p;
 }
 
+// M > 128 on 256 x 224 tiles with K in parts (see the file comment); kp == 0 if none
+struct Tile8 {
+    int kp = 0, tiles_m = 0, tiles_n = 0;
+    int tiles() const { return tiles_m * tiles_n; }
+    int grid() const { return 8 * kp * ((tiles() + 7) / 8); }
+    bool fits_device() const { return kp != 0 && grid() <= device_cus(); }
+};
+
+Tile8 tile8_plan(int64_t M, int64_t N, int64_t K) {
+    Tile8 p;
+    if (M <= 128 || N < 1 || (M > N ? M : N) * K >= ((int64_t)1 << 31)) return p;
+    const int64_t tm = (M + tile224_fp8::kTM - 1) / tile224_fp8::kTM, tn = (N + tile224_fp8::kTN - 1) / tile224_fp8::kTN;
+    if (tm * tn > 128) return p;
+    for (int kp : {8, 4, 2}) {
+        if (K % (128 * kp) != 0 || K / kp < 1024 || 8 * kp * ((tm * tn + 7) / 8) > sk::kMaxGrid) continue;
+        p.kp = kp;
+        p.tiles_m = (int)tm;
+        p.tiles_n = (int)tn;
+        return p;
+    }
+    return p;
+}
+
+template <int KP>
+hipError_t launch_tile8(const Tile8& p, const void* qa, const float* sa, const void* qw, const float* sw, void* y,
+                        int64_t M, int64_t N, int64_t K, void* ws, hipStream_t st) {
+    const uint8_t* a = reinterpret_cast<const uint8_t*>(qa);
+    const uint8_t* w = reinterpret_cast<const uint8_t*>(qw);
+    uint16_t* out = reinterpret_cast<uint16_t*>(y);
+    uint8_t* w8 = reinterpret_cast<uint8_t*>(ws);
+    const dim3 grid((unsigned)p.grid()), block(256);
+    if (N % 8 == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0)
+        hipLaunchKernelGGL((gemm_tile224_fp8<true, KP>), grid, block, 0, st, a, sa, w, sw, out, (int)M, (int)N, (int)K,
+                           p.tiles_m, p.tiles_n, w8);
+    else
+        hipLaunchKernelGGL((gemm_tile224_fp8<false, KP>), grid, block, 0, st, a, sa, w, sw, out, (int)M, (int)N,
+                           (int)K, p.tiles_m, p.tiles_n, w8);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 size_t gemm_a8w8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     const Split8 p = split8_plan(M, N, K);
-    return p.kp ? sk::workspace_bytes(p.tiles, p.kp, 2) : 0;
+    if (p.kp) return sk::workspace_bytes(p.tiles, p.kp, 2);
+    const Tile8 t = tile8_plan(M, N, K);
+    return t.kp ? sk::workspace_bytes_chunked(t.tiles(), t.kp, tile224_fp8::kMf) : 0;
 }
 
 hipError_t launch_gemm_a8w8(const void* qa, const float* sa, const void* qw, const float* sw, void* y, int64_t M,
@@ -63,6 +115,14 @@ hipError_t launch_gemm_a8w8(const void* qa, const float* sa, const void* qw, con
             hipLaunchKernelGGL((gemm_splitk_fp8<2, 3, kNsl8, 8>), grid, block, 0, st, a, sa, w, sw, out, (int)M, (int)N,
                                (int)K, p.tiles, ws);
         return hipGetLastError();
+    }
+    const Tile8 t = tile8_plan(M, N, K);
+    if (workspace && t.fits_device()) {
+        switch (t.kp) {
+            case 8: return launch_tile8<8>(t, qa, sa, qw, sw, y, M, N, K, workspace, st);
+            case 4: return launch_tile8<4>(t, qa, sa, qw, sw, y, M, N, K, workspace, st);
+            default: return launch_tile8<2>(t, qa, sa, qw, sw, y, M, N, K, workspace, st);
+        }
     }
     return launch_gemm<true>(qa, sa, qw, sw, y, M, N, K, st);
 }

@@ -2357,24 +2357,42 @@ static_assert(kLds <= 160 * 1024, "LDS");
 }  // namespace tile224_fp8
 
 // VEC: N % 8 == 0 and y 16-byte aligned (whole 16-byte output stores allowed).
-template <bool VEC>
+// KP > 1: K split into KP parts of K / KP (a multiple of 128) over KP workgroups per tile.  Their FP32
+// accumulators (before the scales) are summed in K-part order by sk::tail_sum_chunked in ws (zero-filled
+// before first use and left zero; sk::workspace_bytes_chunked(tiles, KP, 56) bytes), and the sum is scaled
+// and rounded as the KP == 1 epilogue does; every workgroup of the grid must be resident at once.
+// Workgroup b belongs to XCD b % 8's run of tiles x TX .. x TX + TX - 1 (x = b % 8, TX = ceil(tiles / 8),
+// tile t = tm + tiles_m tn), as part (b / 8) % KP of tile x TX + (b / 8) / KP: the parts of a tile sit on one
+// XCD.  KP == 1 follows tile_coords.
+template <bool VEC, int KP = 1>
 __global__ __launch_bounds__(256, 1) void gemm_tile224_fp8(const uint8_t* __restrict__ qa,
                                                            const float* __restrict__ sa,
                                                            const uint8_t* __restrict__ qw,
                                                            const float* __restrict__ sw, uint16_t* __restrict__ y,
-                                                           int M, int N, int K, int tiles_m, int tiles_n) {
+                                                           int M, int N, int K, int tiles_m, int tiles_n,
+                                                           uint8_t* __restrict__ ws) {
     using namespace tile224_fp8;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
 
-    int tm, tn;
-    tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    int tm, tn, kq = 0, tile = 0;  // kq: this workgroup's K part
+    if constexpr (KP == 1) {
+        tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    } else {
+        const int T = tiles_m * tiles_n, TX = (T + 7) >> 3, r = (int)blockIdx.x >> 3;
+        kq = r % KP;
+        tile = ((int)blockIdx.x & 7) * TX + r / KP;
+        if (tile >= T) return;  // padding of the last XCD's run: no part of any tile
+        tm = tile % tiles_m;
+        tn = tile / tiles_m;
+    }
     const int m0 = tm * kTM, n0 = tn * kTN;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar registers
     const int wn = wave & 1, wm = wave >> 1;
     const int l16 = lane & 15, g = lane >> 4;
     const int KB = K;  // code bytes per row
-    const int nsup = K / 128;
+    const int nsup = K / KP / 128;  // superstages of this workgroup's K part
+    const int kbase = kq * (K / KP);  // code bytes of a row before the part
 
     // code copies as in gemm_tile224_fp4: buffer loads with the operand's size as the range (the
     // host keeps rows * K below 2^31), rows 8 (copies per wave * wave + i) + lane / 8, physical chunk
@@ -2393,7 +2411,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tile224_fp8(const uint8_t* __rest
         cdst[i] = isw ? (kWCopies * wave + i) * 1024 : kWBytes + (kACopies * wave + i - kWCopies) * 1024;
     }
     auto issue_code = [&](int u, int i) {  // copy i of superstage min(u, nsup - 1) into the slot of u
-        const int koff = min(u, nsup - 1) * kRowBytes;
+        const int koff = kbase + min(u, nsup - 1) * kRowBytes;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(i < kWCopies ? wrsrc : arsrc,
                                                  (__attribute__((address_space(3))) void*)(lds + (u & 1) * kSlot + cdst[i]),
                                                  16, coff[i], koff, 0, 0);
@@ -2547,6 +2565,36 @@ __global__ __launch_bounds__(256, 1) void gemm_tile224_fp8(const uint8_t* __rest
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
 
+    if constexpr (KP > 1) {
+        // the K parts' sum: accumulator u = f kFA + j of a lane is the 4 consecutive n of one m stored below,
+        // scaled and rounded as in the epilogue that follows
+        auto mine = [&](auto uc) -> v4f {
+            constexpr int u = decltype(uc)::value;
+            return acc[u / kFA][u % kFA];
+        };
+        auto store_one = [&](int u, const v4f& v) {
+            const int f = u / kFA, j = u % kFA;
+            const int m = m0 + (kTM / 2) * wm + 16 * j + l16, n = n0 + (kTN / 2) * wn + 16 * f + 4 * g;
+            if (m >= M) return;
+            const float sxm = sa[m];
+            float o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = ptpc_scaled(v[e], sxm, sw[min(n + e, N - 1)]);
+            uint16_t* dst = y + (int64_t)m * N + n;
+            const uint32_t w2[2] = {bf16x2_rne(o[0], o[1]), bf16x2_rne(o[2], o[3])};
+            if (VEC && n + 3 < N) {
+                *reinterpret_cast<uint2*>(dst) = make_uint2(w2[0], w2[1]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (n + e < N) dst[e] = (uint16_t)(w2[e >> 1] >> (16 * (e & 1)));
+            }
+        };
+        const int ws_range = (int)sk::workspace_bytes_chunked(tiles_m * tiles_n, KP, kMf);
+        sk::tail_sum_chunked<kMf, KP, 7>(mine, ws, ws_range, tile, kq, wave, lane, store_one);
+        return;
+    }
+
     // Epilogue through LDS: acc * sA[m] * sW[n] (in FP64) rounded to BF16, each lane 4 consecutive n of one
     // m per fragment pair; then whole 448-byte tile rows.
     float sxm[kFA];
@@ -2677,13 +2725,13 @@ inline hipError_t launch_gemm(const void* qa, const void* sa, const void* qw, co
         const bool fp8_224 = FP8 && 7 * ((t224 + 255) / 256) < 8 * ((t256 + 255) / 256) &&
                              (M > N ? M : N) * K < ((int64_t)1 << 31);
         if (fp8_224 && vec16)
-            hipLaunchKernelGGL(gemm_tile224_fp8<true>, dim3((unsigned)t224), dim3(256), 0, st, a,
+            hipLaunchKernelGGL((gemm_tile224_fp8<true, 1>), dim3((unsigned)t224), dim3(256), 0, st, a,
                                reinterpret_cast<const float*>(sa), w, reinterpret_cast<const float*>(sw), out, m, n, k,
-                               tiles_m, tn224);
+                               tiles_m, tn224, nullptr);
         else if (fp8_224)
-            hipLaunchKernelGGL(gemm_tile224_fp8<false>, dim3((unsigned)t224), dim3(256), 0, st, a,
+            hipLaunchKernelGGL((gemm_tile224_fp8<false, 1>), dim3((unsigned)t224), dim3(256), 0, st, a,
                                reinterpret_cast<const float*>(sa), w, reinterpret_cast<const float*>(sw), out, m, n, k,
-                               tiles_m, tn224);
+                               tiles_m, tn224, nullptr);
         else if (FP8 && vec16)
             hipLaunchKernelGGL(gemm_tile_fp8<true>, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, st, a,
                                reinterpret_cast<const float*>(sa), w, reinterpret_cast<const float*>(sw), out, m, n, k,

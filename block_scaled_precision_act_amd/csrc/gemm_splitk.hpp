@@ -83,6 +83,10 @@ constexpr size_t kMaxWorkspaceBytes = (size_t)kMaxGrid * 4 * 2 * 4096;
 __host__ __device__ inline size_t workspace_bytes_compact(int tiles, int KP, int MF) {
     return (size_t)tiles * (KP - 1) * 4 * MF * 4096;
 }
+// tail_sum_chunked's slots: KP - 1 slots of NF / KP float4s per lane for each slice of each (tile, wave).
+__host__ __device__ inline size_t workspace_bytes_chunked(int tiles, int KP, int NF) {
+    return (size_t)tiles * 4 * (KP - 1) * NF * 1024;
+}
 }  // namespace sk
 
 // FUSED prologue: quantize rows 0 .. M-1 of BF16 X, K-values 256 s0 .. 256 (s0 + NSL) - 1, into the LDS
@@ -254,6 +258,84 @@ __device__ __forceinline__ void tail_sum(const v4f (&mine)[MF][4], uint8_t* ws, 
         v4u* const dst = reinterpret_cast<v4u*>(ws + slot(q, o < q ? o : o + 1));
 #pragma unroll
         for (int uu = 0; uu < U; ++uu) dst[64 * uu] = v4u{0u, 0u, 0u, 0u};
+    });
+}
+
+// The same protocol for a wave holding NF float4s per lane (a large output tile, its accumulators in AGPRs):
+// every part p < KP owns the slice of float4s U p .. U p + U - 1 (U = NF / KP), the slots are compact (slot
+// (p, qq) of a (tile, wave): slice p written by part qq != p; float4 uu of lane l at + 1024 uu + 16 l), and the
+// owner polls, sums in K-part order, stores and clears its slice CH float4s at a time, so only CH float4s of
+// each other part are in registers at once.  mine(ic) returns the wave's float4 ic (an integral_constant);
+// store_one(u, v) stores the sum of float4 u.  The poll budget kSpinLimit is shared by the chunks: once it is
+// spent, every chunk not yet complete is stored as NaN after one more poll.
+template <int NF, int KP, int CH, typename Mine, typename Store>
+__device__ __forceinline__ void tail_sum_chunked(Mine&& mine, uint8_t* ws, int ws_range, int t, int q, int wave,
+                                                  int lane, Store&& store_one) {
+    constexpr int U = NF / KP;
+    static_assert(U * KP == NF && U % CH == 0, "slices of whole chunks");
+    auto slot = [&](int p, int qq) -> uint32_t {
+        return (uint32_t)(((((size_t)t * 4 + wave) * KP + p) * (KP - 1) + (qq < p ? qq : qq - 1)) * (1024 * U) +
+                          16 * lane);
+    };
+    static_for<KP>([&](auto pc) {
+        constexpr int p = decltype(pc)::value;
+        if (p == q) return;
+        v4u* const dst = reinterpret_cast<v4u*>(ws + slot(p, q));
+        static_for<U>([&](auto uc) {
+            constexpr int uu = decltype(uc)::value;
+            dst[64 * uu] = partial_words(mine(std::integral_constant<int, U * p + uu>{}));
+        });
+    });
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(ws, (short)0, ws_range, kBufferWord3);
+    int spins = 0;
+    static_for<KP>([&](auto pc) {
+        constexpr int p = decltype(pc)::value;  // this part's slice: p == q
+        if (p != q) return;
+        static_for<U / CH>([&](auto cc) {
+            constexpr int c0 = decltype(cc)::value * CH;  // first float4 of the chunk within the slice
+            v4u pv[KP - 1][CH];
+            bool complete = false;
+            do {
+                uint32_t present = 1;
+                static_for<KP - 1>([&](auto oc) {
+                    constexpr int o = decltype(oc)::value;  // slot o holds part o < p ? o : o + 1
+                    uint32_t off = slot(p, o < p ? o : o + 1);
+                    asm volatile("" : "+v"(off));  // an opaque address: the loads are repeated each poll
+#pragma unroll
+                    for (int k = 0; k < CH; ++k) {
+                        // cache policy sc1: coherent at device scope, so every poll reads L2 again
+                        pv[o][k] = __builtin_bit_cast(
+                            v4u, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 1024 * (c0 + k), 0, 16));
+                        present &= (pv[o][k][0] != 0u) & (pv[o][k][1] != 0u) & (pv[o][k][2] != 0u) &
+                                   (pv[o][k][3] != 0u);
+                    }
+                });
+                complete = __all(present);
+                if (!complete) __builtin_amdgcn_s_sleep(1);
+            } while (!complete && ++spins < kSpinLimit);
+            static_for<CH>([&](auto kc) {
+                constexpr int k = decltype(kc)::value, u = U * p + c0 + k;
+                v4f sum;
+                static_for<KP>([&](auto sc) {
+                    constexpr int s = decltype(sc)::value;
+                    v4f v;
+                    if constexpr (s == p)  // NaNs made canonical, as the others'
+                        v = partial_values(partial_words(mine(std::integral_constant<int, u>{})));
+                    else
+                        v = partial_values(pv[s < p ? s : s - 1][k]);
+                    if constexpr (s == 0) sum = v;
+                    else sum += v;
+                });
+                const float nan = __uint_as_float(0x7FC00000u);
+                store_one(u, complete ? sum : v4f{nan, nan, nan, nan});  // a timed-out wait shows as NaN
+            });
+            static_for<KP - 1>([&](auto oc) {
+                constexpr int o = decltype(oc)::value;
+                v4u* const dst = reinterpret_cast<v4u*>(ws + slot(p, o < p ? o : o + 1));
+#pragma unroll
+                for (int k = 0; k < CH; ++k) dst[64 * (c0 + k)] = v4u{0u, 0u, 0u, 0u};
+            });
+        });
     });
 }
 }  // namespace sk

@@ -235,9 +235,13 @@ mx_status ptpc_quant_weight_f32(const float *w, int64_t N, int64_t K,
 
 /*
  * Bytes of workspace gemm_a8w8_ptpc_bf16 needs for this shape: nonzero for the
- * decode sizes that split K across workgroups - 33 <= M <= 64, K split into 4
- * or 8 parts of 2048, 128-column tiles x parts between 128 and 256
- * workgroups; e.g. 7,340,032 bytes for (64, 7168, 8192) - and 0 otherwise.
+ * sizes that split K across workgroups - 33 <= M <= 64, K split into 4 or 8
+ * parts of 2048, 128-column tiles x parts between 128 and 256 workgroups
+ * (e.g. 7,340,032 bytes for (64, 7168, 8192)); M > 128 with at most 128
+ * output tiles of 256 x 224, K split into the largest of 8, 4 or 2 parts of
+ * at least 1024 whose grid stays within 256 workgroups, tiles x (parts - 1) x
+ * 224 KB (e.g. 44,040,192 bytes for (512, 7168, 8192), 51,380,224 at most) -
+ * and 0 otherwise.
  * Same rules as mx_gemm_a4w4_workspace_bytes: it depends on the shape only,
  * must be zero-filled before first use, is left all zero by every call, and
  * calls that share a workspace must not run concurrently.
@@ -254,7 +258,7 @@ size_t gemm_a8w8_ptpc_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *   sa, sw 4-byte aligned; y_bf16 2-byte aligned.
  *   workspace: at least gemm_a8w8_ptpc_workspace_bytes(M, N, K) bytes,
  *   16-byte aligned, zero-filled before first use; may be NULL when that size
- *   is 0, else MX_ERROR_WORKSPACE.  At those decode sizes the K parts of each
+ *   is 0, else MX_ERROR_WORKSPACE.  At those sizes the K parts of each
  *   output are summed across workgroups in a fixed order (deterministic), as
  *   in mx_gemm_a4w4_bf16, when the grid fits the device's CUs at once.
  */

@@ -144,6 +144,7 @@ A8W8_FAMILIES = [
     ("decode, register-staged", 24, 256, 384),
     ("split-K decode, 64 rows", 48, 4096, 8192),
     ("256 x 224 tile", 300, 256, 1024),
+    ("256 x 224 tile, K parts", 300, 256, 2048),
     ("256 x 256 tile", 4096, 4096, 512),
 ]
 

@@ -146,6 +146,13 @@ SPLIT8_SHAPES = [
     (40, 4096, 16384),   # 8 parts, 256 workgroups
     (50, 2900, 16384),   # 8 parts, 23 tiles: idle workgroups
 ]
+# M > 128 with at most 128 tiles of 256 x 224: the FP8 tile kernel with K in 8, 4 or 2 parts of >= 1024
+TILE8_SHAPES = [
+    (256, 7168, 8192),   # 32 tiles, 8 parts, 256 workgroups
+    (512, 2048, 8192),   # 20 tiles, 8 parts: idle workgroups in the last XCD's runs
+    (129, 1001, 4096),   # one row in the tile, N % 8 != 0 (element stores), 4 parts
+    (300, 1000, 2048),   # ragged M and N, 2 parts
+]
 
 
 def _operands8(orc, seed, M, N, K):
@@ -165,7 +172,7 @@ def _gemm8(mx, torch, qa, sa, qw, sw, ws):
     return y
 
 
-@pytest.mark.parametrize("M,N,K", SPLIT8_SHAPES)
+@pytest.mark.parametrize("M,N,K", SPLIT8_SHAPES + TILE8_SHAPES)
 def test_splitk_fp8_matches_oracle(mx, orc, M, N, K):
     import torch
     wsb = mx.gemm_a8w8_ptpc_workspace_bytes(M, N, K)
