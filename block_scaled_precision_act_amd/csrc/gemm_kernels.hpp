@@ -1489,6 +1489,8 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_fp4(const uint8_t* __restric
     wait_vmcnt<0>();
     lds_wait_n_of<0, FW>(r0w, r0x);
     lds_wait_n_of<0, FW>(r1w, r1x);
+    lds_tie(wsc);  // the last superstage's (unused) scale reads have landed before their registers are reused
+    lds_tie(xsc);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
 
@@ -1759,6 +1761,8 @@ __global__ __launch_bounds__(512, 1) void gemm_tile128_pc_fp4(const uint8_t* __r
 #undef MX_STEP_RD
         lds_wait_n_of<0, FW>(r0w, r0x);
         lds_wait_n_of<0, FW>(r1w, r1x);
+        lds_tie(wsc);  // the last superstage's (unused) scale reads have landed before their registers are reused
+        lds_tie(xsc);
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (KP > 1) {
