@@ -11,15 +11,21 @@
 // is as fast or faster (M = 1 11.4 vs 13.0, M = 32 13.4 vs 13.1 us), so it
 // keeps those.
 //
-// M > 128 where the 256 x 224 tiles number at most 128: each tile takes one
-// workgroup about 133 us at K = 8192 (the FP16 MFMAs bound it), so a few tiles
-// would leave most CUs idle.  K is split into KP = 8, 4 or 2 parts (the largest
-// whose grid, 8 KP ceil(tiles / 8) workgroups, fits the CUs, with parts of at
-// least 1024), summed in the caller's workspace (gemm_tile224_fp8<VEC, KP>).
-// Measured (graph-replayed, rotated weights, N = 7168, K = 8192), split vs one
-// workgroup per tile: M = 136 / 256 48.8 / 51.6 us (KP = 8) vs 133; M = 512
-// 70.4 us (KP = 4; 86.0 with 2) vs 134; M = 768 / 1024 93.0 / 103.8 us (KP = 2)
-// vs 135.  Everything else runs the kernels of gemm_kernels.hpp.
+// M > 128 with at most 256 output tiles of 128 x 128 (M <= 512 at N = 7168):
+// gemm_tile128_pc_fp8 (copy waves beside the MFMA waves), one tile per
+// workgroup, and with at most 128 tiles K in two parts over 2 x tiles
+// workgroups summed in the caller's workspace (64 KB per tile).  Otherwise, where
+// the 256 x 224 tiles number at most 128 (M <= 1024 at N = 7168), K is split
+// into KP = 8, 4 or 2 parts of them (the largest whose grid, 8 KP ceil(tiles /
+// 8) workgroups, fits the CUs, with parts of at least 1024), summed in the
+// caller's workspace (gemm_tile224_fp8<VEC, KP>): one workgroup takes about
+// 133 us per tile at K = 8192 (the FP16 MFMAs bound it), so few tiles left most
+// CUs idle.  Measured (graph-replayed, rotated weights, N = 7168, K = 8192):
+// one 256 x 224 workgroup per tile took 133-135 us at every M from 129 to 1024;
+// its K parts M = 136 / 256 48.8 / 51.6 us (KP = 8), M = 512 70.4 us (KP = 4),
+// M = 768 / 1024 93.0 / 103.8 us (KP = 2); the 128 x 128 tile M = 136 / 200 /
+// 256 35.4 / 35.1 / 35.5 us (two parts), M = 384 / 512 55.8 / 60.8-65.2 us.
+// Everything else runs the kernels of gemm_kernels.hpp.
 #include "gemm_kernels.hpp"
 #include "gemm_splitk.hpp"
 #include "launch.hpp"
@@ -47,6 +53,42 @@ Split8 split8_plan(int64_t M, int64_t N, int64_t K) {
     p.kp = (int)kp;
     p.tiles = tiles;
     return p;
+}
+
+// M > 128 on 128 x 128 tiles, two K parts when kp == 2 (see the file comment); kp == 0 if none
+struct Pc8 {
+    int kp = 0, tiles_m = 0, tiles_n = 0;
+    int tiles() const { return tiles_m * tiles_n; }
+    int grid() const { return kp == 1 ? tiles() : 8 * kp * ((tiles() + 7) / 8); }
+    bool fits_device() const { return kp == 2 && grid() <= device_cus(); }
+};
+
+Pc8 pc8_plan(int64_t M, int64_t N, int64_t K) {
+    Pc8 p;
+    if (M <= 128 || N < 1) return p;
+    const int64_t tm = (M + 127) / 128, tn = (N + 127) / 128;
+    if (tm * tn > 256) return p;
+    p.kp = tm * tn <= 128 && K % 256 == 0 && K / 2 >= 1024 ? 2 : 1;
+    p.tiles_m = (int)tm;
+    p.tiles_n = (int)tn;
+    return p;
+}
+
+template <int KP>
+hipError_t launch_pc8(const Pc8& p, const void* qa, const float* sa, const void* qw, const float* sw, void* y,
+                      int64_t M, int64_t N, int64_t K, void* ws, hipStream_t st) {
+    const uint8_t* a = reinterpret_cast<const uint8_t*>(qa);
+    const uint8_t* w = reinterpret_cast<const uint8_t*>(qw);
+    uint16_t* out = reinterpret_cast<uint16_t*>(y);
+    uint8_t* w8 = reinterpret_cast<uint8_t*>(ws);
+    const dim3 grid((unsigned)(KP == 1 ? p.tiles() : p.grid())), block(512);
+    if (N % 8 == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0)
+        hipLaunchKernelGGL((gemm_tile128_pc_fp8<true, KP>), grid, block, 0, st, a, sa, w, sw, out, (int)M, (int)N,
+                           (int)K, p.tiles_m, p.tiles_n, w8);
+    else
+        hipLaunchKernelGGL((gemm_tile128_pc_fp8<false, KP>), grid, block, 0, st, a, sa, w, sw, out, (int)M, (int)N,
+                           (int)K, p.tiles_m, p.tiles_n, w8);
+    return hipGetLastError();
 }
 
 // M > 128 on 256 x 224 tiles with K in parts (see the file comment); kp == 0 if none
@@ -94,6 +136,8 @@ hipError_t launch_tile8(const Tile8& p, const void* qa, const float* sa, const v
 size_t gemm_a8w8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     const Split8 p = split8_plan(M, N, K);
     if (p.kp) return sk::workspace_bytes(p.tiles, p.kp, 2);
+    const Pc8 c = pc8_plan(M, N, K);
+    if (c.kp) return c.kp == 2 ? sk::workspace_bytes_compact(c.tiles(), 2, 4) : 0;
     const Tile8 t = tile8_plan(M, N, K);
     return t.kp ? sk::workspace_bytes_chunked(t.tiles(), t.kp, tile224_fp8::kMf) : 0;
 }
@@ -115,6 +159,11 @@ hipError_t launch_gemm_a8w8(const void* qa, const float* sa, const void* qw, con
             hipLaunchKernelGGL((gemm_splitk_fp8<2, 3, kNsl8, 8>), grid, block, 0, st, a, sa, w, sw, out, (int)M, (int)N,
                                (int)K, p.tiles, ws);
         return hipGetLastError();
+    }
+    const Pc8 c = pc8_plan(M, N, K);
+    if (c.kp) {
+        if (workspace && c.fits_device()) return launch_pc8<2>(c, qa, sa, qw, sw, y, M, N, K, workspace, st);
+        return launch_pc8<1>(c, qa, sa, qw, sw, y, M, N, K, nullptr, st);
     }
     const Tile8 t = tile8_plan(M, N, K);
     if (workspace && t.fits_device()) {

@@ -2324,6 +2324,260 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_fp8(const uint8_t* __restric
 }
 
 // ============================================================================
+// Tile path, FP8 (E4M3 widened exactly to FP16), 128 x 128 tiles when they fit one round: the copy-wave /
+// MFMA-wave split of gemm_tile128_pc_fp4 on E4M3 codes.  A superstage is K = 128 (128 code bytes per row, as
+// the FP4 kernels' K = 256) of the 128 weight and 128 activation rows, in a 4-slot ring of 32 KB slots; no
+// scales travel (the per-row FP32 scales are applied at the end, (acc * sA) * sW, before the BF16
+// rounding).  Waves 4..7 copy (8 copies of 8 rows each per superstage and wave); waves 0..3 each own 2 x 2
+// fragments of 32 x 32 and read the row's chunk 4h + j for read group j, which widens into two 8 x FP16
+// operands (two k-steps of v_mfma_f32_32x32x16_f16; the other half of each chunk is widened between the
+// first half's MFMAs).  KP > 1 splits K into KP parts of K / KP (a multiple of 128) over KP workgroups per
+// tile, the accumulators summed by sk::tail_sum (compact slots, sk::workspace_bytes_compact(tiles, KP, 4)
+// bytes of zero-filled workspace) before the scales; the workgroup-to-tile mapping is gemm_tile128_pc_fp4's.
+// ============================================================================
+namespace tile128_fp8 {
+constexpr int kRows = 128;
+constexpr int kRowBytes = 128;                 // code bytes (K values) per row per superstage
+constexpr int kOpBytes = kRows * kRowBytes;    // 16 KB
+constexpr int kSlot = 2 * kOpBytes;            // W rows, then A rows
+constexpr int kS = 4;                          // ring slots
+constexpr int kCopies = 2 * kRows / 32;        // code copies per producer wave and superstage (W, then A)
+constexpr int kOutPitch = 2 * kRows + 16;      // epilogue staging pitch (bytes)
+constexpr int kLds = kS * kSlot > kRows * kOutPitch ? kS * kSlot : kRows * kOutPitch;
+static_assert(kLds <= 160 * 1024, "LDS");
+}  // namespace tile128_fp8
+
+template <bool VEC, int KP = 1>
+__global__ __launch_bounds__(512, 1) void gemm_tile128_pc_fp8(const uint8_t* __restrict__ qa,
+                                                              const float* __restrict__ sa,
+                                                              const uint8_t* __restrict__ qw,
+                                                              const float* __restrict__ sw, uint16_t* __restrict__ y,
+                                                              int M, int N, int K, int tiles_m, int tiles_n,
+                                                              uint8_t* __restrict__ ws) {
+    using namespace tile128_fp8;
+    constexpr int TM = kRows, FW = 2;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
+
+    int tm, tn, kq = 0, tile = 0;  // kq: this workgroup's K part
+    if constexpr (KP == 1) {
+        tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    } else {
+        const int T = tiles_m * tiles_n, TX = (T + 7) >> 3, r = (int)blockIdx.x >> 3;
+        kq = r % KP;
+        tile = ((int)blockIdx.x & 7) * TX + r / KP;
+        if (tile >= T) return;  // padding of the last XCD's run: no part of any tile
+        tm = tile % tiles_m;
+        tn = tile / tiles_m;
+    }
+    const int m0 = tm * TM, n0 = tn * TM;
+    const int lane = threadIdx.x & 63;
+    const int wave8 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform role
+    const int wave = wave8 & 3;
+    const int64_t KB = (int64_t)K;
+    const int nsup = K / KP / 128;               // superstages of this workgroup's K part
+    const int64_t kbase = kq * (KB / KP);        // code bytes of a row before the part
+
+    if (wave8 >= 4) {
+        // Producer: copy i moves W rows (i < 4) or A rows 8 (4 wave + i % 4) + lane / 8, the lane filling
+        // physical chunk lane % 8 with logical chunk (lane % 8) ^ ((row / 2) % 8).
+        const uint8_t* src[kCopies];
+#pragma unroll
+        for (int i = 0; i < kCopies; ++i) {
+            const int row = 8 * (4 * wave + (i & 3)) + (lane >> 3);
+            const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+            src[i] = i < 4 ? qw + (int64_t)min(n0 + row, N - 1) * KB + 16 * chunk
+                           : qa + (int64_t)min(m0 + row, M - 1) * KB + 16 * chunk;
+        }
+        auto batch = [&](int u) {  // the copies of superstage min(u, nsup - 1) into the slot of u
+            uint8_t* slot = lds + (u % kS) * kSlot;
+            const int64_t koff = kbase + (int64_t)min(u, nsup - 1) * kRowBytes;
+#pragma unroll
+            for (int i = 0; i < kCopies; ++i)
+                g2lds16(src[i] + koff, slot + (i < 4 ? 0 : kOpBytes) + (4 * wave + (i & 3)) * 1024);
+        };
+#pragma unroll
+        for (int v = 0; v < kS; ++v) batch(v);
+        wait_vmcnt<(kS - 1) * kCopies>();  // superstage 0 is in
+        __builtin_amdgcn_s_barrier();
+        for (int u = 0; u < nsup - kS; ++u) {
+            wait_vmcnt<(kS - 2) * kCopies>();  // this wave's copies of u + 1 have landed
+            __builtin_amdgcn_s_barrier();
+            batch(u + kS);
+        }
+        static_for<kS>([&](auto t) {
+            constexpr int T = decltype(t)::value;
+            if (nsup - kS + T >= 0) {
+                wait_vmcnt<(kS - 2 - T > 0 ? kS - 2 - T : 0) * kCopies>();
+                __builtin_amdgcn_s_barrier();
+            }
+        });
+        wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();  // the consumers' barrier before the epilogue: no copy lands after it
+    } else {
+        // Consumer: 2 x 2 fragments of 32 x 32 (f: weight rows 64 wn + 32 f, g: activation rows 64 wm + 32 g).
+        const int wn = wave & 1, wm = wave >> 1;
+        const int l32 = lane & 31, h = lane >> 5;
+        int woff[FW], xoff[FW];
+#pragma unroll
+        for (int f = 0; f < FW; ++f) {
+            const int wr = 64 * wn + 32 * f + l32, xr = 64 * wm + 32 * f + l32;
+            woff[f] = wr * kRowBytes + ((wr >> 1) & 7);  // low bits: the swizzle key, split off below
+            xoff[f] = kOpBytes + xr * kRowBytes + ((xr >> 1) & 7);
+        }
+        const uint32_t base = lds_addr(lds);
+        // read i (0 .. 2 FW - 1) of group j of superstage u: fragment i / 2 of W (even i) or of A (odd i)
+        auto rd_one = [&](v4u (&rw)[FW], v4u (&rx)[FW], int u, int j, int i) {
+            const uint32_t sb = base + (u % kS) * kSlot;
+            const int f = i >> 1;
+            if (i & 1) rx[f] = lds_read16(sb + (xoff[f] & ~7) + 16 * ((4 * h + j) ^ (xoff[f] & 7)));
+            else rw[f] = lds_read16(sb + (woff[f] & ~7) + 16 * ((4 * h + j) ^ (woff[f] & 7)));
+        };
+        v16f acc[FW][FW];
+#pragma unroll
+        for (int f = 0; f < FW; ++f)
+#pragma unroll
+            for (int g = 0; g < FW; ++g)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[f][g][r] = 0.f;
+        // read group (RW, RX): half 0 widened, its FW^2 MFMAs with half 1's widening between them, then half
+        // 1's MFMAs; the 2 FW reads of the next group (NW, NX of superstage NU, group NJ) spread over the 2 FW^2
+        // MFMAs, one after every FW of them
+        auto group = [&](const v4u (&RW)[FW], const v4u (&RX)[FW], v4u (&NW)[FW], v4u (&NX)[FW], int nu, int nj) {
+            v8h wa0[FW], xv0[FW], wa1[FW], xv1[FW];
+#pragma unroll
+            for (int f = 0; f < FW; ++f) {
+                wa0[f] = e4m3x8_to_f16x8(RW[f][0], RW[f][1]);
+                xv0[f] = e4m3x8_to_f16x8(RX[f][0], RX[f][1]);
+            }
+#pragma unroll
+            for (int f = 0; f < FW; ++f)
+#pragma unroll
+                for (int g = 0; g < FW; ++g) {
+                    const int i = f * FW + g;
+                    acc[f][g] = mfma32_f16(wa0[f], xv0[g], acc[f][g]);
+                    if (i < FW) wa1[i] = e4m3x8_to_f16x8(RW[i][2], RW[i][3]);  // FW^2 == 2 FW operands
+                    else xv1[i - FW] = e4m3x8_to_f16x8(RX[i - FW][2], RX[i - FW][3]);
+                    if ((i % FW) == FW - 1) rd_one(NW, NX, nu, nj, i / FW);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+#pragma unroll
+            for (int f = 0; f < FW; ++f)
+#pragma unroll
+                for (int g = 0; g < FW; ++g) {
+                    const int i = f * FW + g;
+                    acc[f][g] = mfma32_f16(wa1[f], xv1[g], acc[f][g]);
+                    if ((i % FW) == FW - 1) rd_one(NW, NX, nu, nj, FW + i / FW);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+        };
+        __builtin_amdgcn_s_barrier();  // superstage 0 is in
+        __builtin_amdgcn_sched_barrier(0);
+        v4u g0w[FW], g0x[FW], g1w[FW], g1x[FW], g2w[FW], g2x[FW], g3w[FW], g3x[FW];
+#pragma unroll
+        for (int i = 0; i < 2 * FW; ++i) rd_one(g0w, g0x, 0, 0, i);
+#pragma unroll
+        for (int i = 0; i < 2 * FW; ++i) rd_one(g1w, g1x, 0, 1, i);
+        // superstage u: groups 0 and 1 (reading groups 2 and 3 meanwhile), the barrier, then groups 2 and 3
+        // (reading groups 0 and 1 of u + 1; past the end these read stale slot data, never used)
+        for (int u = 0; u < nsup; ++u) {
+            lds_wait_n_of<2 * FW, FW>(g0w, g0x);
+            __builtin_amdgcn_sched_barrier(0);
+            group(g0w, g0x, g2w, g2x, u, 2);
+            lds_wait_n_of<2 * FW, FW>(g1w, g1x);
+            __builtin_amdgcn_sched_barrier(0);
+            group(g1w, g1x, g3w, g3x, u, 3);
+            lds_wait_n_of<0, FW>(g2w, g2x);
+            lds_wait_n_of<0, FW>(g3w, g3x);
+            __builtin_amdgcn_s_barrier();  // every consumer done reading u; every copy of u + 1 landed
+            __builtin_amdgcn_sched_barrier(0);
+            group(g2w, g2x, g0w, g0x, u + 1, 0);
+            group(g3w, g3x, g1w, g1x, u + 1, 1);
+        }
+        lds_wait_n_of<0, FW>(g0w, g0x);
+        lds_wait_n_of<0, FW>(g1w, g1x);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (KP > 1) {
+            // the K parts' sum: fragment (f, g) is tail fragment FW f + g, its registers 4 j .. 4 j + 3 the 4
+            // consecutive n of one m; scaled and rounded as in the one-part epilogue
+            v4f mine[FW * FW][4];
+#pragma unroll
+            for (int f = 0; f < FW; ++f)
+#pragma unroll
+                for (int g = 0; g < FW; ++g)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        mine[FW * f + g][j] = v4f{acc[f][g][4 * j], acc[f][g][4 * j + 1], acc[f][g][4 * j + 2],
+                                                  acc[f][g][4 * j + 3]};
+            auto store_one = [&](int fr, int j, const v4f& v) {
+                const int f = fr / FW, g = fr % FW;
+                const int m = m0 + 64 * wm + 32 * g + l32, n = n0 + 64 * wn + 32 * f + 8 * j + 4 * h;
+                if (m >= M) return;
+                const float sxm = sa[m];
+                float o[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = ptpc_scaled(v[e], sxm, sw[min(n + e, N - 1)]);
+                uint16_t* dst = y + (int64_t)m * N + n;
+                const uint32_t w2[2] = {bf16x2_rne(o[0], o[1]), bf16x2_rne(o[2], o[3])};
+                if (VEC && n + 3 < N) {
+                    *reinterpret_cast<uint2*>(dst) = make_uint2(w2[0], w2[1]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < N) dst[e] = (uint16_t)(w2[e >> 1] >> (16 * (e & 1)));
+                }
+            };
+            sk::tail_sum<FW * FW, KP>(mine, ws, (int)sk::workspace_bytes_compact(tiles_m * tiles_n, KP, FW * FW), tile,
+                                      kq, wave, lane, store_one, std::true_type{});
+        } else {
+            // scaled BF16 sub-tile into LDS (padded pitch) for whole-row stores below
+#pragma unroll
+            for (int g = 0; g < FW; ++g) {
+                const int ml = 64 * wm + 32 * g + l32;
+                const float sxm = sa[min(m0 + ml, M - 1)];
+#pragma unroll
+                for (int f = 0; f < FW; ++f)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int nl = 64 * wn + 32 * f + 8 * j + 4 * h;
+                        float v[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            v[e] = ptpc_scaled(acc[f][g][4 * j + e], sxm, sw[min(n0 + nl + e, N - 1)]);
+                        uint2 pk;
+                        pk.x = bf16x2_rne(v[0], v[1]);
+                        pk.y = bf16x2_rne(v[2], v[3]);
+                        *reinterpret_cast<uint2*>(lds + ml * kOutPitch + 2 * nl) = pk;
+                    }
+            }
+        }
+    }
+    if constexpr (KP > 1) return;
+    __syncthreads();
+    // all 8 waves store whole tile rows (2 TM bytes each): wave w rows 16 w .. 16 w + 15
+    constexpr int kLanesPerRow = TM / 8;  // 16-byte pieces per tile row
+    constexpr int kRowsPerStore = 64 / kLanesPerRow;
+    const int lr = lane / kLanesPerRow, lc = lane % kLanesPerRow;
+#pragma unroll
+    for (int r = 0; r < TM / 8 / kRowsPerStore; ++r) {
+        const int ml = (TM / 8) * wave8 + kRowsPerStore * r + lr;
+        const int m = m0 + ml;
+        const int n = n0 + 8 * lc;
+        const uint4 v = *reinterpret_cast<const uint4*>(lds + ml * kOutPitch + 16 * lc);
+        if (m >= M) continue;
+        uint16_t* dst = y + (int64_t)m * N + n;
+        if (VEC && n + 7 < N) {
+            *reinterpret_cast<uint4*>(dst) = v;
+        } else {
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (n + e < N) dst[e] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+        }
+    }
+}
+
+// ============================================================================
 // Tile path, FP8 (E4M3 widened exactly to FP16), K % 128 == 0: 256 x 224
 // output tiles from 16 x 16 x 32 FP16 MFMAs, four full rounds at N = 7168
 // and M = 8192 (as gemm_tile224_fp4).  Same staging: a superstage is K = 128

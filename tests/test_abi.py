@@ -135,13 +135,16 @@ def test_gemm_argument_errors(mx):
     assert w8(64, 7168, 4096) == 0      # 2 parts
     assert w8(64, 7168, 16384) == 0     # 448 workgroups
     assert w8(65, 7168, 8192) == 0
-    # M > 128, at most 128 tiles of 256 x 224: K in 8, 4 or 2 parts of >= 1024, tiles x 4 waves x (parts - 1) x 56 KB
-    assert w8(512, 7168, 8192) == 64 * 4 * 3 * 56 * 1024 == 44040192      # 4 parts
-    assert w8(256, 7168, 8192) == 32 * 4 * 7 * 56 * 1024 == 51380224      # 8 parts: the largest
-    assert w8(1024, 7168, 8192) == 128 * 4 * 1 * 56 * 1024                # 2 parts
-    assert w8(129, 1001, 4096) == 5 * 4 * 3 * 56 * 1024                   # parts of 1024: 4
-    assert w8(300, 1000, 2048) == 10 * 4 * 1 * 56 * 1024                  # 2 parts
+    # M > 128, at most 128 tiles of 128 x 128 (and K / 2 >= 1024): two K parts, tiles x 64 KB; at most 256 tiles:
+    # full K, no workspace
+    assert w8(256, 7168, 8192) == 112 * 64 * 1024 == 7340032
+    assert w8(129, 1001, 4096) == 16 * 64 * 1024
+    assert w8(300, 1000, 2048) == 24 * 64 * 1024
     assert w8(300, 1000, 1024) == 0                                        # parts would be under 1024
+    assert w8(512, 7168, 8192) == 0                                        # 224 tiles: full K
+    # past 256 tiles of 128, at most 128 tiles of 256 x 224: K in parts of them, tiles x 4 waves x (parts - 1) x 56 KB
+    assert w8(1024, 7168, 8192) == 128 * 4 * 1 * 56 * 1024                # 2 parts
+    assert w8(1100, 4096, 4096) == 95 * 4 * 1 * 56 * 1024
     assert w8(1025, 7168, 8192) == 0                                       # 160 tiles: one workgroup each
     assert g8(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 7168, 8192, None, 0) == mx.MX_ERROR_WORKSPACE
     assert g8(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 7168, 8192, FAKE, 1024) == mx.MX_ERROR_WORKSPACE

@@ -58,8 +58,10 @@ def test_a4w4_layer_graph_replay(mx, M, N, K):
     _replays_match(mx, torch, layer, [qa, sa, y])
 
 
-# the decode ring (64 x 512 x 1024), the split-K kernel (64 x 4096 x 8192) and the 256 x 224 FP8 tile (300)
-@pytest.mark.parametrize("M,N,K", [(64, 512, 1024), (64, 4096, 8192), (300, 512, 1024)])
+# the decode ring (64 x 512 x 1024), the split-K kernel (64 x 4096 x 8192), the 128-row FP8 tile with copy and
+# MFMA waves (300 x 512 x 1024), in two K parts (256 x 2048 x 8192), and the 256 x 224 FP8 tile (2200 x 3900 x 512)
+@pytest.mark.parametrize("M,N,K", [(64, 512, 1024), (64, 4096, 8192), (300, 512, 1024), (256, 2048, 8192),
+                                   (2200, 3900, 512)])
 def test_a8w8_layer_graph_replay(mx, M, N, K):
     import torch
     x = bf16_dev(synth.act_normal(63, M, K))

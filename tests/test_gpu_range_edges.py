@@ -143,8 +143,10 @@ A8W8_FAMILIES = [
     ("decode ring, two row halves", 100, 256, 1024),
     ("decode, register-staged", 24, 256, 384),
     ("split-K decode, 64 rows", 48, 4096, 8192),
-    ("256 x 224 tile", 300, 256, 1024),
-    ("256 x 224 tile, K parts", 300, 256, 2048),
+    ("128-row tile, copy and MFMA waves", 300, 256, 1024),
+    ("128-row tile, two K parts", 300, 256, 2048),
+    ("256 x 224 tile", 2200, 3900, 512),
+    ("256 x 224 tile, K parts", 1100, 4096, 2048),
     ("256 x 256 tile", 4096, 4096, 512),
 ]
 

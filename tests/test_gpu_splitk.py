@@ -146,12 +146,15 @@ SPLIT8_SHAPES = [
     (40, 4096, 16384),   # 8 parts, 256 workgroups
     (50, 2900, 16384),   # 8 parts, 23 tiles: idle workgroups
 ]
-# M > 128 with at most 128 tiles of 256 x 224: the FP8 tile kernel with K in 8, 4 or 2 parts of >= 1024
+# M > 128: the FP8 128 x 128 tile with copy and MFMA waves in two K parts (at most 128 tiles), and past 256
+# such tiles the 256 x 224 tile with K in parts of >= 1024 (at most 128 of those tiles)
 TILE8_SHAPES = [
-    (256, 7168, 8192),   # 32 tiles, 8 parts, 256 workgroups
-    (512, 2048, 8192),   # 20 tiles, 8 parts: idle workgroups in the last XCD's runs
-    (129, 1001, 4096),   # one row in the tile, N % 8 != 0 (element stores), 4 parts
-    (300, 1000, 2048),   # ragged M and N, 2 parts
+    (256, 7168, 8192),   # 128 tile: 112 tiles, 224 workgroups
+    (512, 2048, 8192),   # 128 tile: 64 tiles
+    (129, 1001, 4096),   # 128 tile: one row in the second tile row, N % 8 != 0 (element stores)
+    (300, 1000, 2048),   # 128 tile: ragged M and N
+    (1100, 4096, 4096),  # 256 x 224 tile: 95 tiles, 2 parts (idle workgroups in the last XCD's runs)
+    (600, 9000, 2048),   # 256 x 224 tile: 123 tiles, 2 parts of 1024, 256 workgroups
 ]
 
 
