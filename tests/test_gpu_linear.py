@@ -49,6 +49,7 @@ def _weight(orc, seed, N, K):
     (33, 8100, 4096),   # quantizer + decode ring (2 parts: no GEMM split)
     (100, 3000, 2048),  # quantizer + GEMM (M > 64)
     (24, 5000, 640),    # quantizer + GEMM (K % 1024 != 0)
+    (200, 2048, 4096),  # quantizer + 128-row tile GEMM in two K parts (its partials below the codes)
 ])
 def test_linear_matches_oracle(mx, orc, M, N, K):
     import torch
@@ -97,7 +98,7 @@ def test_linear_repeatable_and_shares_workspace(mx, orc):
     """Repeated one-call layers give identical bits; one zero-filled workspace serves layer and GEMM calls
     of different shapes in turn (each leaves the partial area, the first 8 MiB, all zero)."""
     import torch
-    shapes = [(64, 7168, 8192), (5, 4000, 4096), (100, 3000, 2048), (2, 7168, 8192)]
+    shapes = [(64, 7168, 8192), (5, 4000, 4096), (100, 3000, 2048), (256, 2048, 8192), (2, 7168, 8192)]
     size = max(max(mx.mx_linear_a4w4_workspace_bytes(*s), mx.mx_gemm_a4w4_workspace_bytes(*s)) for s in shapes)
     size = max(size, mx.mx_gemm_a4w4_workspace_bytes(64, 4096, 8192))
     ws = torch.zeros(size, dtype=torch.uint8, device="cuda")
