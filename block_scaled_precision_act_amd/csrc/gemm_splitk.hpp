@@ -3,7 +3,9 @@
 //   gemm_splitk_fp4_rh  A4W4, 64 < M <= 128, in two 64-row halves
 //   gemm_splitk_fp8     PTPC A8W8, 33 <= M <= 64
 // all sharing one tail (sk::tail_sum), and gemm_grouped_fp4 (MoE experts, K % 1024 == 0), the first's
-// tile body walking K in parts within the workgroup.  The design, described for the first:
+// tile body walking K in parts within the workgroup.  The tail also sums the K parts of the tile kernels
+// of gemm_kernels.hpp that split K (the 128-row tiles with copy and MFMA waves, in compact slots; the FP8
+// 256 x 224 tile through sk::tail_sum_chunked).  The design, described for the first:
 //
 // The layer ("Kimi-K3 DSpark O-Proj-only MXFP4", section "Exact quantization
 // coverage": weight (7168, 8192) MXFP4 with (7168, 256) E8M0 scales, dynamic
@@ -73,7 +75,9 @@ struct Cfg {
 };
 
 // Workspace: the partial slots of every column group (tile, wave), KP x MF x 4 KB per group.  A launch has
-// at most kMaxGrid workgroups (all resident at once, one per CU), so at most 8 MiB.
+// at most kMaxGrid workgroups (all resident at once, one per CU), so at most 8 MiB; every A4W4 plan (the
+// compact slots of the two-part 128-row tile included) stays within it.  The FP8 256 x 224 tile's chunked
+// slots (workspace_bytes_chunked) can take up to about 51 MB of the A8W8 caller's workspace.
 constexpr int kMaxGrid = 256;
 __host__ __device__ inline size_t workspace_bytes(int tiles, int KP, int MF) {
     return (size_t)tiles * KP * 4 * MF * 4096;
