@@ -320,10 +320,10 @@ def make_a4w4(ctx, cfg_name, M=None, rotate=None):
     return A4W4Layer(ctx, x_bits, qw, sw, R)
 
 
-def make_a8w8(ctx, cfg_name, rotate=None):
+def make_a8w8(ctx, cfg_name, rotate=None, M=None):
     from block_scaled_precision_act_amd import synth
     cfg = synth.CONFIGS[cfg_name]
-    x_bits = synth.make_activations(cfg)
+    x_bits = synth.make_activations(cfg, M)
     qw, sw = ctx.weight(cfg_name, "a8w8")
     Mx, K = x_bits.shape
     per_set = algorithmic_bytes("a8w8", Mx, cfg["N"], K) + 2 * Mx * K
@@ -711,6 +711,18 @@ def main():
             also[name] = layer_entry(ctx, lay, "a8w8", args, name)
             del lay
             torch.cuda.empty_cache()
+        log("mid-size M")
+        mid = {}
+        for kind, cfg_name in (("a4w4", "oproj_prefill_a4w4"), ("a8w8", "ptpc_a8w8_m8192")):
+            for Ms in (256, 512):
+                lay = (make_a4w4(ctx, cfg_name, M=Ms) if kind == "a4w4" else make_a8w8(ctx, cfg_name, M=Ms))
+                mid["%s M=%d" % (kind, Ms)] = layer_entry(ctx, lay, kind, args, "%s rows 0 .. %d" % (cfg_name, Ms - 1))
+                del lay
+                torch.cuda.empty_cache()
+            ctx.weights.clear()
+        also["mid_m"] = {"workload": "o_proj layer (N = 7168, K = 8192) at M = 256 and 512, the first M rows of the "
+                                     "M = 8192 activations: the 128-row tiles with copy and MFMA waves (two K parts "
+                                     "at M = 256)", "by_case": mid}
         log("one-call layer")
         also["a4w4_one_call_layer"] = one_call_layer_entry(ctx, args)
         log("offline weight conversion")
