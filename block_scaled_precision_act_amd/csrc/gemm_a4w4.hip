@@ -200,11 +200,12 @@ hipError_t launch_split(const SplitPlan& p, const void* qa, const void* sa, cons
         return p.nsl == 8 ? launch_split_nsl<1, 5, 8, true>(p, a, sa8, w, sw8, out, m, n, k, ws, st)
                           : launch_split_nsl<1, 4, 4, true>(p, a, sa8, w, sw8, out, m, n, k, ws, st);
     } else {
+        // the GEMM's plans: parts of 2048 (8 slabs), 4 or 8 of them
         if (p.mf == 1)
-            return p.nsl == 8 ? launch_split_nsl<1, 5, 8, false>(p, a, sa8, w, sw8, out, m, n, k, ws, st)
-                              : launch_split_nsl<1, 4, 4, false>(p, a, sa8, w, sw8, out, m, n, k, ws, st);
-        return p.nsl == 8 ? launch_split_nsl<2, 4, 8, false>(p, a, sa8, w, sw8, out, m, n, k, ws, st)
-                          : launch_split_nsl<2, 4, 4, false>(p, a, sa8, w, sw8, out, m, n, k, ws, st);
+            return p.kp == 4 ? launch_split_kp<1, 5, 8, 4, false>(p, a, sa8, w, sw8, out, m, n, k, ws, st)
+                             : launch_split_kp<1, 5, 8, 8, false>(p, a, sa8, w, sw8, out, m, n, k, ws, st);
+        return p.kp == 4 ? launch_split_kp<2, 4, 8, 4, false>(p, a, sa8, w, sw8, out, m, n, k, ws, st)
+                         : launch_split_kp<2, 4, 8, 8, false>(p, a, sa8, w, sw8, out, m, n, k, ws, st);
     }
 }
 

@@ -16,15 +16,16 @@
 // workgroup, and with at most 128 tiles K in two parts over 2 x tiles
 // workgroups summed in the caller's workspace (64 KB per tile).  Otherwise, where
 // the 256 x 224 tiles number at most 128 (M <= 1024 at N = 7168), K is split
-// into KP = 8, 4 or 2 parts of them (the largest whose grid, 8 KP ceil(tiles /
-// 8) workgroups, fits the CUs, with parts of at least 1024), summed in the
-// caller's workspace (gemm_tile224_fp8<VEC, KP>): one workgroup takes about
-// 133 us per tile at K = 8192 (the FP16 MFMAs bound it), so few tiles left most
-// CUs idle.  Measured (graph-replayed, rotated weights, N = 7168, K = 8192):
+// into two parts of them (parts of at least 1024), summed in the caller's
+// workspace (gemm_tile224_fp8<VEC, 2>): one workgroup takes about 133 us per
+// tile at K = 8192 (the FP16 MFMAs bound it), so few tiles left most CUs idle.
+// More parts would fit only at most 64 such tiles, which the 128 x 128 tiles
+// always take.  Measured (graph-replayed, rotated weights, N = 7168, K = 8192):
 // one 256 x 224 workgroup per tile took 133-135 us at every M from 129 to 1024;
-// its K parts M = 136 / 256 48.8 / 51.6 us (KP = 8), M = 512 70.4 us (KP = 4),
-// M = 768 / 1024 93.0 / 103.8 us (KP = 2); the 128 x 128 tile M = 136 / 200 /
-// 256 35.4 / 35.1 / 35.5 us (two parts), M = 384 / 512 55.8 / 60.8-65.2 us.
+// its two K parts M = 768 / 1024 93.0 / 103.8 us (before the 128 x 128 tile took
+// the smaller M: 8 parts at M = 136 / 256 48.8 / 51.6 us, 4 at M = 512 70.4 us);
+// the 128 x 128 tile M = 136 / 200 / 256 35.4 / 35.1 / 35.5 us (two parts),
+// M = 384 / 512 55.8 / 60.8-65.2 us.
 // Everything else runs the kernels of gemm_kernels.hpp.
 #include "gemm_kernels.hpp"
 #include "gemm_splitk.hpp"
@@ -103,14 +104,13 @@ Tile8 tile8_plan(int64_t M, int64_t N, int64_t K) {
     Tile8 p;
     if (M <= 128 || N < 1 || (M > N ? M : N) * K >= ((int64_t)1 << 31)) return p;
     const int64_t tm = (M + tile224_fp8::kTM - 1) / tile224_fp8::kTM, tn = (N + tile224_fp8::kTN - 1) / tile224_fp8::kTN;
-    if (tm * tn > 128) return p;
-    for (int kp : {8, 4, 2}) {
-        if (K % (128 * kp) != 0 || K / kp < 1024 || 8 * kp * ((tm * tn + 7) / 8) > sk::kMaxGrid) continue;
-        p.kp = kp;
-        p.tiles_m = (int)tm;
-        p.tiles_n = (int)tn;
-        return p;
-    }
+    // Two K parts.  More never fit: this plan runs only past 256 tiles of 128 x 128 (the copy/MFMA-wave
+    // kernel takes fewer), which means more than 64 of these tiles (128 tn128 tm128 <= 2 tm ceil(1.75 tn),
+    // at most 256 when tm tn <= 64), and 4 parts of more than 64 tiles would exceed 256 workgroups.
+    if (tm * tn > 128 || K % 256 != 0 || K / 2 < 1024 || 16 * ((tm * tn + 7) / 8) > sk::kMaxGrid) return p;
+    p.kp = 2;
+    p.tiles_m = (int)tm;
+    p.tiles_n = (int)tn;
     return p;
 }
 
@@ -166,13 +166,7 @@ hipError_t launch_gemm_a8w8(const void* qa, const float* sa, const void* qw, con
         return launch_pc8<1>(c, qa, sa, qw, sw, y, M, N, K, nullptr, st);
     }
     const Tile8 t = tile8_plan(M, N, K);
-    if (workspace && t.fits_device()) {
-        switch (t.kp) {
-            case 8: return launch_tile8<8>(t, qa, sa, qw, sw, y, M, N, K, workspace, st);
-            case 4: return launch_tile8<4>(t, qa, sa, qw, sw, y, M, N, K, workspace, st);
-            default: return launch_tile8<2>(t, qa, sa, qw, sw, y, M, N, K, workspace, st);
-        }
-    }
+    if (workspace && t.fits_device()) return launch_tile8<2>(t, qa, sa, qw, sw, y, M, N, K, workspace, st);
     return launch_gemm<true>(qa, sa, qw, sw, y, M, N, K, st);
 }
 

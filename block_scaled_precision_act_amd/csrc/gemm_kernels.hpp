@@ -844,8 +844,8 @@ __global__ __launch_bounds__(256, 1) void gemm_decode_fp8(const uint8_t* __restr
 // ============================================================================
 // Tile path (large M, MFMA-bound).
 // 256 x 256 output tile per workgroup of 4 waves (2 x 2, 128 x 128 each, 4 x 4
-// fragments of 32 x 32).  Each K-stage moves 128 code bytes per row of both
-// operands (K = 256 FP4 or 128 FP8) from global memory through registers into
+// fragments of 32 x 32).  gemm_tile_kernel (FP4, the fallback for K % 256 != 0):
+// each K-stage moves 128 code bytes per row of both operands (K = 256) from global memory through registers into
 // a padded LDS tile (row pitch 144 B keeps ds_read_b128 conflict-free), double
 // buffered: the loads of stage s+1 are in flight while stage s computes.
 // MFMA operand A is the weight tile (rows n), operand B the activation tile
@@ -872,9 +872,10 @@ __device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int
     tn = rem / gsz;
 }
 
-template <bool FP8>
-__global__ __launch_bounds__(256, 1) void gemm_tile_kernel(const uint8_t* __restrict__ qa, const void* __restrict__ sa_,
-                                                           const uint8_t* __restrict__ qw, const void* __restrict__ sw_,
+// VEC8: N % 4 == 0 and y 8-byte aligned (whole 8-byte output stores allowed).
+template <bool VEC8>
+__global__ __launch_bounds__(256, 1) void gemm_tile_kernel(const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa,
+                                                           const uint8_t* __restrict__ qw, const uint8_t* __restrict__ sw,
                                                            uint16_t* __restrict__ y, int M, int N, int K, int tiles_m,
                                                            int tiles_n) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[kTileLds];
@@ -885,7 +886,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(const uint8_t* __rest
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wn = wave & 1, wm = wave >> 1;
     const int l32 = lane & 31, h = lane >> 5;
-    const int64_t KB = FP8 ? (int64_t)K : (int64_t)K / 2;
+    const int64_t KB = (int64_t)K / 2;
     const int64_t KS = (int64_t)K / 32;
     const int nst = (int)((KB + kStageBytes - 1) / kStageBytes);
 
@@ -898,13 +899,13 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(const uint8_t* __rest
         wsrc[i] = qw + (int64_t)min(n0 + crow + 32 * i, N - 1) * KB + ccol * 16;
         xsrc[i] = qa + (int64_t)min(m0 + crow + 32 * i, M - 1) * KB + ccol * 16;
     }
-    // FP4 scale rows of this lane's fragments
+    // scale rows of this lane's fragments
     const uint8_t* wsc[4];
     const uint8_t* xsc[4];
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
-        wsc[f] = reinterpret_cast<const uint8_t*>(sw_) + (int64_t)min(n0 + 128 * wn + 32 * f + l32, N - 1) * KS;
-        xsc[f] = reinterpret_cast<const uint8_t*>(sa_) + (int64_t)min(m0 + 128 * wm + 32 * f + l32, M - 1) * KS;
+        wsc[f] = sw + (int64_t)min(n0 + 128 * wn + 32 * f + l32, N - 1) * KS;
+        xsc[f] = sa + (int64_t)min(m0 + 128 * wm + 32 * f + l32, M - 1) * KS;
     }
 
     uint4 pw[8], px[8];
@@ -918,14 +919,12 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(const uint8_t* __rest
             pw[i] = kin ? ldg16(wsrc[i] + koff) : make_uint4(0, 0, 0, 0);
             px[i] = kin ? ldg16(xsrc[i] + koff) : make_uint4(0, 0, 0, 0);
         }
-        if constexpr (!FP8) {
-            const int64_t sidx = 8 * (int64_t)s + 4 * h;
-            const bool sin = sidx < KS;
+        const int64_t sidx = 8 * (int64_t)s + 4 * h;
+        const bool sin = sidx < KS;
 #pragma unroll
-            for (int f = 0; f < 4; ++f) {
-                psw[f] = sin ? ldg4(wsc[f] + sidx) : 0x7f7f7f7f;
-                psx[f] = sin ? ldg4(xsc[f] + sidx) : 0x7f7f7f7f;
-            }
+        for (int f = 0; f < 4; ++f) {
+            psw[f] = sin ? ldg4(wsc[f] + sidx) : 0x7f7f7f7f;
+            psx[f] = sin ? ldg4(xsc[f] + sidx) : 0x7f7f7f7f;
         }
     };
     auto lstore = [&](int buf) {
@@ -936,12 +935,10 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(const uint8_t* __rest
             *reinterpret_cast<uint4*>(wd + 32 * i * kLdsPitch) = pw[i];
             *reinterpret_cast<uint4*>(xd + 32 * i * kLdsPitch) = px[i];
         }
-        if constexpr (!FP8) {
 #pragma unroll
-            for (int f = 0; f < 4; ++f) {
-                csw[f] = psw[f];
-                csx[f] = psx[f];
-            }
+        for (int f = 0; f < 4; ++f) {
+            csw[f] = psw[f];
+            csx[f] = psx[f];
         }
     };
 
@@ -962,8 +959,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(const uint8_t* __rest
         if (s + 1 < nst) gload(s + 1);
         const uint8_t* wb = lds + (cur * 2 + 0) * 256 * kLdsPitch + (128 * wn + l32) * kLdsPitch;
         const uint8_t* xb = lds + (cur * 2 + 1) * 256 * kLdsPitch + (128 * wm + l32) * kLdsPitch;
-        if constexpr (!FP8) {
-            // lane group h holds bytes [64h, 64h+64) of the stage (blocks 4h..4h+3); MFMA t takes block 4h+t
+        // lane group h holds bytes [64h, 64h+64) of the stage (blocks 4h..4h+3); MFMA t takes block 4h+t
 #define MX_TILE_FP4_STEP(T)                                                                                     \
     {                                                                                                           \
         uint4 wa[4], xv[4];                                                                                     \
@@ -974,50 +970,22 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(const uint8_t* __rest
         _Pragma("unroll") for (int f = 0; f < 4; ++f) _Pragma("unroll") for (int g = 0; g < 4; ++g) acc[f][g] = \
             mfma32<kFmtFP4, (T)>(fp4_operand(wa[f]), fp4_operand(xv[g]), acc[f][g], csw[f], csx[g]);           \
     }
-            MX_TILE_FP4_STEP(0)
-            MX_TILE_FP4_STEP(1)
-            MX_TILE_FP4_STEP(2)
-            MX_TILE_FP4_STEP(3)
+        MX_TILE_FP4_STEP(0)
+        MX_TILE_FP4_STEP(1)
+        MX_TILE_FP4_STEP(2)
+        MX_TILE_FP4_STEP(3)
 #undef MX_TILE_FP4_STEP
-        } else {
-            // FP8 codes are widened exactly to FP16 and run through 32x32x16 FP16 MFMAs.  Lane group
-            // h holds bytes [64h, 64h+64) of the stage; sub-step t reads 16 of them (two operands).
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                v8h wa[4][2], xv[4][2];
-#pragma unroll
-                for (int f = 0; f < 4; ++f) {
-                    const uint4 v = *reinterpret_cast<const uint4*>(wb + 32 * f * kLdsPitch + 64 * h + 16 * t);
-                    wa[f][0] = e4m3x8_to_f16x8(v.x, v.y);
-                    wa[f][1] = e4m3x8_to_f16x8(v.z, v.w);
-                }
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const uint4 v = *reinterpret_cast<const uint4*>(xb + 32 * g * kLdsPitch + 64 * h + 16 * t);
-                    xv[g][0] = e4m3x8_to_f16x8(v.x, v.y);
-                    xv[g][1] = e4m3x8_to_f16x8(v.z, v.w);
-                }
-#pragma unroll
-                for (int u = 0; u < 2; ++u)
-#pragma unroll
-                    for (int f = 0; f < 4; ++f)
-#pragma unroll
-                        for (int g = 0; g < 4; ++g) acc[f][g] = mfma32_f16(wa[f][u], xv[g][u], acc[f][g]);
-            }
-        }
         if (s + 1 < nst) lstore(cur ^ 1);
         __syncthreads();
     }
 
     // epilogue: lane holds, per fragment (f, g) and j, Y[m][n .. n+3] with
     // m = m0 + 128wm + 32g + l32 and n = n0 + 128wn + 32f + 8j + 4h
-    const bool vec_ok = (N & 3) == 0 && (reinterpret_cast<uintptr_t>(y) & 7) == 0;
+    constexpr bool vec_ok = VEC8;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
         const int m = m0 + 128 * wm + 32 * g + l32;
         if (m >= M) continue;
-        float sxm = 1.f;
-        if constexpr (FP8) sxm = reinterpret_cast<const float*>(sa_)[m];
         uint16_t* yrow = y + (int64_t)m * N;
 #pragma unroll
         for (int f = 0; f < 4; ++f)
@@ -1026,10 +994,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(const uint8_t* __rest
                 const int n = n0 + 128 * wn + 32 * f + 8 * j + 4 * h;
                 float v[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    v[e] = acc[f][g][4 * j + e];
-                    if constexpr (FP8) v[e] = ptpc_scaled(v[e], sxm, reinterpret_cast<const float*>(sw_)[min(n + e, N - 1)]);
-                }
+                for (int e = 0; e < 4; ++e) v[e] = acc[f][g][4 * j + e];
                 if (vec_ok && n + 3 < N) {
                     uint2 pk;
                     pk.x = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
@@ -3049,9 +3014,14 @@ inline hipError_t launch_gemm(const void* qa, const void* sa, const void* qw, co
             hipLaunchKernelGGL(gemm_tile_dma_fp4<4>, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, st, a,
                                reinterpret_cast<const uint8_t*>(sa), w, reinterpret_cast<const uint8_t*>(sw), out, m, n,
                                k, tiles_m, tiles_n);
-        else
-            hipLaunchKernelGGL((gemm_tile_kernel<FP8>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, st, a, sa,
-                               w, sw, out, m, n, k, tiles_m, tiles_n);
+        else if constexpr (!FP8) {  // the FP8 branches above take every K
+            if (N % 4 == 0 && (reinterpret_cast<uintptr_t>(y) & 7) == 0)
+                hipLaunchKernelGGL(gemm_tile_kernel<true>, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, st, a,
+                                   sa8, w, sw8, out, m, n, k, tiles_m, tiles_n);
+            else
+                hipLaunchKernelGGL(gemm_tile_kernel<false>, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, st, a,
+                                   sa8, w, sw8, out, m, n, k, tiles_m, tiles_n);
+        }
     }
     return hipGetLastError();
 }
@@ -3059,8 +3029,8 @@ inline hipError_t launch_gemm(const void* qa, const void* sa, const void* qw, co
 // Grouped A4W4 decode GEMM (MoE experts): grid (N / 32, G); max_rows (the largest group, or a bound on it)
 // picks 32- or 64-row chunks - every row of every group is written either way.  K % 512 == 0, K <= 16384,
 // all code and scale pointers 16-byte aligned (checked by the caller, which takes gemm_grouped_fp4 of
-// gemm_splitk.hpp instead where that measured faster): K % 2048 == 0 takes the decode ring, other K the
-// LDS-staged decode kernel.
+// gemm_splitk.hpp instead where that measured faster): K % 2048 == 0 with max_rows <= 32 takes the decode
+// ring in 32-row chunks, everything else the LDS-staged decode kernel.
 inline hipError_t launch_gemm_a4w4_grouped(const void* qa, const void* sa, const void* qw, const void* sw, void* y,
                                            const int32_t* offsets, int64_t G, int64_t max_rows, int64_t N, int64_t K,
                                            hipStream_t st) {
@@ -3071,7 +3041,7 @@ inline hipError_t launch_gemm_a4w4_grouped(const void* qa, const void* sa, const
     uint16_t* out = reinterpret_cast<uint16_t*>(y);
     const int n = (int)N, k = (int)K;
     const dim3 grid((unsigned)((N + dec4::kNT - 1) / dec4::kNT), (unsigned)G);
-    if (K % 2048 != 0) {
+    if (K % 2048 != 0 || max_rows > 32) {  // (the caller sends max_rows > 32 with K % 1024 == 0 to the tiles)
         if (max_rows <= 32)
             hipLaunchKernelGGL((gemm_decode_lds_fp4<2, true>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, 0, n, k,
                                offsets);
@@ -3080,17 +3050,11 @@ inline hipError_t launch_gemm_a4w4_grouped(const void* qa, const void* sa, const
                                offsets);
         return hipGetLastError();
     }
-    if (max_rows <= 32 && K <= 8192)
+    if (K <= 8192)
         hipLaunchKernelGGL((gemm_decode_fp4<1, 2, 256, true>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, 0, n, k,
                            offsets);
-    else if (max_rows <= 32)
-        hipLaunchKernelGGL((gemm_decode_fp4<1, 4, 512, true>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, 0, n, k,
-                           offsets);
-    else if (K <= 8192)
-        hipLaunchKernelGGL((gemm_decode_fp4<2, 2, 256, true>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, 0, n, k,
-                           offsets);
     else
-        hipLaunchKernelGGL((gemm_decode_fp4<2, 2, 512, true>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, 0, n, k,
+        hipLaunchKernelGGL((gemm_decode_fp4<1, 4, 512, true>), grid, dim3(256), 0, st, a, sa8, w, sw8, out, 0, n, k,
                            offsets);
     return hipGetLastError();
 }

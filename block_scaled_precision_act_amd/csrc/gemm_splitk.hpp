@@ -77,7 +77,7 @@ struct Cfg {
 // Workspace: the partial slots of every column group (tile, wave), KP x MF x 4 KB per group.  A launch has
 // at most kMaxGrid workgroups (all resident at once, one per CU), so at most 8 MiB; every A4W4 plan (the
 // compact slots of the two-part 128-row tile included) stays within it.  The FP8 256 x 224 tile's chunked
-// slots (workspace_bytes_chunked) can take up to about 51 MB of the A8W8 caller's workspace.
+// slots (workspace_bytes_chunked, two K parts) take up to 28 MiB of the A8W8 caller's workspace.
 constexpr int kMaxGrid = 256;
 __host__ __device__ inline size_t workspace_bytes(int tiles, int KP, int MF) {
     return (size_t)tiles * KP * 4 * MF * 4096;

@@ -240,10 +240,9 @@ mx_status ptpc_quant_weight_f32(const float *w, int64_t N, int64_t K,
  * (e.g. 7,340,032 bytes for (64, 7168, 8192)); M > 128 with at most 128
  * output tiles of 128 x 128 and K % 256 == 0, K >= 2048: two K parts, 64 KB
  * per tile (7,340,032 bytes for (256, 7168, 8192)); past 256 such tiles, with
- * at most 128 output tiles of 256 x 224: K split into the largest of 8, 4 or
- * 2 parts of at least 1024 whose grid stays within 256 workgroups, tiles x
- * (parts - 1) x 224 KB (e.g. 29,360,128 bytes for (1024, 7168, 8192)) - and 0
- * otherwise.
+ * at most 128 output tiles of 256 x 224, K % 256 == 0 and K >= 2048: two K
+ * parts, 224 KB per tile (e.g. 29,360,128 bytes for (1024, 7168, 8192), and
+ * at most 29,360,128) - and 0 otherwise.
  * Same rules as mx_gemm_a4w4_workspace_bytes: it depends on the shape only,
  * must be zero-filled before first use, is left all zero by every call, and
  * calls that share a workspace must not run concurrently.

@@ -132,6 +132,16 @@ def _sampled_check(mx, orc, qa, sa, qw, sw, what, seed, gemm="a4w4", sa_scales=N
     _check(yg[:, cols], y, ad, what + " (all rows, sampled columns)")
 
 
+@pytest.mark.parametrize("gemm", ["a4w4", "a8w8"])
+def test_256_row_tiles_unaligned_output(mx, orc, gemm):
+    """More than 160 tiles of 256 x 256 with N % 8 != 0, where 256 x 224 tiles would take more rounds
+    (240 tiles against 276): the 256 x 256 tile kernels with element-wise output stores
+    (gemm_tile_fp4<false, 256>, gemm_tile_fp8<false>), on sampled rows and columns."""
+    M, N, K = 3072, 5001, 1024
+    ops = (_random_mx if gemm == "a4w4" else _random_ptpc)(orc, 901 if gemm == "a4w4" else 902, M, N, K)
+    _sampled_check(mx, orc, *ops, "%s 256-row tiles %dx%dx%d" % (gemm, M, N, K), 903, gemm=gemm)
+
+
 def test_a4w4_prefill_config_sampled(mx, orc):
     cfg = synth.CONFIGS["oproj_prefill_a4w4"]
     qw, sw = _weight_mx("oproj_prefill_a4w4")

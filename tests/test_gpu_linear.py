@@ -44,6 +44,8 @@ def _weight(orc, seed, N, K):
     (5, 4000, 4096),    # one launch: 4 slabs, 4 parts, ragged last tile
     (3, 2900, 8192),    # one launch: 4 slabs, 8 parts, idle workgroups
     (8, 2048, 16384),   # one launch: 8 slabs, 8 parts
+    (4, 8200, 4096),    # one launch: 8 slabs, 2 parts (65 tiles)
+    (6, 8200, 2048),    # one launch: 4 slabs, 2 parts
     (64, 7168, 8192),   # quantizer + split-K GEMM: the o_proj decode layer
     (16, 7168, 8192),   # quantizer + split-K GEMM, 32-row fragments
     (33, 8100, 4096),   # quantizer + decode ring (2 parts: no GEMM split)

@@ -58,6 +58,7 @@ RH_SHAPES = [
     (65, 4000, 8192),    # one row in the second half, ragged last tile, 128 workgroups
     (100, 2900, 16384),  # 4 parts of 4096, 23 tiles: idle workgroups
     (128, 7168, 16384),  # 2 parts of 8192
+    (100, 2048, 32768),  # 4 parts of 8192, 16 tiles (128 workgroups)
 ]
 
 
@@ -147,7 +148,7 @@ SPLIT8_SHAPES = [
     (50, 2900, 16384),   # 8 parts, 23 tiles: idle workgroups
 ]
 # M > 128: the FP8 128 x 128 tile with copy and MFMA waves in two K parts (at most 128 tiles), and past 256
-# such tiles the 256 x 224 tile with K in parts of >= 1024 (at most 128 of those tiles)
+# such tiles the 256 x 224 tile with K in two parts of >= 1024 (at most 128 of those tiles)
 TILE8_SHAPES = [
     (256, 7168, 8192),   # 128 tile: 112 tiles, 224 workgroups
     (512, 2048, 8192),   # 128 tile: 64 tiles
@@ -155,6 +156,7 @@ TILE8_SHAPES = [
     (300, 1000, 2048),   # 128 tile: ragged M and N
     (1100, 4096, 4096),  # 256 x 224 tile: 95 tiles, 2 parts (idle workgroups in the last XCD's runs)
     (600, 9000, 2048),   # 256 x 224 tile: 123 tiles, 2 parts of 1024, 256 workgroups
+    (1100, 4001, 4096),  # 256 x 224 tile, 2 parts, N % 8 != 0 (element stores)
 ]
 
 
