@@ -58,6 +58,26 @@ def test_a4w4_layer_graph_replay(mx, M, N, K):
     _replays_match(mx, torch, layer, [qa, sa, y])
 
 
+# the one-call layer: one launch that quantizes inside the split-K GEMM (M <= 8), and quantizer + GEMM in one
+# call (M = 64), each with its workspace shared by the replays
+@pytest.mark.parametrize("M,N,K", [(1, 7168, 8192), (8, 2048, 16384), (64, 7168, 8192)])
+def test_a4w4_one_call_layer_graph_replay(mx, M, N, K):
+    import torch
+    x = bf16_dev(synth.act_normal(71, M, K))
+    qw, sw = mx.quant_weight_mx(torch.from_numpy(synth.weight_normal(72, N, K, 0.02)).cuda())
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    wsb = mx.mx_linear_a4w4_workspace_bytes(M, N, K)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")  # zero-filled before first use
+
+    def layer():
+        s = torch.cuda.current_stream().cuda_stream
+        assert mx.mx_linear_a4w4_bf16(x.data_ptr(), qw.data_ptr(), sw.data_ptr(), y.data_ptr(), M, N, K,
+                                      ws.data_ptr(), wsb, s) == 0
+
+    _replays_match(mx, torch, layer, [y])
+    assert int(ws[:8 << 20].count_nonzero()) == 0  # the partial area is left zero by every replay
+
+
 # the decode ring (64 x 512 x 1024), the split-K kernel (64 x 4096 x 8192), the 128-row FP8 tile with copy and
 # MFMA waves (300 x 512 x 1024), in two K parts (256 x 2048 x 8192), and the 256 x 224 FP8 tile (2200 x 3900 x 512)
 @pytest.mark.parametrize("M,N,K", [(64, 512, 1024), (64, 4096, 8192), (300, 512, 1024), (256, 2048, 8192),
