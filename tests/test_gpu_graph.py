@@ -78,6 +78,25 @@ def test_a4w4_one_call_layer_graph_replay(mx, M, N, K):
     assert int(ws[:8 << 20].count_nonzero()) == 0  # the partial area is left zero by every replay
 
 
+# the allocation-free GEMM, for callers under graph capture: its split-K workspace is the library's static
+# per-GPU array, left zero by every replay
+@pytest.mark.parametrize("M,N,K", [(64, 7168, 8192), (256, 2048, 8192)])
+def test_a4w4_noalloc_graph_replay(mx, M, N, K):
+    import torch
+    assert mx.mx_gemm_a4w4_workspace_bytes(M, N, K) > 0, "the shape should take a split-K plan"
+    qa, sa = mx.quant_act_mx(bf16_dev(synth.act_normal(81, M, K)))
+    qw, sw = mx.quant_weight_mx(torch.from_numpy(synth.weight_normal(82, N, K, 0.02)).cuda())
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+    def gemm():
+        s = torch.cuda.current_stream().cuda_stream
+        assert mx.mx_gemm_a4w4_bf16_noalloc(qa.data_ptr(), sa.data_ptr(), qw.data_ptr(), sw.data_ptr(), y.data_ptr(),
+                                            M, N, K, s) == 0
+
+    _replays_match(mx, torch, gemm, [y])
+    assert torch.equal(y.view(torch.int16), mx.gemm_a4w4(qa, sa, qw, sw).view(torch.int16))
+
+
 # the decode ring (64 x 512 x 1024), the split-K kernel (64 x 4096 x 8192), the 128-row FP8 tile with copy and
 # MFMA waves (300 x 512 x 1024), in two K parts (256 x 2048 x 8192), and the 256 x 224 FP8 tile (2200 x 3900 x 512)
 @pytest.mark.parametrize("M,N,K", [(64, 512, 1024), (64, 4096, 8192), (300, 512, 1024), (256, 2048, 8192),
