@@ -126,10 +126,13 @@ size_t mx_gemm_a4w4_workspace_bytes(int64_t M, int64_t N, int64_t K);
  * only when the whole grid fits the device's CUs at once (one workgroup per
  * CU); otherwise the workspace-free kernels run.  They rely on
  * workgroups being dealt round-robin to the XCDs (the parts of a tile meet in
- * one XCD's L2), and on no other work keeping CUs from the grid for long: a
- * workgroup waiting for a partner gives up after about 0.3 s, so that no
- * launch can hang; the outputs it owns are then NaN, and the workspace must
- * be zero-filled again before its next use.
+ * one XCD's L2), and on no other work keeping CUs from the grid for long -
+ * in particular, two such launches (of this or of the other split-K entry
+ * points) must not run at the same time on different streams, since each
+ * would hold CUs the other waits for: a workgroup waiting for a partner
+ * gives up after about 0.3 s, so that no launch can hang; the outputs it
+ * owns are then NaN, and the workspace must be zero-filled again before its
+ * next use.
  */
 mx_status mx_gemm_a4w4_bf16(const void *qa, const void *sa, const void *qw, const void *sw,
                             void *y_bf16, int64_t M, int64_t N, int64_t K,
