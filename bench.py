@@ -232,12 +232,30 @@ class A8W8Layer:
         return lambda: (q(), g())
 
 
+# Graph replays leave the GPU idle for several us between one replay's last kernel and the next one's first;
+# kernel timings capture at least this many launches per graph, so that gap is spread thin.
+LAUNCHES_PER_GRAPH = 160
+
+
+def cycled_graph(ctx, thunks):
+    """A graph cycling over the calls `thunks` (e.g. one per rotated copy) at least LAUNCHES_PER_GRAPH times
+    in all, and its call count."""
+    m = max(1, -(-LAUNCHES_PER_GRAPH // len(thunks)))
+    return ctx.capture(list(thunks) * m), m * len(thunks)
+
+
+def graph_ms(ctx, thunks, reps):
+    """Average ms per call over about reps x len(thunks) calls (at least two graph replays)."""
+    g, n = cycled_graph(ctx, thunks)
+    return ctx.event_ms(g, max(2, -(-reps * len(thunks) // n))) / n
+
+
 def kernel_ms(ctx, layer, which, reps):
-    g = ctx.capture([getattr(layer, which)(r) for r in range(layer.R)])
-    return ctx.event_ms(g, reps) / layer.R
+    return graph_ms(ctx, [getattr(layer, which)(r) for r in range(layer.R)], reps)
 
 
 SUSTAIN_S = 0.05
+STEPS_PER_GRAPH = 1000
 
 
 def sustained_entry(ctx, layer, which, reps, kind):
@@ -247,13 +265,12 @@ def sustained_entry(ctx, layer, which, reps, kind):
     load; both figures are reported, the primary ones keep the short warm-up."""
     import time
     torch = ctx.torch
-    g = ctx.capture([getattr(layer, which)(r) for r in range(layer.R)])
+    g, n = cycled_graph(ctx, [getattr(layer, which)(r) for r in range(layer.R)])
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < SUSTAIN_S:
-        for _ in range(4):
-            g.replay()
+        g.replay()
         torch.cuda.synchronize()
-    ms = ctx.event_ms(g, reps) / layer.R
+    ms = ctx.event_ms(g, max(2, -(-reps * layer.R // n))) / n
     r = roofline_gemm(kind, layer.M, layer.N, layer.K, ms)
     return {"warmup_s": SUSTAIN_S, "kernel_us": r["kernel_us"], "achieved": r["achieved"], "unit": r["unit"],
             "frac": r["frac"]}
@@ -332,20 +349,29 @@ def make_a8w8(ctx, cfg_name, rotate=None, M=None):
 
 
 def time_steps(ctx, layer, steps, warmup):
-    """Wall-clock time of exactly `steps` layer steps replayed from graphs."""
+    """Wall-clock time of exactly `steps` layer steps (step i on rotated copy i mod R), captured as graphs of
+    up to STEPS_PER_GRAPH consecutive steps and replayed back to back.  A graph launch costs the host 15-30 us
+    before its first kernel starts, and the next launch can wait on it, so the timed steps go in as few
+    launches as possible: one for up to STEPS_PER_GRAPH steps.  Warm-up: ceil(warmup / R) replays of all R copies,
+    then one untimed replay of each timed graph (its first launch)."""
     torch = ctx.torch
     R = layer.R
+    cache = {}
+    timed = []
+    for s0 in range(0, steps, STEPS_PER_GRAPH):
+        key = (s0 % R, min(STEPS_PER_GRAPH, steps - s0))
+        if key not in cache:
+            cache[key] = ctx.capture([layer.step((key[0] + i) % R) for i in range(key[1])])
+        timed.append(cache[key])
     full = ctx.capture([layer.step(r) for r in range(R)])
-    rem = steps % R
-    tail = ctx.capture([layer.step(r) for r in range(rem)]) if rem else None
     for _ in range(-(-warmup // R)):
         full.replay()
+    for g in cache.values():
+        g.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps // R):
-        full.replay()
-    if tail is not None:
-        tail.replay()
+    for g in timed:
+        g.replay()
     torch.cuda.synchronize()
     return (time.perf_counter() - t0) * 1e3 / steps
 
@@ -410,8 +436,7 @@ def weight_conversion_entry(ctx, args):
                                   ("ptpc_fp8", "ptpcw", mx.ptpc_quant_weight_f32, q8, s8)):
         thunks = [(lambda i=i: ok(fn(ws[i].data_ptr(), N, K, qs[i].data_ptr(), ss[i].data_ptr(), ctx.stream()),
                                   key)) for i in range(len(ws))]
-        g = ctx.capture(thunks)
-        ms = ctx.event_ms(g, args.kernel_reps) / len(ws)
+        ms = graph_ms(ctx, thunks, args.kernel_reps)
         byt = algorithmic_bytes(kind, N, 0, K)
         gbs = byt / (ms * 1e-3) / 1e9
         out[key] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -446,8 +471,7 @@ def grouped_entry(ctx, args, name="moe_grouped_a4w4"):
                                                            sws[r].data_ptr(), y.data_ptr(), offsets.data_ptr(), G,
                                                            max_rows, N, K, ctx.stream()), "grouped"))
               for r in range(R)]
-    g = ctx.capture(thunks)
-    ms = ctx.event_ms(g, args.kernel_reps) / R
+    ms = graph_ms(ctx, thunks, args.kernel_reps)
     used = counts > 0
     byt = int(used.sum()) * (N * K // 2 + N * K // 32) + T * (K // 2 + K // 32) + 2 * T * N
     gbs = byt / (ms * 1e-3) / 1e9
